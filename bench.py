@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the varlen attention backward on one MI355X.
+
+One step = one fa_varlen_bwd call over the whole workload (row preprocess,
+main backward kernel, dQ convert) with every input already resident in HBM.
+Default workload: bf16, 4 sequences x 16384 tokens, 16 heads, D = 128,
+bottom-right causal mask, keep_prob 1.
+
+Metric: useful TFLOP/s = 10 * N * D * (admitted query/key pairs) / step time
+(five contractions of 2*D flops per admitted pair and head).
+
+Also reported:
+  roofline      the main kernel's useful flops per launch over its average
+                duration (HIP events on the launch stream, recorded by the
+                library during the timed steps) against the bf16 MFMA peak;
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
+                same workload (a few (sequence, head) units), as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flashattention_fa_amd", "csrc", "fa_kernels.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per main-kernel launch from committed counter runs, if taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, y_host, smax_h, ssum_h, wl, units_wanted: int):
+    """Time the oracle backward on the first `units` (sequence, head) units of the workload."""
+    import numpy as np
+
+    from oracle import fa_oracle as O
+    from variable_length_flashattention_fa_amd import synth
+    from variable_length_flashattention_fa_amd.inputs_forward import pair_count
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(16, cores, units_wanted))
+    nb = len(inp.cu_q) - 1
+    units = [(b, n) for n in range(wl.heads) for b in range(nb)][:workers]
+    q, k, v, dy = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v, inp.dy))
+    flops = 0
+    for b, _ in units:
+        cq = inp.cu_q[b:b + 2] - inp.cu_q[b]
+        ck = inp.cu_kv[b:b + 2] - inp.cu_kv[b]
+        flops += 10 * wl.head_dim * pair_count(cq, ck, wl.mode, wl.pre, wl.nxt)
+    log(f"cpu baseline: oracle on {len(units)} (sequence, head) units with {workers} worker processes")
+    t0 = time.perf_counter()
+    O.backward(q, k, v, dy, y_host, smax_h, ssum_h, inp.cu_q, inp.cu_kv, mode=wl.mode, pre=wl.pre, nxt=wl.nxt,
+               keep_prob=wl.keep_prob, drop_mask=inp.drop_mask, scale=wl.scale, head_num=wl.heads,
+               workers=workers, units=units)
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{len(units)} of {nb * wl.heads} (sequence, head) units of the same workload "
+                   f"(each one sequence x one head, fp64 numpy, one BLAS thread per worker process); "
+                   f"{dt:.1f} s wall"),
+        "seconds": dt,
+        "useful_tflop": flops / 1e12,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (default 3)")
+    ap.add_argument("--cpu-units", type=int, default=16, help="(sequence, head) units for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each (sequence, head) unit is "
+              "independent; see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from variable_length_flashattention_fa_amd import binding as B
+    from variable_length_flashattention_fa_amd import synth
+    from variable_length_flashattention_fa_amd.inputs_forward import forward_stats, pair_count
+
+    B.load()  # fail loudly before any work if the library is missing
+    wl = synth.workload(args.workload)
+    t0 = time.time()
+    log(f"workload {args.workload}: {wl.name}; drawing inputs")
+    inp = synth.make(wl)
+    dev = torch.device("cuda:0")
+    q, k, v, dy = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.dy))
+    drop = torch.from_numpy(inp.drop_mask).to(dev) if inp.drop_mask is not None else None
+    log(f"inputs on device ({time.time() - t0:.1f}s); forward for Y and statistics")
+    y, smax, ssum = forward_stats(q, k, v, inp.cu_q, inp.cu_kv, mode=wl.mode, pre=wl.pre, nxt=wl.nxt,
+                                  keep_prob=wl.keep_prob, drop_mask=drop, scale=wl.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        B.fa_varlen_bwd(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt, wl.keep_prob,
+                        drop, wl.scale, wl.heads, dq, dk, dv, stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.profile_read()  # drop anything recorded before the timed region
+    B.profile_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    B.profile_enable(False)
+    prof = B.profile_read()
+    ms_per_step = elapsed * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    pairs = pair_count(inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt)
+    useful = 10.0 * wl.heads * wl.head_dim * pairs
+    value = useful / (ms_per_step * 1e-3) / 1e12
+    main_ms, main_n = prof["bwd_main"]
+    main_avg = main_ms / max(main_n, 1)
+    achieved = useful / (main_avg * 1e-3) / 1e12
+    tq, heads, d = q.shape
+    esz = q.element_size()
+    pre_bytes = tq * heads * (2 * d * esz + 2 * 4 + 8 + 4 * d)   # dY, Y, m, l in; {delta, beta}, zeroed dQ acc out
+    cvt_bytes = tq * heads * (4 * d + d * esz)                   # fp32 dQ acc in, dQ out
+    kernels = {}
+    for name, nbytes in (("preprocess", pre_bytes), ("bwd_main", None), ("convert_dq", cvt_bytes)):
+        ms, n = prof[name]
+        avg = ms / max(n, 1)
+        entry = {"avg_ms": avg, "launches": n}
+        if nbytes is not None:
+            entry["algorithmic_bytes"] = nbytes
+            entry["GB/s"] = nbytes / (avg * 1e-3) / 1e9 if avg > 0 else None
+            entry["hbm_frac"] = entry["GB/s"] / PEAK_HBM_GBS if entry["GB/s"] else None
+        else:
+            entry["useful_tflop"] = useful / 1e12
+            entry["TFLOP/s"] = achieved
+        kernels[name] = entry
+
+    dtype_name = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[q.dtype]
+    out = {
+        "metric": "attn-bwd useful TFLOP/s (varlen TND, causal) and % of bf16 MFMA peak, 1 GPU",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic (seeded normal Q/K/V/dY; Y and softmax stats from a device forward)",
+        "config": {"workload": wl.name, "sequences": len(wl.lengths), "tokens": wl.tokens, "heads": wl.heads,
+                   "head_dim": wl.head_dim, "mask": ["none", "causal", "band"][wl.mode], "pre_tokens": wl.pre,
+                   "next_tokens": wl.nxt, "keep_prob": wl.keep_prob, "admitted_pairs_per_head": pairs},
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for(wl.name),
+                     "kernel": "bwd_main_kernel", "avg_ms": main_avg},
+        "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        y_host = synth.as_float_array(y.cpu())
+        smax_h, ssum_h = smax.cpu().numpy(), ssum.cpu().numpy()
+        del q, k, v, dy, y, dq, dk, dv
+        out["cpu_baseline"] = cpu_baseline(inp, y_host, smax_h, ssum_h, wl, args.cpu_units)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

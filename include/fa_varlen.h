@@ -1,0 +1,187 @@
+/*
+ * fa_varlen.h -- C ABI of the MI355X (gfx950) varlen attention backward.
+ *
+ * Operation: the backward pass of scaled-dot-product attention over
+ * variable-length sequences packed in TND layout, as defined on the CANN
+ * ops-transformer page "FlashAttention梯度V2"
+ * (aclnnFlashAttentionUnpaddingScoreGradV2), section 计算公式 (formulas):
+ *
+ *     forward    S = Mask(scale * Q K^T, atten_mask)
+ *                P = Dropout(Softmax(S), keepProb),   Y = P V
+ *     backward   dV = P^T dY
+ *                dQ = scale * dS K
+ *                dK = scale * dS^T Q
+ *
+ * with the softmax Jacobian step dP = dY V^T, dS = Ps o (dP o Z/kp - D),
+ * D_i = sum_d dY_i,d Y_i,d, where Ps is the pre-dropout softmax rebuilt from
+ * the forward statistics, Ps = exp(S - max) / sum, and Z the keep bits.
+ *
+ * Argument list and error classes follow the page's 函数原型 (prototypes),
+ * 参数说明 (parameter table) and 返回值 (return codes) sections, collapsed
+ * into one call: there is no separate workspace query, the library keeps its
+ * own workspace.
+ *
+ * Ownership: the caller owns every tensor, both cu_seqlens arrays and the
+ * stream.  Tensor and statistics pointers are DEVICE pointers; cu_seqlens
+ * arrays are HOST arrays, read before the call returns.  dq, dk, dv are fully
+ * overwritten (never accumulated): a query row that sees no key gets dq = 0,
+ * a key that no query sees gets dk = dv = 0.
+ *
+ * Errors are detected before any device work is enqueued; on a non-OK
+ * status nothing has been launched and fa_last_error() describes the cause.
+ * On FA_OK the work is enqueued asynchronously on `stream`.
+ */
+#ifndef FA_VARLEN_H
+#define FA_VARLEN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of the page's tensor table (FLOAT32, FLOAT16, BFLOAT16). */
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype_t;
+
+/* A TND tensor view: element [t, n, d] lives at
+ * data + (t * stride_t + n * stride_h + d) * sizeof(element).
+ * Strides are in elements; the innermost (d) stride must be 1.  Non-contiguous
+ * token and head strides are accepted, as the page's tensor table allows. */
+typedef struct {
+    void*   data;       /* device pointer */
+    int32_t dtype;      /* fa_dtype_t */
+    int64_t tokens;     /* T */
+    int64_t heads;      /* N */
+    int64_t head_dim;   /* D */
+    int64_t stride_t;
+    int64_t stride_h;
+} fa_tensor_t;
+
+/* Sequence boundaries: a HOST array of batch + 1 int64 prefix sums with
+ * cu[0] = 0 and cu[batch] = T (the page's actualSeqQLen / actualSeqKvLen). */
+typedef struct {
+    const int64_t* cu;
+    int64_t        batch;
+} fa_seqlens_t;
+
+/* Status codes.  FA_ERR_NULLPTR and FA_ERR_INVALID mirror the page's
+ * ACLNN_ERR_PARAM_NULLPTR (161001) and ACLNN_ERR_PARAM_INVALID (161002). */
+enum {
+    FA_OK = 0,
+    FA_ERR_NULLPTR = 1,      /* a required pointer is null */
+    FA_ERR_INVALID = 2,      /* a value outside the page's constraints */
+    FA_ERR_UNSUPPORTED = 3,  /* allowed by the page, not built here */
+    FA_ERR_RUNTIME = 4       /* a HIP runtime failure */
+};
+
+/* Mask modes.  The page's atten_mask marks excluded positions with 1; here the
+ * excluded set is generated from the mode.  With off_b = Lkv_b - Lq_b:
+ *   FA_MASK_NONE    every key of the sequence is admitted;
+ *   FA_MASK_CAUSAL  key j is admitted for query i iff j <= i + off_b
+ *                   (lower-triangular, aligned to the bottom-right corner);
+ *   FA_MASK_BAND    iff i + off_b - pre_tokens <= j <= i + off_b + next_tokens
+ *                   (the preTokens/nextTokens sliding window). */
+enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BAND = 2 };
+
+/*
+ * fa_varlen_bwd -- dQ, dK, dV of varlen attention.
+ *
+ * q, dy, y          [Tq, N, D] inputs (y is the forward output attentionIn).
+ * k, v              [Tkv, N, D] inputs.
+ * softmax_max/sum   [N, Tq, 8] contiguous fp32 device arrays: the forward's
+ *                   row max and row sum of exp, replicated over the last
+ *                   axis (element 0 is read).  Rows with no admitted key are
+ *                   never read.
+ * cu_seqlens_q/kv   HOST prefix sums, equal batch counts (1..2048).
+ * atten_mode        FA_MASK_*; pre_tokens/next_tokens are read only in
+ *                   FA_MASK_BAND.
+ * keep_prob         in (0, 1].  Below 1, drop_mask must be given.
+ * drop_mask         DEVICE uint8 bit stream, least significant bit first:
+ *                   for each sequence b in order, a row-major
+ *                   [N, Lq_b, Lkv_b] block of keep bits with no padding
+ *                   (bit 1 keeps; kept values are scaled by 1/keep_prob).
+ *                   Not read when keep_prob == 1 (may be NULL).
+ * scale             the page's scaleValue (replaces 1/sqrt(d)).
+ * head_num          N; must equal q->heads.
+ * dq, dk, dv        outputs, same dtype and shapes as q, k, v.
+ * stream            hipStream_t (NULL = the null stream).
+ *
+ * Supported: all tensors one dtype (FA_F32, FA_F16 or FA_BF16); D in {64,128};
+ * k/v heads == q heads; v head_dim == q head_dim.  Other values the page
+ * allows (grouped heads, Dv < Dk, other D) return FA_ERR_UNSUPPORTED.
+ * Tq == 0 returns FA_OK with nothing launched.
+ *
+ * Calls on different streams share one library workspace per device and
+ * must not overlap in time.
+ */
+int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                  const fa_tensor_t* dy, const fa_tensor_t* y,
+                  const float* softmax_max, const float* softmax_sum,
+                  const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
+                  int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens,
+                  double keep_prob, const uint8_t* drop_mask,
+                  double scale, int64_t head_num,
+                  const fa_tensor_t* dq, const fa_tensor_t* dk, const fa_tensor_t* dv,
+                  void* stream);
+
+/* Thread-local description of the last non-OK status (empty string if none). */
+const char* fa_last_error(void);
+
+/* Frees the library's cached device workspace and work lists (synchronises
+ * the device first).  The next fa_varlen_bwd call re-allocates them. */
+void fa_release(void);
+
+/* One work item of the main kernel: a block of FA_BLOCK_KV keys of one
+ * sequence and the range of FA_BLOCK_Q-row query tiles that can see it. */
+typedef struct {
+    int32_t q_start;     /* first token of the sequence in q/dy/y/dq */
+    int32_t kv_start;    /* first token of the sequence in k/v/dk/dv */
+    int32_t len_q;       /* Lq_b */
+    int32_t len_kv;      /* Lkv_b */
+    int32_t kv_block;    /* block index: keys [kv_block*FA_BLOCK_KV, +FA_BLOCK_KV) */
+    int32_t tile_begin;  /* first query tile (rows tile*block_q ...) with an admitted pair */
+    int32_t tile_end;    /* one past the last; == tile_begin: block sees no query */
+    int32_t seq;         /* sequence index b */
+    int64_t drop_base;   /* bit index of element (0, 0) of head 0 of this sequence */
+} fa_work_item_t;
+
+#define FA_BLOCK_KV 128
+
+/*
+ * fa_varlen_worklist -- the host-side work list the backward launches over
+ * (exposed for inspection and testing; no device work).
+ *
+ * For every sequence with Lkv_b > 0 and every block of FA_BLOCK_KV keys, the
+ * item's tile range covers exactly the query tiles of block_q rows that hold
+ * at least one admitted (query, key) pair with a key in the block.  Blocks
+ * that no query sees are kept with an empty range so that their dK/dV rows
+ * are written as zeros.  Items are ordered longest first (by tile count).
+ *
+ * block_q: the query tile height (64 for 16-bit types, 32 for FA_F32).
+ * items: HOST array of capacity entries, may be NULL to only count.
+ * Returns the number of items (>= 0), or -FA_ERR_* on invalid input.
+ */
+int64_t fa_varlen_worklist(const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
+                           int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens,
+                           int64_t heads, int32_t block_q,
+                           fa_work_item_t* items, int64_t capacity);
+
+/*
+ * Kernel timing (instrumentation for benchmarks).  While enabled, every
+ * fa_varlen_bwd call records a pair of HIP events around each of its kernels
+ * on the call's stream: index 0 the row preprocess, 1 the main backward
+ * kernel, 2 the dQ convert.
+ */
+void fa_profile_enable(int on);
+
+/* Waits for the recorded events, writes the summed milliseconds and launch
+ * counts per kernel index into ms[] / launches[] (capacity entries each, may be
+ * NULL) and clears the record.  Returns the number of kernel indices (3), or
+ * -FA_ERR_RUNTIME if an event could not be read. */
+int fa_profile_read(double* ms, int64_t* launches, int capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_VARLEN_H */

@@ -1,0 +1,137 @@
+"""C ABI checks that need no GPU: exported symbols and every validation path.
+
+All validation returns before any device work, so these calls run on the CPU
+with fake (never dereferenced) device addresses.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from variable_length_flashattention_fa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def _header_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_header_function():
+    lib = B.load()
+    names = _header_functions()
+    assert {"fa_varlen_bwd", "fa_last_error", "fa_release", "fa_varlen_worklist"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _t(tokens, heads=2, dim=64, dtype=B.FA_BF16, data=FAKE):
+    return B.FaTensor(ctypes.c_void_p(data), dtype, tokens, heads, dim, heads * dim, dim)
+
+
+def _call(q=None, k=None, v=None, dy=None, y=None, smax=FAKE, ssum=FAKE, cu_q=(0, 10), cu_kv=(0, 10),
+          mode=0, pre=0, nxt=0, kp=1.0, drop=None, scale=0.125, head_num=2, dq=None, dk=None, dv=None):
+    tq = cu_q[-1]
+    tk = cu_kv[-1]
+    q = q if q is not None else _t(tq)
+    k = k if k is not None else _t(tk)
+    v = v if v is not None else _t(tk)
+    dy = dy if dy is not None else _t(tq)
+    y = y if y is not None else _t(tq)
+    dq = dq if dq is not None else _t(tq)
+    dk = dk if dk is not None else _t(tk)
+    dv = dv if dv is not None else _t(tk)
+    aq = np.asarray(cu_q, dtype=np.int64)
+    ak = np.asarray(cu_kv, dtype=np.int64)
+    sq = B.FaSeqlens(aq.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), aq.size - 1)
+    sk = B.FaSeqlens(ak.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ak.size - 1)
+    lib = B.load()
+    ref = lambda x: None if x is None else ctypes.byref(x)  # noqa: E731
+    st = lib.fa_varlen_bwd(ref(q), ref(k), ref(v), ref(dy), ref(y),
+                           None if smax is None else ctypes.c_void_p(smax),
+                           None if ssum is None else ctypes.c_void_p(ssum), ctypes.byref(sq), ctypes.byref(sk),
+                           mode, pre, nxt, kp, None if drop is None else ctypes.c_void_p(drop), scale,
+                           head_num, ref(dq), ref(dk), ref(dv), None)
+    return st, lib.fa_last_error().decode()
+
+
+def test_null_pointers():
+    lib = B.load()
+    st = lib.fa_varlen_bwd(None, None, None, None, None, None, None, None, None, 0, 0, 0, 1.0, None, 1.0, 1,
+                           None, None, None, None)
+    assert st == B.FA_ERR_NULLPTR
+    assert _call(q=_t(10, data=0))[0] == B.FA_ERR_NULLPTR
+    assert _call(dv=_t(10, data=0))[0] == B.FA_ERR_NULLPTR
+    assert _call(smax=None)[0] == B.FA_ERR_NULLPTR
+    st, msg = _call(kp=0.9, drop=None)
+    assert st == B.FA_ERR_NULLPTR and "drop_mask" in msg
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(kp=0.0), dict(kp=1.5), dict(kp=float("nan")),
+    dict(head_num=3),
+    dict(dq=_t(10, dtype=B.FA_F16)),
+    dict(q=_t(10, dtype=7)),
+    dict(q=_t(10, heads=300), k=_t(10, heads=300), v=_t(10, heads=300), dy=_t(10, heads=300),
+         y=_t(10, heads=300), dq=_t(10, heads=300), dk=_t(10, heads=300), dv=_t(10, heads=300), head_num=300),
+    dict(cu_q=(0, 1 << 21), cu_kv=(0, 10)),
+    dict(cu_q=(1, 10)), dict(cu_q=(0, 6, 4, 10), cu_kv=(0, 3, 7, 10)),
+    dict(cu_q=(0, 9), q=_t(10), dy=_t(10), y=_t(10), dq=_t(10)),
+    dict(cu_q=(0, 4, 10), cu_kv=(0, 10)),
+    dict(mode=3), dict(mode=-1),
+    dict(q=_t(10, dim=128)),
+    dict(k=_t(12)),
+    dict(scale=float("inf")),
+])
+def test_invalid_arguments(kwargs):
+    st, msg = _call(**kwargs)
+    assert st == B.FA_ERR_INVALID, (kwargs, st, msg)
+    assert msg
+
+
+def test_batch_limits():
+    cu = tuple(range(0, 2050))  # 2049 sequences of one token
+    st, _ = _call(cu_q=cu, cu_kv=cu, q=_t(2049), k=_t(2049), v=_t(2049), dy=_t(2049), y=_t(2049),
+                  dq=_t(2049), dk=_t(2049), dv=_t(2049))
+    assert st == B.FA_ERR_INVALID
+    assert _call(cu_q=(0,), cu_kv=(0,))[0] == B.FA_ERR_INVALID
+
+
+def test_unsupported_variants():
+    # head dims outside {64, 128}
+    args = {n: _t(10, dim=96) for n in ("q", "k", "v", "dy", "y", "dq", "dk", "dv")}
+    assert _call(**args)[0] == B.FA_ERR_UNSUPPORTED
+    # grouped heads: 4 query heads over 2 key/value heads
+    args = {n: _t(10, heads=4) for n in ("q", "dy", "y", "dq")}
+    args.update({n: _t(10, heads=2) for n in ("k", "v", "dk", "dv")})
+    assert _call(head_num=4, **args)[0] == B.FA_ERR_UNSUPPORTED
+    # v head dim smaller than k's
+    assert _call(v=_t(10, dim=32), dv=_t(10, dim=32))[0] == B.FA_ERR_UNSUPPORTED
+    # misaligned base address
+    assert _call(q=_t(10, data=FAKE + 2))[0] == B.FA_ERR_UNSUPPORTED
+
+
+def test_empty_query_returns_ok_without_device_work():
+    # T == 0: validated, then returned before any HIP call (runs on a GPU-less host)
+    st, msg = _call(cu_q=(0, 0), cu_kv=(0, 0), q=_t(0, data=0), k=_t(0, data=0), v=_t(0, data=0),
+                    dy=_t(0, data=0), y=_t(0, data=0), dq=_t(0, data=0), dk=_t(0, data=0), dv=_t(0, data=0))
+    assert st == B.FA_OK, msg
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        B.load(str(tmp_path / "libfa_varlen.so"))

@@ -1,0 +1,83 @@
+"""Build libfa_varlen.so for gfx950 with hipcc (in-tree, no JIT cache).
+
+Usage: python -m variable_length_flashattention_fa_amd.csrc.build  [--arch gfx950]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(HERE)
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+LIBDIR = os.path.join(PKG, "lib")
+LIBNAME = "libfa_varlen.so"
+
+HIP_SOURCES = ["fa_kernels.hip", "fa_api.cpp"]
+CXX_SOURCES = ["fa_worklist.cpp"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass does not know the packed-fp32 feature and says so; that is harmless
+    lines = [l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l and "--hip-link" not in l]
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + "\n".join(lines))
+    return "\n".join(lines)
+
+
+def build(arch: str = "gfx950", verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    common = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{HERE}", "-Wall"]
+    hip_flags = [f"--offload-arch={arch}", "-munsafe-fp-atomics",
+                 # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
+                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    jobs = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        lang = [] if src.endswith(".hip") else ["-x", "hip"]
+        jobs.append([hipcc] + common + hip_flags + lang + ["-c", os.path.join(HERE, src), "-o", obj])
+        objs.append(obj)
+    for src in CXX_SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        jobs.append(["g++"] + common + ["-c", os.path.join(HERE, src), "-o", obj])
+        objs.append(obj)
+    with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        outs = list(ex.map(_run, jobs))
+    if verbose:
+        for o in outs:
+            if o:
+                print(o)
+    out = os.path.join(LIBDIR, LIBNAME)
+    tmp = out + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={arch}", "-o", tmp] + objs)
+    os.replace(tmp, out)
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--arch", default="gfx950")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    print(build(args.arch, args.verbose))
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

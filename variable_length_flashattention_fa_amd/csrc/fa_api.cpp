@@ -1,0 +1,414 @@
+// C ABI entry points: validation, workspace, work list and launch sequence.
+//
+// Validation follows the constraints and return codes of the
+// "FlashAttention梯度V2" page (约束说明 and 返回值 sections): null required
+// pointers -> FA_ERR_NULLPTR; dtype / shape / range violations ->
+// FA_ERR_INVALID.  Everything is checked before any device work is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "fa_internal.h"
+#include "fa_kernels.h"
+
+namespace fa {
+const char* last_error_cstr();
+}
+
+namespace {
+
+using fa::set_error;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 20;  // T in [1, 1M]
+constexpr int64_t kMaxHeads = 256;                 // N in [1, 256]
+constexpr int64_t kMaxHeadDim = 768;               // D in [1, 768]
+
+int check_tensor(const fa_tensor_t* t, const char* name) {
+    if (t == nullptr || (t->data == nullptr && t->tokens != 0)) {
+        set_error(std::string(name) + " is null");
+        return FA_ERR_NULLPTR;
+    }
+    if (t->dtype != FA_F32 && t->dtype != FA_F16 && t->dtype != FA_BF16) {
+        set_error(std::string(name) + ": dtype must be FA_F32, FA_F16 or FA_BF16");
+        return FA_ERR_INVALID;
+    }
+    if (t->tokens < 0 || t->tokens > kMaxTokens) {
+        set_error(std::string(name) + ": tokens must be in [0, 2^20]");
+        return FA_ERR_INVALID;
+    }
+    if (t->heads < 1 || t->heads > kMaxHeads) {
+        set_error(std::string(name) + ": heads must be in [1, 256]");
+        return FA_ERR_INVALID;
+    }
+    if (t->head_dim < 1 || t->head_dim > kMaxHeadDim) {
+        set_error(std::string(name) + ": head_dim must be in [1, 768]");
+        return FA_ERR_INVALID;
+    }
+    if (t->stride_t < 0 || t->stride_h < 0) {
+        set_error(std::string(name) + ": strides must be non-negative");
+        return FA_ERR_INVALID;
+    }
+    return FA_OK;
+}
+
+size_t elem_size(int32_t dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+// 16-byte vector access of rows needs aligned bases and strides.
+bool aligned16(const fa_tensor_t* t) {
+    const size_t es = elem_size(t->dtype);
+    return (reinterpret_cast<uintptr_t>(t->data) % 16 == 0) && ((t->stride_t * es) % 16 == 0) &&
+           ((t->stride_h * es) % 16 == 0);
+}
+
+struct Workspace {
+    float* dq_acc = nullptr;
+    size_t dq_acc_bytes = 0;
+    float2* rowstat = nullptr;
+    size_t rowstat_bytes = 0;
+    fa_work_item_t* items = nullptr;
+    size_t items_cap = 0;
+    // cached work list: key and host copy
+    std::vector<int64_t> key;
+    int64_t n_items = 0;
+};
+
+std::mutex g_mutex;
+std::unordered_map<int, Workspace> g_ws;
+
+// ---- optional per-kernel event timing ----
+constexpr int kKernels = 3;  // 0 preprocess, 1 main, 2 convert
+struct EventPair {
+    int kernel;
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+bool g_profile = false;
+std::vector<EventPair> g_events;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Records `start` before and `stop` after the launch made by fn (when profiling).
+template <typename F>
+hipError_t timed(int kernel, hipStream_t s, F&& fn) {
+    if (!g_profile) return fn();
+    hipEvent_t a = take_event();
+    hipEvent_t b = take_event();
+    if (a == nullptr || b == nullptr) return fn();
+    (void)hipEventRecord(a, s);
+    hipError_t e = fn();
+    (void)hipEventRecord(b, s);
+    g_events.push_back({kernel, a, b});
+    return e;
+}
+
+int runtime_error(const char* what, hipError_t e) {
+    set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return FA_ERR_RUNTIME;
+}
+
+int grow(void** ptr, size_t* cap, size_t need, const char* what) {
+    if (need <= *cap && *ptr != nullptr) return FA_OK;
+    if (*ptr != nullptr) {
+        hipError_t e = hipFree(*ptr);  // hipFree synchronises with outstanding work
+        *ptr = nullptr;
+        *cap = 0;
+        if (e != hipSuccess) return runtime_error(what, e);
+    }
+    size_t bytes = need < 256 ? 256 : need;
+    hipError_t e = hipMalloc(ptr, bytes);
+    if (e != hipSuccess) return runtime_error(what, e);
+    *cap = bytes;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" const char* fa_last_error(void) { return fa::last_error_cstr(); }
+
+extern "C" void fa_release(void) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (auto& kv : g_ws) {
+        (void)hipSetDevice(kv.first);
+        (void)hipDeviceSynchronize();
+        if (kv.second.dq_acc) (void)hipFree(kv.second.dq_acc);
+        if (kv.second.rowstat) (void)hipFree(kv.second.rowstat);
+        if (kv.second.items) (void)hipFree(kv.second.items);
+    }
+    g_ws.clear();
+    (void)hipSetDevice(cur);
+}
+
+extern "C" void fa_profile_enable(int on) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_profile = on != 0;
+}
+
+extern "C" int fa_profile_read(double* ms, int64_t* launches, int capacity) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    double sum[kKernels] = {0, 0, 0};
+    int64_t cnt[kKernels] = {0, 0, 0};
+    int status = kKernels;
+    for (auto& ev : g_events) {
+        float t = 0.f;
+        if (hipEventSynchronize(ev.stop) != hipSuccess || hipEventElapsedTime(&t, ev.start, ev.stop) != hipSuccess) {
+            set_error("fa_profile_read: event query failed");
+            status = -FA_ERR_RUNTIME;
+        } else {
+            sum[ev.kernel] += t;
+            cnt[ev.kernel] += 1;
+        }
+        g_event_pool.push_back(ev.start);
+        g_event_pool.push_back(ev.stop);
+    }
+    g_events.clear();
+    for (int i = 0; i < kKernels && i < capacity; ++i) {
+        if (ms) ms[i] = sum[i];
+        if (launches) launches[i] = cnt[i];
+    }
+    return status;
+}
+
+extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                             const fa_tensor_t* dy, const fa_tensor_t* y, const float* softmax_max,
+                             const float* softmax_sum, const fa_seqlens_t* cu_seqlens_q,
+                             const fa_seqlens_t* cu_seqlens_kv, int32_t atten_mode, int64_t pre_tokens,
+                             int64_t next_tokens, double keep_prob, const uint8_t* drop_mask, double scale,
+                             int64_t head_num, const fa_tensor_t* dq, const fa_tensor_t* dk,
+                             const fa_tensor_t* dv, void* stream) {
+    fa::clear_error();
+    // ---- null pointers (page: ACLNN_ERR_PARAM_NULLPTR) ----
+    const fa_tensor_t* all[8] = {q, k, v, dy, y, dq, dk, dv};
+    const char* names[8] = {"q", "k", "v", "dy", "y", "dq", "dk", "dv"};
+    for (int i = 0; i < 8; ++i) {
+        // an empty tensor (zero tokens) may carry a null data pointer
+        if (all[i] == nullptr || (all[i]->data == nullptr && all[i]->tokens != 0)) {
+            set_error(std::string(names[i]) + " is null");
+            return FA_ERR_NULLPTR;
+        }
+    }
+    if (softmax_max == nullptr || softmax_sum == nullptr) {
+        set_error("softmax_max / softmax_sum is null");
+        return FA_ERR_NULLPTR;
+    }
+    if (cu_seqlens_q == nullptr || cu_seqlens_q->cu == nullptr || cu_seqlens_kv == nullptr ||
+        cu_seqlens_kv->cu == nullptr) {
+        set_error("cu_seqlens_q / cu_seqlens_kv is null");
+        return FA_ERR_NULLPTR;
+    }
+    if (!(keep_prob > 0.0 && keep_prob <= 1.0)) {
+        set_error("keep_prob must be in (0, 1]");
+        return FA_ERR_INVALID;
+    }
+    if (keep_prob < 1.0 && drop_mask == nullptr) {
+        set_error("drop_mask is null while keep_prob < 1");
+        return FA_ERR_NULLPTR;
+    }
+    // ---- values (page: ACLNN_ERR_PARAM_INVALID) ----
+    for (int i = 0; i < 8; ++i) {
+        int st = check_tensor(all[i], names[i]);
+        if (st != FA_OK) return st;
+    }
+    for (int i = 1; i < 8; ++i) {
+        if (all[i]->dtype != q->dtype) {
+            set_error(std::string(names[i]) + ": dtype differs from q (all tensors share one dtype)");
+            return FA_ERR_INVALID;
+        }
+    }
+    if (head_num != q->heads) {
+        set_error("head_num must equal the N axis of q");
+        return FA_ERR_INVALID;
+    }
+    if (k->heads != v->heads || k->tokens != v->tokens) {
+        set_error("k and v must have equal shapes apart from D");
+        return FA_ERR_INVALID;
+    }
+    if (q->heads % k->heads != 0) {
+        set_error("q heads must be a multiple of k/v heads");
+        return FA_ERR_INVALID;
+    }
+    if (q->head_dim != k->head_dim || k->head_dim < v->head_dim) {
+        set_error("head dims must satisfy qD == kD >= vD");
+        return FA_ERR_INVALID;
+    }
+    if (dy->tokens != q->tokens || dy->heads != q->heads || dy->head_dim != q->head_dim ||
+        y->tokens != q->tokens || y->heads != q->heads || y->head_dim != q->head_dim) {
+        set_error("dy and y must have the shape of q");
+        return FA_ERR_INVALID;
+    }
+    if (dq->tokens != q->tokens || dq->heads != q->heads || dq->head_dim != q->head_dim ||
+        dk->tokens != k->tokens || dk->heads != k->heads || dk->head_dim != k->head_dim ||
+        dv->tokens != v->tokens || dv->heads != v->heads || dv->head_dim != v->head_dim) {
+        set_error("dq/dk/dv must have the shapes of q/k/v");
+        return FA_ERR_INVALID;
+    }
+    if (atten_mode < FA_MASK_NONE || atten_mode > FA_MASK_BAND) {
+        set_error("atten_mode must be 0 (none), 1 (causal) or 2 (band)");
+        return FA_ERR_INVALID;
+    }
+    if (!std::isfinite(scale)) {
+        set_error("scale must be finite");
+        return FA_ERR_INVALID;
+    }
+    int st = fa::check_seqlens(cu_seqlens_q, "cu_seqlens_q");
+    if (st != FA_OK) return st;
+    st = fa::check_seqlens(cu_seqlens_kv, "cu_seqlens_kv");
+    if (st != FA_OK) return st;
+    if (cu_seqlens_q->batch != cu_seqlens_kv->batch) {
+        set_error("cu_seqlens_q and cu_seqlens_kv must have equal batch counts");
+        return FA_ERR_INVALID;
+    }
+    const int64_t batch = cu_seqlens_q->batch;
+    if (cu_seqlens_q->cu[batch] != q->tokens || cu_seqlens_kv->cu[batch] != k->tokens) {
+        set_error("cu_seqlens must end at the token counts of q and k");
+        return FA_ERR_INVALID;
+    }
+    // ---- allowed by the page, not built ----
+    if (q->heads != k->heads) {
+        set_error("grouped heads (k/v heads < q heads) are not supported");
+        return FA_ERR_UNSUPPORTED;
+    }
+    if (v->head_dim != k->head_dim) {
+        set_error("v head_dim < k head_dim is not supported");
+        return FA_ERR_UNSUPPORTED;
+    }
+    if (q->head_dim != 64 && q->head_dim != 128) {
+        set_error("head_dim must be 64 or 128");
+        return FA_ERR_UNSUPPORTED;
+    }
+    for (int i = 0; i < 8; ++i) {
+        if (!aligned16(all[i])) {
+            set_error(std::string(names[i]) + ": data and strides must be 16-byte aligned");
+            return FA_ERR_UNSUPPORTED;
+        }
+    }
+
+    const int64_t tq = q->tokens;
+    const int64_t heads = q->heads;
+    const int d = static_cast<int>(q->head_dim);
+    if (tq == 0) return FA_OK;  // empty input: nothing to compute
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t dtype = q->dtype;
+    const int block_q = fa::block_q_for(dtype);
+
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return runtime_error("hipGetDevice", e);
+    Workspace& ws = g_ws[dev];
+
+    // work list, rebuilt only when the sequence layout or mask changes
+    std::vector<int64_t> key;
+    key.reserve(2 * (batch + 1) + 5);
+    key.push_back(atten_mode);
+    key.push_back(atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0);
+    key.push_back(atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0);
+    key.push_back(heads);
+    key.push_back(block_q);
+    key.insert(key.end(), cu_seqlens_q->cu, cu_seqlens_q->cu + batch + 1);
+    key.insert(key.end(), cu_seqlens_kv->cu, cu_seqlens_kv->cu + batch + 1);
+    if (key != ws.key) {
+        std::vector<fa_work_item_t> list;
+        const int64_t pre = atten_mode == FA_MASK_BAND ? pre_tokens : 0;
+        const int64_t nxt = atten_mode == FA_MASK_BAND ? next_tokens : 0;
+        const int64_t n = fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt,
+                                             heads, block_q, list);
+        size_t cap_bytes = ws.items_cap * sizeof(fa_work_item_t);
+        void* ptr = ws.items;
+        int g = grow(&ptr, &cap_bytes, static_cast<size_t>(n) * sizeof(fa_work_item_t), "work list");
+        ws.items = static_cast<fa_work_item_t*>(ptr);
+        ws.items_cap = cap_bytes / sizeof(fa_work_item_t);
+        if (g != FA_OK) {
+            ws.key.clear();
+            return g;
+        }
+        if (n > 0) {
+            // The previous list may still be read by kernels queued on this
+            // stream; wait for them, then copy synchronously (lists are small
+            // and reused by later calls with the same layout).
+            e = hipStreamSynchronize(s);
+            if (e != hipSuccess) {
+                ws.key.clear();
+                return runtime_error("stream synchronize", e);
+            }
+            e = hipMemcpy(ws.items, list.data(), static_cast<size_t>(n) * sizeof(fa_work_item_t),
+                          hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                ws.key.clear();
+                return runtime_error("work list upload", e);
+            }
+        }
+        ws.key = key;
+        ws.n_items = n;
+    }
+
+    {
+        void* ptr = ws.dq_acc;
+        int g = grow(&ptr, &ws.dq_acc_bytes, static_cast<size_t>(tq * heads * d) * sizeof(float), "dq accumulator");
+        ws.dq_acc = static_cast<float*>(ptr);
+        if (g != FA_OK) return g;
+        ptr = ws.rowstat;
+        g = grow(&ptr, &ws.rowstat_bytes, static_cast<size_t>(tq * heads) * sizeof(float2), "row statistics");
+        ws.rowstat = static_cast<float2*>(ptr);
+        if (g != FA_OK) return g;
+    }
+
+    fa::TensorArg tdy{dy->data, dy->stride_t, dy->stride_h};
+    fa::TensorArg ty{y->data, y->stride_t, y->stride_h};
+    e = timed(0, s, [&] {
+        return fa::launch_preprocess(dtype, d, tdy, ty, softmax_max, softmax_sum, ws.rowstat, ws.dq_acc, tq, heads, s);
+    });
+    if (e != hipSuccess) return runtime_error("preprocess launch", e);
+
+    if (ws.n_items > 0) {
+        fa::MainArgs a;
+        a.q = {q->data, q->stride_t, q->stride_h};
+        a.k = {k->data, k->stride_t, k->stride_h};
+        a.v = {v->data, v->stride_t, v->stride_h};
+        a.dy = tdy;
+        a.dk = dk->data;
+        a.dk_st = dk->stride_t;
+        a.dk_sh = dk->stride_h;
+        a.dv = dv->data;
+        a.dv_st = dv->stride_t;
+        a.dv_sh = dv->stride_h;
+        a.rowstat = ws.rowstat;
+        a.dq_acc = ws.dq_acc;
+        a.items = ws.items;
+        a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
+        a.tq = static_cast<int32_t>(tq);
+        a.heads = static_cast<int32_t>(heads);
+        a.mode = atten_mode;
+        a.pre = static_cast<int32_t>(atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0);
+        a.nxt = static_cast<int32_t>(atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0);
+        a.exp_scale = static_cast<float>(scale * 1.4426950408889634);
+        a.inv_keep = static_cast<float>(1.0 / keep_prob);
+        a.scale = static_cast<float>(scale);
+        e = timed(1, s, [&] { return fa::launch_main(dtype, d, keep_prob < 1.0, a, ws.n_items, s); });
+        if (e != hipSuccess) return runtime_error("main kernel launch", e);
+    }
+
+    e = timed(2, s, [&] {
+        return fa::launch_convert(dtype, d, ws.dq_acc, dq->data, dq->stride_t, dq->stride_h, tq, heads,
+                                  static_cast<float>(scale), s);
+    });
+    if (e != hipSuccess) return runtime_error("convert launch", e);
+    return FA_OK;
+}

@@ -1,0 +1,52 @@
+// Launchers of the gfx950 kernels (defined in fa_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fa_varlen.h"
+
+namespace fa {
+
+struct TensorArg {
+    const void* data;
+    int64_t stride_t;
+    int64_t stride_h;
+};
+
+// Row pass: delta[n, t] = sum_d dY * Y (fp32), beta[n, t] = max*log2(e) + log2(sum),
+// stored as float2 {delta, beta} in rowstat[n * tq + t]; also zeroes dq_acc [tq, N, D].
+hipError_t launch_preprocess(int32_t dtype, int head_dim, TensorArg dy, TensorArg y,
+                             const float* softmax_max, const float* softmax_sum, float2* rowstat,
+                             float* dq_acc, int64_t tq, int64_t heads, hipStream_t stream);
+
+struct MainArgs {
+    TensorArg q, k, v, dy;
+    void* dk;
+    int64_t dk_st, dk_sh;
+    void* dv;
+    int64_t dv_st, dv_sh;
+    const float2* rowstat;
+    float* dq_acc;
+    const fa_work_item_t* items;
+    const uint8_t* drop_mask;
+    int32_t tq;
+    int32_t heads;
+    int32_t mode;
+    int32_t pre;     // clamped window bounds
+    int32_t nxt;
+    float exp_scale;  // scale * log2(e)
+    float inv_keep;   // 1 / keep_prob
+    float scale;      // folded into dK
+};
+
+// KV-block-major backward over n_items work items x heads.
+hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs& a, int64_t n_items,
+                       hipStream_t stream);
+
+// dq[t, n, :] = scale * dq_acc[t, n, :] converted to the output dtype.
+hipError_t launch_convert(int32_t dtype, int head_dim, const float* dq_acc, void* dq, int64_t dq_st,
+                          int64_t dq_sh, int64_t tq, int64_t heads, float scale, hipStream_t stream);
+
+}  // namespace fa
