@@ -40,7 +40,10 @@ def assert_close(name, g, o, dtype):
     err = np.linalg.norm(g - o)
     mx = np.max(np.abs(o)) if o.size else 0.0
     if ref == 0.0:
-        assert err == 0.0, f"{name}: expected exact zeros, |err|={err}"
+        # The relative criterion is undefined for an all-zero reference.  Where the
+        # zero comes from cancellation (dP - D with Ps = 1) fp32 leaves a residue of
+        # order 1e-7; rows with no admitted key are checked for exact zeros separately.
+        assert np.max(np.abs(g)) <= 1e-5, f"{name}: expected zeros, max |gpu| = {np.max(np.abs(g)):.3e}"
         return
     rel = err / ref
     assert rel <= tol_for(dtype), f"{name}: relative Frobenius error {rel:.3e}"
