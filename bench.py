@@ -105,6 +105,9 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (default 3)")
     ap.add_argument("--cpu-units", type=int, default=16, help="(sequence, head) units for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="copy this many MiB device-to-device once before the timed steps (a plain copy of "
+                         "known size, for scaling HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,6 +145,15 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.calibration_copy_mib > 0:
+        nel = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy of {args.calibration_copy_mib} MiB done")
     B.profile_read()  # drop anything recorded before the timed region
     B.profile_enable(True)
     torch.cuda.synchronize()

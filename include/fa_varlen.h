@@ -131,46 +131,54 @@ const char* fa_last_error(void);
  * the device first).  The next fa_varlen_bwd call re-allocates them. */
 void fa_release(void);
 
-/* One work item of the main kernel: a block of FA_BLOCK_KV keys of one
- * sequence and the range of FA_BLOCK_Q-row query tiles that can see it. */
+/* One work item: a block of rows of one sequence that a workgroup keeps
+ * resident (keys, or queries), and the range of tiles of the other side that
+ * hold at least one admitted (query, key) pair with it. */
 typedef struct {
     int32_t q_start;     /* first token of the sequence in q/dy/y/dq */
     int32_t kv_start;    /* first token of the sequence in k/v/dk/dv */
     int32_t len_q;       /* Lq_b */
     int32_t len_kv;      /* Lkv_b */
-    int32_t kv_block;    /* block index: keys [kv_block*FA_BLOCK_KV, +FA_BLOCK_KV) */
-    int32_t tile_begin;  /* first query tile (rows tile*block_q ...) with an admitted pair */
-    int32_t tile_end;    /* one past the last; == tile_begin: block sees no query */
+    int32_t block;       /* resident block index: rows [block*block_rows, +block_rows) */
+    int32_t tile_begin;  /* first walked tile (rows tile*tile_rows ...) with an admitted pair */
+    int32_t tile_end;    /* one past the last; == tile_begin: the block sees nothing */
     int32_t seq;         /* sequence index b */
     int64_t drop_base;   /* bit index of element (0, 0) of head 0 of this sequence */
 } fa_work_item_t;
 
-#define FA_BLOCK_KV 128
+/* Item kinds of fa_varlen_worklist. */
+enum {
+    FA_ITEMS_KEY_BLOCKS = 0,   /* resident key blocks walking query tiles (dK, dV) */
+    FA_ITEMS_QUERY_BLOCKS = 1  /* resident query blocks walking key tiles (dQ) */
+};
 
 /*
- * fa_varlen_worklist -- the host-side work list the backward launches over
+ * fa_varlen_worklist -- a host-side work list the backward launches over
  * (exposed for inspection and testing; no device work).
  *
- * For every sequence with Lkv_b > 0 and every block of FA_BLOCK_KV keys, the
- * item's tile range covers exactly the query tiles of block_q rows that hold
- * at least one admitted (query, key) pair with a key in the block.  Blocks
- * that no query sees are kept with an empty range so that their dK/dV rows
- * are written as zeros.  Items are ordered longest first (by tile count).
+ * kind FA_ITEMS_KEY_BLOCKS: one item per block of block_rows keys of every
+ * sequence with Lkv_b > 0; its tile range covers exactly the query tiles of
+ * tile_rows rows that hold an admitted pair with a key of the block.
+ * kind FA_ITEMS_QUERY_BLOCKS: one item per block of block_rows queries of
+ * every sequence with Lq_b > 0; its range covers exactly the key tiles of
+ * tile_rows rows that hold a key admitted by some query of the block.
+ * Blocks with an empty range are kept so their outputs are written as zeros.
+ * Items are ordered longest range first.
  *
- * block_q: the query tile height (64 for 16-bit types, 32 for FA_F32).
  * items: HOST array of capacity entries, may be NULL to only count.
  * Returns the number of items (>= 0), or -FA_ERR_* on invalid input.
  */
 int64_t fa_varlen_worklist(const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
                            int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens,
-                           int64_t heads, int32_t block_q,
+                           int64_t heads, int32_t kind, int32_t block_rows, int32_t tile_rows,
                            fa_work_item_t* items, int64_t capacity);
 
 /*
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
  * fa_varlen_bwd call records a pair of HIP events around each of its kernels
- * on the call's stream: index 0 the row preprocess, 1 the main backward
- * kernel, 2 the dQ convert.
+ * on the call's stream: index 0 the row preprocess, 1 the main backward work
+ * (for bf16 / fp16 the dK/dV and dQ kernels together), 2 the dQ convert (fp32
+ * inputs only).
  */
 void fa_profile_enable(int on);
 

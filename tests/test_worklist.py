@@ -10,36 +10,41 @@ from oracle import fa_oracle as O
 from variable_length_flashattention_fa_amd import binding as B
 from variable_length_flashattention_fa_amd.inputs_forward import pair_count
 
-BKV = B.FA_BLOCK_KV
-
-
-def _check(lq, lkv, mode, pre, nxt, heads, block_q):
+def _check(lq, lkv, mode, pre, nxt, heads, block_rows, tile_rows, kind):
     cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
     cu_k = np.concatenate([[0], np.cumsum(lkv)]).astype(np.int64)
-    items = B.worklist(cu_q, cu_k, mode, pre, nxt, heads, block_q)
-    # one item per key block of every sequence with keys
-    expect_blocks = {(b, jb) for b in range(len(lq)) for jb in range((lkv[b] + BKV - 1) // BKV)}
-    got_blocks = [(it["seq"], it["kv_block"]) for it in items]
+    items = B.worklist(cu_q, cu_k, mode, pre, nxt, heads, kind, block_rows, tile_rows)
+    by_key = kind == B.FA_ITEMS_KEY_BLOCKS
+    resident = lkv if by_key else lq
+    # one item per resident block of every sequence
+    expect_blocks = {(b, blk) for b in range(len(lq)) for blk in range((resident[b] + block_rows - 1) // block_rows)}
+    got_blocks = [(it["seq"], it["block"]) for it in items]
     assert len(got_blocks) == len(set(got_blocks))
     assert set(got_blocks) == expect_blocks
     # longest first
     spans = [it["tile_end"] - it["tile_begin"] for it in items]
     assert spans == sorted(spans, reverse=True)
     bases = O.dropout_bit_bases(cu_q, cu_k, heads)
-    by_block = {(it["seq"], it["kv_block"]): it for it in items}
+    index = {(it["seq"], it["block"]): it for it in items}
     for b in range(len(lq)):
         a = O.admit_mask(lq[b], lkv[b], mode, pre, nxt) if lq[b] and lkv[b] else np.zeros((lq[b], lkv[b]), bool)
-        for jb in range((lkv[b] + BKV - 1) // BKV):
-            it = by_block[(b, jb)]
+        if not by_key:
+            a = a.T  # rows: keys of the walked side ... resident queries become columns
+        for blk in range((resident[b] + block_rows - 1) // block_rows):
+            it = index[(b, blk)]
             assert it["q_start"] == cu_q[b] and it["kv_start"] == cu_k[b]
             assert it["len_q"] == lq[b] and it["len_kv"] == lkv[b]
             assert it["drop_base"] == bases[b]
-            blk = a[:, jb * BKV:(jb + 1) * BKV]
-            rows = np.where(blk.any(axis=1))[0]
-            tiles = set((rows // block_q).tolist())
+            sub = a[:, blk * block_rows:(blk + 1) * block_rows]
+            walked = np.where(sub.any(axis=1))[0]
+            tiles = set((walked // tile_rows).tolist())
             got = set(range(it["tile_begin"], it["tile_end"]))
             # exactly the tiles that hold an admitted pair: every pair covered, no dead tile
-            assert got == tiles, (b, jb, sorted(got), sorted(tiles))
+            assert got == tiles, (b, blk, sorted(got), sorted(tiles))
+
+
+KINDS = [(B.FA_ITEMS_KEY_BLOCKS, 128, 64), (B.FA_ITEMS_KEY_BLOCKS, 128, 32),
+         (B.FA_ITEMS_QUERY_BLOCKS, 256, 32), (B.FA_ITEMS_QUERY_BLOCKS, 64, 64)]
 
 
 CASES = [
@@ -57,27 +62,30 @@ CASES = [
 
 
 @pytest.mark.parametrize("lq,lkv,mode,pre,nxt", CASES)
-@pytest.mark.parametrize("block_q", [32, 64])
-def test_worklist_covers_exactly_admitted_tiles(lq, lkv, mode, pre, nxt, block_q):
-    _check(list(lq), list(lkv if lkv is not None else lq), mode, pre, nxt, heads=3, block_q=block_q)
+@pytest.mark.parametrize("kind,block_rows,tile_rows", KINDS)
+def test_worklist_covers_exactly_admitted_tiles(lq, lkv, mode, pre, nxt, kind, block_rows, tile_rows):
+    _check(list(lq), list(lkv if lkv is not None else lq), mode, pre, nxt, 3, block_rows, tile_rows, kind)
 
 
 def test_worklist_random_cases():
     rng = np.random.default_rng(0)
-    for _ in range(30):
+    for _ in range(40):
         b = int(rng.integers(1, 6))
         lq = rng.integers(0, 400, b).tolist()
         lkv = lq if rng.random() < 0.5 else rng.integers(0, 400, b).tolist()
         mode = int(rng.integers(0, 3))
         pre, nxt = int(rng.integers(-20, 300)), int(rng.integers(-20, 300))
-        _check(lq, lkv, mode, pre, nxt, heads=2, block_q=int(rng.choice([32, 64])))
+        kind, block_rows, tile_rows = KINDS[int(rng.integers(len(KINDS)))]
+        _check(lq, lkv, mode, pre, nxt, 2, block_rows, tile_rows, kind)
 
 
 def test_worklist_rejects_bad_input():
     with pytest.raises(B.FaError):
-        B.worklist([0, 5, 3], [0, 5, 3], 0, 0, 0, 1, 64)
+        B.worklist([0, 5, 3], [0, 5, 3], 0, 0, 0, 1, B.FA_ITEMS_KEY_BLOCKS, 128, 64)
     with pytest.raises(B.FaError):
-        B.worklist([0, 5], [0, 5, 6], 0, 0, 0, 1, 64)
+        B.worklist([0, 5], [0, 5, 6], 0, 0, 0, 1, B.FA_ITEMS_KEY_BLOCKS, 128, 64)
+    with pytest.raises(B.FaError):
+        B.worklist([0, 5], [0, 5], 0, 0, 0, 1, 7, 128, 64)
 
 
 @pytest.mark.parametrize("lq,lkv,mode,pre,nxt", CASES)

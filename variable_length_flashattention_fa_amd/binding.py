@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libfa_varlen.so")
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_NULLPTR, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_RUNTIME = 0, 1, 2, 3, 4
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_BAND = 0, 1, 2
-FA_BLOCK_KV = 128
+FA_ITEMS_KEY_BLOCKS, FA_ITEMS_QUERY_BLOCKS = 0, 1
 
 _DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
@@ -37,7 +37,7 @@ class FaSeqlens(ctypes.Structure):
 
 class FaWorkItem(ctypes.Structure):
     _fields_ = [("q_start", ctypes.c_int32), ("kv_start", ctypes.c_int32), ("len_q", ctypes.c_int32),
-                ("len_kv", ctypes.c_int32), ("kv_block", ctypes.c_int32), ("tile_begin", ctypes.c_int32),
+                ("len_kv", ctypes.c_int32), ("block", ctypes.c_int32), ("tile_begin", ctypes.c_int32),
                 ("tile_end", ctypes.c_int32), ("seq", ctypes.c_int32), ("drop_base", ctypes.c_int64)]
 
 
@@ -74,7 +74,8 @@ def load(path: Optional[str] = None):
     lib.fa_release.argtypes = []
     lib.fa_release.restype = None
     lib.fa_varlen_worklist.argtypes = [S, S, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                       ctypes.c_int32, ctypes.POINTER(FaWorkItem), ctypes.c_int64]
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(FaWorkItem),
+                                       ctypes.c_int64]
     lib.fa_varlen_worklist.restype = ctypes.c_int64
     lib.fa_profile_enable.argtypes = [ctypes.c_int]
     lib.fa_profile_enable.restype = None
@@ -169,18 +170,18 @@ def varlen_bwd(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlen
 
 
 def worklist(cu_seqlens_q, cu_seqlens_kv, atten_mode: int, pre_tokens: int, next_tokens: int, heads: int,
-             block_q: int):
-    """The host work list as a list of dicts (no device work)."""
+             kind: int, block_rows: int, tile_rows: int):
+    """A host work list (FA_ITEMS_KEY_BLOCKS or FA_ITEMS_QUERY_BLOCKS) as a list of dicts."""
     lib = load()
     sq, aq = _seqlens(cu_seqlens_q)
     sk, ak = _seqlens(cu_seqlens_kv)
-    n = lib.fa_varlen_worklist(ctypes.byref(sq), ctypes.byref(sk), int(atten_mode), int(pre_tokens),
-                               int(next_tokens), int(heads), int(block_q), None, 0)
+    args = (ctypes.byref(sq), ctypes.byref(sk), int(atten_mode), int(pre_tokens), int(next_tokens), int(heads),
+            int(kind), int(block_rows), int(tile_rows))
+    n = lib.fa_varlen_worklist(*args, None, 0)
     if n < 0:
         raise FaError(-n, last_error())
     buf = (FaWorkItem * max(n, 1))()
-    lib.fa_varlen_worklist(ctypes.byref(sq), ctypes.byref(sk), int(atten_mode), int(pre_tokens),
-                           int(next_tokens), int(heads), int(block_q), buf, n)
+    lib.fa_varlen_worklist(*args, buf, n)
     del aq, ak
     return [{f: getattr(buf[i], f) for f, _ in FaWorkItem._fields_} for i in range(n)]
 

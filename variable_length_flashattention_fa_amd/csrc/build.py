@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libfa_varlen.so"
 
-HIP_SOURCES = ["fa_kernels.hip", "fa_api.cpp"]
+HIP_SOURCES = ["fa_kernels.hip", "fa_bwd16.hip", "fa_api.cpp"]
 CXX_SOURCES = ["fa_worklist.cpp"]
 
 

@@ -72,9 +72,10 @@ struct Workspace {
     size_t rowstat_bytes = 0;
     fa_work_item_t* items = nullptr;
     size_t items_cap = 0;
-    // cached work list: key and host copy
+    // cached work lists: their key and item counts (key-block items, then query-block items)
     std::vector<int64_t> key;
     int64_t n_items = 0;
+    int64_t n_q_items = 0;
 };
 
 std::mutex g_mutex;
@@ -306,7 +307,9 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t dtype = q->dtype;
-    const int block_q = fa::block_q_for(dtype);
+    const bool wide = dtype == FA_F32;  // fp32 runs the single-kernel path with a dQ accumulator
+    const int64_t pre = atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0;
+    const int64_t nxt = atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0;
 
     std::lock_guard<std::mutex> lock(g_mutex);
     int dev = 0;
@@ -314,22 +317,32 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     if (e != hipSuccess) return runtime_error("hipGetDevice", e);
     Workspace& ws = g_ws[dev];
 
-    // work list, rebuilt only when the sequence layout or mask changes
+    // work lists, rebuilt only when the sequence layout, mask or path changes:
+    // key-block items first, then (16-bit path) query-block items
     std::vector<int64_t> key;
     key.reserve(2 * (batch + 1) + 5);
     key.push_back(atten_mode);
-    key.push_back(atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0);
-    key.push_back(atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0);
+    key.push_back(pre);
+    key.push_back(nxt);
     key.push_back(heads);
-    key.push_back(block_q);
+    key.push_back(wide ? 1 : 0);
     key.insert(key.end(), cu_seqlens_q->cu, cu_seqlens_q->cu + batch + 1);
     key.insert(key.end(), cu_seqlens_kv->cu, cu_seqlens_kv->cu + batch + 1);
     if (key != ws.key) {
-        std::vector<fa_work_item_t> list;
-        const int64_t pre = atten_mode == FA_MASK_BAND ? pre_tokens : 0;
-        const int64_t nxt = atten_mode == FA_MASK_BAND ? next_tokens : 0;
-        const int64_t n = fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt,
-                                             heads, block_q, list);
+        std::vector<fa_work_item_t> list, qlist;
+        if (wide) {
+            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
+                               FA_ITEMS_KEY_BLOCKS, fa::kBlockKv32, fa::kTileQ32, list);
+        } else {
+            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
+                               FA_ITEMS_KEY_BLOCKS, fa::FA16_DKDV_BLOCK, fa::FA16_DKDV_TILE_Q, list);
+            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
+                               FA_ITEMS_QUERY_BLOCKS, fa::FA16_DQ_BLOCK, fa::FA16_DQ_TILE_K, qlist);
+        }
+        const int64_t n_kv = static_cast<int64_t>(list.size());
+        const int64_t n_q = static_cast<int64_t>(qlist.size());
+        list.insert(list.end(), qlist.begin(), qlist.end());
+        const int64_t n = n_kv + n_q;
         size_t cap_bytes = ws.items_cap * sizeof(fa_work_item_t);
         void* ptr = ws.items;
         int g = grow(&ptr, &cap_bytes, static_cast<size_t>(n) * sizeof(fa_work_item_t), "work list");
@@ -356,26 +369,74 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
             }
         }
         ws.key = key;
-        ws.n_items = n;
+        ws.n_items = n_kv;
+        ws.n_q_items = n_q;
     }
 
     {
-        void* ptr = ws.dq_acc;
-        int g = grow(&ptr, &ws.dq_acc_bytes, static_cast<size_t>(tq * heads * d) * sizeof(float), "dq accumulator");
-        ws.dq_acc = static_cast<float*>(ptr);
-        if (g != FA_OK) return g;
-        ptr = ws.rowstat;
-        g = grow(&ptr, &ws.rowstat_bytes, static_cast<size_t>(tq * heads) * sizeof(float2), "row statistics");
+        void* ptr = ws.rowstat;
+        int g = grow(&ptr, &ws.rowstat_bytes, static_cast<size_t>(tq * heads) * sizeof(float2), "row statistics");
         ws.rowstat = static_cast<float2*>(ptr);
         if (g != FA_OK) return g;
+        if (wide) {
+            ptr = ws.dq_acc;
+            g = grow(&ptr, &ws.dq_acc_bytes, static_cast<size_t>(tq * heads * d) * sizeof(float), "dq accumulator");
+            ws.dq_acc = static_cast<float*>(ptr);
+            if (g != FA_OK) return g;
+        }
     }
 
     fa::TensorArg tdy{dy->data, dy->stride_t, dy->stride_h};
     fa::TensorArg ty{y->data, y->stride_t, y->stride_h};
     e = timed(0, s, [&] {
-        return fa::launch_preprocess(dtype, d, tdy, ty, softmax_max, softmax_sum, ws.rowstat, ws.dq_acc, tq, heads, s);
+        return fa::launch_preprocess(dtype, d, tdy, ty, softmax_max, softmax_sum, ws.rowstat,
+                                     wide ? ws.dq_acc : nullptr, tq, heads, s);
     });
     if (e != hipSuccess) return runtime_error("preprocess launch", e);
+
+    const float exp_scale = static_cast<float>(scale * 1.4426950408889634);
+    const float inv_keep = static_cast<float>(1.0 / keep_prob);
+    if (!wide) {
+        fa::Bwd16Args a;
+        a.q = q->data;
+        a.k = k->data;
+        a.v = v->data;
+        a.dy = dy->data;
+        a.q_st = q->stride_t;
+        a.q_sh = q->stride_h;
+        a.k_st = k->stride_t;
+        a.k_sh = k->stride_h;
+        a.v_st = v->stride_t;
+        a.v_sh = v->stride_h;
+        a.dy_st = dy->stride_t;
+        a.dy_sh = dy->stride_h;
+        a.dq = dq->data;
+        a.dk = dk->data;
+        a.dv = dv->data;
+        a.dq_st = dq->stride_t;
+        a.dq_sh = dq->stride_h;
+        a.dk_st = dk->stride_t;
+        a.dk_sh = dk->stride_h;
+        a.dv_st = dv->stride_t;
+        a.dv_sh = dv->stride_h;
+        a.rowstat = ws.rowstat;
+        a.items_kv = ws.items;
+        a.items_q = ws.items + ws.n_items;
+        a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
+        a.tq = static_cast<int32_t>(tq);
+        a.heads = static_cast<int32_t>(heads);
+        a.mode = atten_mode;
+        a.pre = static_cast<int32_t>(pre);
+        a.nxt = static_cast<int32_t>(nxt);
+        a.exp_scale = exp_scale;
+        a.inv_keep = inv_keep;
+        a.scale = static_cast<float>(scale);
+        e = timed(1, s, [&] {
+            return fa::launch_bwd16(dtype, d, keep_prob < 1.0, a, ws.n_items, ws.n_q_items, s);
+        });
+        if (e != hipSuccess) return runtime_error("backward kernel launch", e);
+        return FA_OK;
+    }
 
     if (ws.n_items > 0) {
         fa::MainArgs a;
@@ -396,10 +457,10 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         a.tq = static_cast<int32_t>(tq);
         a.heads = static_cast<int32_t>(heads);
         a.mode = atten_mode;
-        a.pre = static_cast<int32_t>(atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0);
-        a.nxt = static_cast<int32_t>(atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0);
-        a.exp_scale = static_cast<float>(scale * 1.4426950408889634);
-        a.inv_keep = static_cast<float>(1.0 / keep_prob);
+        a.pre = static_cast<int32_t>(pre);
+        a.nxt = static_cast<int32_t>(nxt);
+        a.exp_scale = exp_scale;
+        a.inv_keep = inv_keep;
         a.scale = static_cast<float>(scale);
         e = timed(1, s, [&] { return fa::launch_main(dtype, d, keep_prob < 1.0, a, ws.n_items, s); });
         if (e != hipSuccess) return runtime_error("main kernel launch", e);

@@ -13,9 +13,8 @@ namespace fa {
 void set_error(const std::string& msg);
 void clear_error();
 
-// Query tile height per element type: 64 rows for 16-bit types, 32 for fp32
-// (fp32 operands double the LDS footprint of every staged tile).
-inline int block_q_for(int32_t dtype) { return dtype == FA_F32 ? 32 : 64; }
+// Query tile height of the fp32 kernel (fp32 operands double every staged tile).
+constexpr int kTileQ32 = 32;
 
 // Window bounds are clamped to +-2^24: T <= 2^20 on the page, so any wider
 // window admits the same keys, and int32 index math in the kernel cannot
@@ -29,10 +28,13 @@ inline int64_t clamp_window(int64_t x) {
 // Returns FA_OK or an error status (message set).
 int check_seqlens(const fa_seqlens_t* s, const char* name);
 
-// Builds the work list (see fa_varlen_worklist in fa_varlen.h).  Inputs must
+// Key rows per workgroup of the fp32 kernel.
+constexpr int kBlockKv32 = 128;
+
+// Builds a work list (see fa_varlen_worklist in fa_varlen.h).  Inputs must
 // already be validated.  Returns the item count.
-int64_t build_worklist(const int64_t* cu_q, const int64_t* cu_kv, int64_t batch, int32_t mode,
-                       int64_t pre, int64_t nxt, int64_t heads, int32_t block_q,
+int64_t build_worklist(const int64_t* cu_q, const int64_t* cu_kv, int64_t batch, int32_t mode, int64_t pre,
+                       int64_t nxt, int64_t heads, int32_t kind, int32_t block_rows, int32_t tile_rows,
                        std::vector<fa_work_item_t>& out);
 
 }  // namespace fa

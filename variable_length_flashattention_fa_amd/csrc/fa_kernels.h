@@ -16,7 +16,8 @@ struct TensorArg {
 };
 
 // Row pass: delta[n, t] = sum_d dY * Y (fp32), beta[n, t] = max*log2(e) + log2(sum),
-// stored as float2 {delta, beta} in rowstat[n * tq + t]; also zeroes dq_acc [tq, N, D].
+// stored as float2 {delta, beta} in rowstat[n * tq + t]; also zeroes the head-major
+// dq_acc [N, tq, D] when dq_acc is not null.
 hipError_t launch_preprocess(int32_t dtype, int head_dim, TensorArg dy, TensorArg y,
                              const float* softmax_max, const float* softmax_sum, float2* rowstat,
                              float* dq_acc, int64_t tq, int64_t heads, hipStream_t stream);
@@ -45,8 +46,36 @@ struct MainArgs {
 hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs& a, int64_t n_items,
                        hipStream_t stream);
 
-// dq[t, n, :] = scale * dq_acc[t, n, :] converted to the output dtype.
+// dq[t, n, :] = scale * dq_acc[n, t, :] converted to the output dtype.
 hipError_t launch_convert(int32_t dtype, int head_dim, const float* dq_acc, void* dq, int64_t dq_st,
                           int64_t dq_sh, int64_t tq, int64_t heads, float scale, hipStream_t stream);
+
+// ---- 16-bit path: dK/dV and dQ kernels without atomics ----
+constexpr int FA16_DKDV_BLOCK = 128;  // keys per dK/dV workgroup
+constexpr int FA16_DKDV_TILE_Q = 64;  // query rows per dK/dV step
+constexpr int FA16_DQ_BLOCK = 256;    // queries per dQ workgroup
+constexpr int FA16_DQ_TILE_K = 32;    // key rows per dQ step
+
+struct Bwd16Args {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dy;
+    int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, dy_st, dy_sh;
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh;
+    const float2* rowstat;
+    const fa_work_item_t* items_kv;  // key-block items (FA16_DKDV_BLOCK keys, FA16_DKDV_TILE_Q tiles)
+    const fa_work_item_t* items_q;   // query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles)
+    const uint8_t* drop_mask;
+    int32_t tq, heads, mode, pre, nxt;
+    float exp_scale, inv_keep, scale;
+};
+
+// dK/dV kernel over n_kv_items x heads, then dQ kernel over n_q_items x heads.
+hipError_t launch_bwd16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_kv_items,
+                        int64_t n_q_items, hipStream_t stream);
 
 }  // namespace fa

@@ -114,10 +114,12 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
         const Chunk<T> b = *reinterpret_cast<const Chunk<T>*>(y + t * y_st + n * y_sh + sub * VEC);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) part += static_cast<float>(a.e[e]) * static_cast<float>(b.e[e]);
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4* acc = reinterpret_cast<f32x4*>(dq_acc + r * D + sub * VEC);
+        if (dq_acc != nullptr) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4* acc = reinterpret_cast<f32x4*>(dq_acc + (static_cast<int64_t>(n) * tq + t) * D + sub * VEC);
 #pragma unroll
-        for (int e = 0; e < VEC / 4; ++e) acc[e] = z;
+            for (int e = 0; e < VEC / 4; ++e) acc[e] = z;
+        }
     }
 #pragma unroll
     for (int m = TPR / 2; m > 0; m >>= 1) part += __shfl_xor(part, m, TPR);
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
     if (r >= tq * heads) return;
     const int64_t t = r / heads;
     const int n = static_cast<int>(r - t * heads);
-    const f32x4* src = reinterpret_cast<const f32x4*>(acc + r * D + sub * VEC);
+    const f32x4* src = reinterpret_cast<const f32x4*>(acc + (static_cast<int64_t>(n) * tq + t) * D + sub * VEC);
     Chunk<T> out;
 #pragma unroll
     for (int e = 0; e < VEC / 4; ++e) {
@@ -182,8 +184,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     using vec = typename E::vec;
     constexpr int KL = E::KL;
     constexpr int KS = 2 * KL;                      // MFMA K
-    constexpr int BQ = sizeof(T) == 4 ? 32 : 64;    // query tile rows
-    constexpr int BKV = FA_BLOCK_KV;                // key block rows (4 waves x 32)
+    constexpr int BQ = sizeof(T) == 4 ? 32 : 64;    // query tile rows (fp32 lists use 32)
+    constexpr int BKV = 128;                        // key block rows (4 waves x 32)
     constexpr int MT = BQ / 32;                     // 32-row query sub-tiles
     constexpr int NT = D / 32;                      // 32-column head-dim sub-tiles
     constexpr int PADE = 16 / sizeof(T);            // 16-byte row padding
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     const int L = it.len_q;
     const int K = it.len_kv;
     const int off = K - L;
-    const int j0 = it.kv_block * BKV;
+    const int j0 = it.block * BKV;
     const int jw = j0 + 32 * w + col;  // this lane's key (sequence coordinates) in S / P
 
     const T* __restrict__ gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
             for (int a = 0; a < 16; ++a) {
                 const int i = q0 + mq * 32 + acc_row(a, h);
                 if (i < L) {
-                    float* dst = p.dq_acc + (static_cast<int64_t>(it.q_start + i) * p.heads + n) * D + nd * 32 + col;
+                    float* dst = p.dq_acc + (static_cast<int64_t>(n) * p.tq + it.q_start + i) * D + nd * 32 + col;
                     unsafeAtomicAdd(dst, acc[a]);
                 }
             }
@@ -415,299 +417,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
             if (j < K) {
                 gdk[static_cast<int64_t>(j) * p.dk_st + nt * 32 + col] = cvt<T>(accK[nt][a] * p.scale);
                 gdv[static_cast<int64_t>(j) * p.dv_st + nt * 32 + col] = cvt<T>(accV[nt][a]);
-            }
-        }
-    }
-}
-
-// ----------------------------------------------------------------------------
-// main kernel, 16-bit inputs: transposing LDS reads instead of transposed copies
-// ----------------------------------------------------------------------------
-//
-// gfx950's ds_read_b64_tr_b16 works on groups of 16 lanes: lane j of a group
-// supplies the address of 4 consecutive 16-bit values, and lane i of the group
-// receives element (i % 4) of the value quartets of lanes 4e + i/4, e = 0..3.
-// With lane j pointing at row r0 + j/4, columns c0 + 4*(j%4) of a row-major
-// tile X, lane i therefore receives X[r0 + e][c0 + i], e = 0..3: four
-// consecutive rows of one column, which is the MFMA operand layout for a
-// contraction over the row index.  Every operand that contracts over query
-// rows (dV, dK) or key rows (dQ) is read this way from row-major tiles.
-
-typedef short s16x4 __attribute__((vector_size(8)));
-typedef short s16x8 __attribute__((vector_size(16)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-template <typename T>
-__device__ __forceinline__ s16x4 ds_read_tr(const T* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
-
-// Operand of 8 values: X[r0 + e][c] for e = 0..3 and X[r0 + 4 + e'][c] ...
-// assembled from two transposing reads (rows r0..r0+3 and r1..r1+3).
-template <typename vec, typename T>
-__device__ __forceinline__ vec tr_operand(const T* base, int pitch, int r0, int r1, int c0, int i) {
-    const T* a = base + (r0 + (i >> 2)) * pitch + c0 + 4 * (i & 3);
-    const T* b = base + (r1 + (i >> 2)) * pitch + c0 + 4 * (i & 3);
-    const s16x4 lo = ds_read_tr(a);
-    const s16x4 hi = ds_read_tr(b);
-    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(vec, v);
-}
-
-template <typename T>
-__device__ __forceinline__ s16x4 pack4(float a, float b, float c, float d) {
-    T t[4] = {static_cast<T>(a), static_cast<T>(b), static_cast<T>(c), static_cast<T>(d)};
-    return __builtin_bit_cast(s16x4, t);
-}
-
-template <typename T, int D, bool DROP>
-__global__ __launch_bounds__(256, 1) void bwd_main_tr16_kernel(const DevArgs p) {
-    using E = Elem<T>;
-    using vec = typename E::vec;
-    constexpr int BQ = 64;                  // query tile rows
-    constexpr int BKV = FA_BLOCK_KV;        // key block rows (4 waves x 32)
-    constexpr int MT = BQ / 32;             // 32-row query sub-tiles per wave
-    constexpr int NT = D / 32;              // 32-column head-dim sub-tiles
-    constexpr int PQ = D + 16;              // Q / dY / K tile pitch: 4 rows span 32 banks apart
-    constexpr int PS = BQ + 8;              // dS^T pitch ([key][query])
-    constexpr int CPR = D / 8;              // 16-byte chunks per row
-    constexpr int CPT = BQ * CPR / 256;     // chunks per thread per tile and tensor
-
-    __shared__ __attribute__((aligned(16))) T sQ[2][BQ * PQ];
-    __shared__ __attribute__((aligned(16))) T sdY[2][BQ * PQ];
-    __shared__ __attribute__((aligned(16))) T sK[BKV * PQ];
-    __shared__ __attribute__((aligned(16))) T sdSt[BKV * PS];
-    __shared__ float2 sStat[2][BQ];
-
-    const fa_work_item_t it = p.items[blockIdx.x];
-    const int n = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = tid & 63;
-    const int col = lane & 31;
-    const int h = lane >> 5;
-    const int gi = lane & 15;               // lane within its 16-lane group
-    const int gc = 16 * ((lane >> 4) & 1);  // column offset of the group inside a 32-wide tile
-    const int L = it.len_q;
-    const int K = it.len_kv;
-    const int off = K - L;
-    const int j0 = it.kv_block * BKV;
-    const int jw = j0 + 32 * w + col;
-
-    const T* __restrict__ gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
-    const T* __restrict__ gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
-    const float2* __restrict__ gstat = p.rowstat + static_cast<int64_t>(n) * p.tq + it.q_start;
-
-    // K and V rows of this lane (B operands of S = Q K^T and dP = dY V^T)
-    vec kreg[D / 16];
-    vec vreg[D / 16];
-    {
-        const bool ok = jw < K;
-        const int64_t row = it.kv_start + (ok ? jw : 0);
-        const vec* kr = reinterpret_cast<const vec*>(static_cast<const T*>(p.k) + row * p.k_st + n * p.k_sh);
-        const vec* vr = reinterpret_cast<const vec*>(static_cast<const T*>(p.v) + row * p.v_st + n * p.v_sh);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            kreg[s] = kr[2 * s + h];
-            vreg[s] = vr[2 * s + h];
-            if (!ok) {
-                kreg[s] = vec{};
-                vreg[s] = vec{};
-            }
-        }
-        // row-major K block in LDS: B operand of dQ = dS K through transposing reads
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            *reinterpret_cast<vec*>(&sK[(32 * w + col) * PQ + 16 * s + 8 * h]) = kreg[s];
-    }
-
-    f32x16 accK[NT];
-    f32x16 accV[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        accK[i] = zero16();
-        accV[i] = zero16();
-    }
-
-    const int64_t drop_row0 = DROP ? it.drop_base + static_cast<int64_t>(n) * L * K : 0;
-
-    // register staging of one Q / dY tile (and its row statistics)
-    Chunk<T> pq[CPT];
-    Chunk<T> pd[CPT];
-    float2 pst = make_float2(0.f, 0.f);
-    auto fetch = [&](int t) {
-        const int q0 = t * BQ;
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = tid + 256 * u;
-            const int r = c / CPR;
-            const int cv = c - r * CPR;
-            const int qi = q0 + r;
-            if (qi < L) {
-                pq[u] = *reinterpret_cast<const Chunk<T>*>(gq + static_cast<int64_t>(qi) * p.q_st + cv * 8);
-                pd[u] = *reinterpret_cast<const Chunk<T>*>(gdy + static_cast<int64_t>(qi) * p.dy_st + cv * 8);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pq[u].e[e] = static_cast<T>(0.f);
-                    pd[u].e[e] = static_cast<T>(0.f);
-                }
-            }
-        }
-        if (tid < BQ) pst = (q0 + tid < L) ? gstat[q0 + tid] : make_float2(0.f, 0.f);
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = tid + 256 * u;
-            const int r = c / CPR;
-            const int cv = c - r * CPR;
-            *reinterpret_cast<Chunk<T>*>(&sQ[buf][r * PQ + cv * 8]) = pq[u];
-            *reinterpret_cast<Chunk<T>*>(&sdY[buf][r * PQ + cv * 8]) = pd[u];
-        }
-        if (tid < BQ) sStat[buf][tid] = pst;
-    };
-
-    if (it.tile_begin < it.tile_end) {
-        fetch(it.tile_begin);
-        stage(0);
-        if (it.tile_begin + 1 < it.tile_end) fetch(it.tile_begin + 1);
-    }
-    __syncthreads();
-
-    for (int t = it.tile_begin; t < it.tile_end; ++t) {
-        const int buf = (t - it.tile_begin) & 1;
-        const int q0 = t * BQ;
-        const T* cQ = sQ[buf];
-        const T* cdY = sdY[buf];
-
-        // S = Q K^T and dP = dY V^T for this wave's 32 keys
-        f32x16 accS[MT];
-        f32x16 accP[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            accS[mt] = zero16();
-            accP[mt] = zero16();
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const vec aq = *reinterpret_cast<const vec*>(&cQ[(mt * 32 + col) * PQ + 16 * s + 8 * h]);
-                const vec ad = *reinterpret_cast<const vec*>(&cdY[(mt * 32 + col) * PQ + 16 * s + 8 * h]);
-                accS[mt] = E::mfma(aq, kreg[s], accS[mt]);
-                accP[mt] = E::mfma(ad, vreg[s], accP[mt]);
-            }
-        }
-
-        bool full = (q0 + BQ <= L) && (j0 + BKV <= K);
-        if (p.mode == FA_MASK_CAUSAL) {
-            full = full && (j0 + BKV - 1 <= q0 + off);
-        } else if (p.mode == FA_MASK_BAND) {
-            full = full && (j0 >= q0 + BQ - 1 + off - p.pre) && (j0 + BKV - 1 <= q0 + off + p.nxt);
-        }
-
-        // Ps, Pd = Ps Z / kp (kept in accS) and dS = Ps (dP Z / kp - D) (kept in accP)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                const int il = mt * 32 + acc_row(a, h);
-                const float2 st = sStat[buf][il];
-                float pv = __builtin_amdgcn_exp2f(accS[mt][a] * p.exp_scale - st.y);
-                float zk = 1.f;
-                bool adm = true;
-                if (!full) {
-                    const int i = q0 + il;
-                    adm = (i < L) && (jw < K);
-                    if (p.mode == FA_MASK_CAUSAL) {
-                        adm = adm && (jw <= i + off);
-                    } else if (p.mode == FA_MASK_BAND) {
-                        adm = adm && (jw >= i + off - p.pre) && (jw <= i + off + p.nxt);
-                    }
-                    pv = adm ? pv : 0.f;
-                }
-                if constexpr (DROP) {
-                    zk = 0.f;
-                    if (adm) {
-                        const int64_t bit = drop_row0 + static_cast<int64_t>(q0 + il) * K + jw;
-                        zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
-                    }
-                }
-                const float ds = pv * (accP[mt][a] * zk - st.x);
-                accS[mt][a] = pv * zk;
-                accP[mt][a] = ds;
-            }
-        }
-
-        // dV += Pd^T dY and dK += dS^T Q (contraction over the tile's query rows)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                vec ap, as;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    ap[e] = static_cast<T>(accS[mt][8 * kk + e]);
-                    as[e] = static_cast<T>(accP[mt][8 * kk + e]);
-                }
-                // slots 8kk..8kk+3 hold rows 16kk + 4h + 0..3, slots 8kk+4..8kk+7 rows 16kk + 8 + 4h + 0..3
-                const int r0 = mt * 32 + 16 * kk + 4 * h;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const vec bd = tr_operand<vec>(cdY, PQ, r0, r0 + 8, nt * 32 + gc, gi);
-                    const vec bq = tr_operand<vec>(cQ, PQ, r0, r0 + 8, nt * 32 + gc, gi);
-                    accV[nt] = E::mfma(ap, bd, accV[nt]);
-                    accK[nt] = E::mfma(as, bq, accK[nt]);
-                }
-            }
-        }
-
-        __syncthreads();  // every wave is done with the previous tile's dS^T and this buffer pair's old data
-        // dS^T into LDS ([key][query]): slots 4g..4g+3 are 4 consecutive query rows
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                *reinterpret_cast<s16x4*>(&sdSt[(32 * w + col) * PS + mt * 32 + 8 * g + 4 * h]) =
-                    pack4<T>(accP[mt][4 * g], accP[mt][4 * g + 1], accP[mt][4 * g + 2], accP[mt][4 * g + 3]);
-            }
-        }
-        if (t + 1 < it.tile_end) stage(buf ^ 1);
-        __syncthreads();
-        if (t + 2 < it.tile_end) fetch(t + 2);
-
-        // dQ_acc[tile] += dS K  (unscaled; the convert pass applies scale)
-#pragma unroll
-        for (int tt = w; tt < MT * NT; tt += 4) {
-            const int mq = tt / NT;
-            const int nd = tt - mq * NT;
-            f32x16 acc = zero16();
-#pragma unroll
-            for (int s = 0; s < BKV / 16; ++s) {
-                const vec a = tr_operand<vec>(sdSt, PS, 16 * s + 8 * h, 16 * s + 8 * h + 4, mq * 32 + gc, gi);
-                const vec b = tr_operand<vec>(sK, PQ, 16 * s + 8 * h, 16 * s + 8 * h + 4, nd * 32 + gc, gi);
-                acc = E::mfma(a, b, acc);
-            }
-#pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                const int i = q0 + mq * 32 + acc_row(a, h);
-                if (i < L) {
-                    float* dst = p.dq_acc + (static_cast<int64_t>(it.q_start + i) * p.heads + n) * D + nd * 32 + col;
-                    unsafeAtomicAdd(dst, acc[a]);
-                }
-            }
-        }
-    }
-
-    // epilogue: dK = scale * sum dS^T Q, dV = sum Pd^T dY for this wave's 32 keys
-    T* gdk = static_cast<T*>(p.dk) + static_cast<int64_t>(it.kv_start) * p.dk_st + n * p.dk_sh;
-    T* gdv = static_cast<T*>(p.dv) + static_cast<int64_t>(it.kv_start) * p.dv_st + n * p.dv_sh;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            const int j = j0 + 32 * w + acc_row(a, h);
-            if (j < K) {
-                gdk[static_cast<int64_t>(j) * p.dk_st + nt * 32 + col] = static_cast<T>(accK[nt][a] * p.scale);
-                gdv[static_cast<int64_t>(j) * p.dv_st + nt * 32 + col] = static_cast<T>(accV[nt][a]);
             }
         }
     }
@@ -766,11 +475,7 @@ hipError_t launch_convert(int32_t dtype, int head_dim, const float* dq_acc, void
 template <typename T, int D, bool DROP>
 static hipError_t main_t(const DevArgs& d, int64_t n_items, int heads, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(n_items), static_cast<unsigned>(heads));
-    if constexpr (sizeof(T) == 2) {
-        bwd_main_tr16_kernel<T, D, DROP><<<grid, dim3(256), 0, stream>>>(d);
-    } else {
-        bwd_main_kernel<T, D, DROP><<<grid, dim3(256), 0, stream>>>(d);
-    }
+    bwd_main_kernel<T, D, DROP><<<grid, dim3(256), 0, stream>>>(d);
     return hipGetLastError();
 }
 
@@ -810,8 +515,7 @@ hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs
 #define FA_MAIN(T, D)                                                          \
     return dropout ? main_t<T, D, true>(d, n_items, a.heads, stream)           \
                    : main_t<T, D, false>(d, n_items, a.heads, stream)
-    if (dtype == FA_BF16) { if (head_dim == 128) FA_MAIN(__bf16, 128); FA_MAIN(__bf16, 64); }
-    if (dtype == FA_F16) { if (head_dim == 128) FA_MAIN(_Float16, 128); FA_MAIN(_Float16, 64); }
+    if (dtype != FA_F32) return hipErrorInvalidValue;  // 16-bit inputs run launch_bwd16
     if (head_dim == 128) FA_MAIN(float, 128);
     FA_MAIN(float, 64);
 #undef FA_MAIN

@@ -1,13 +1,16 @@
-// Host-side work list for the KV-block-major backward kernel.
+// Host-side work lists of the backward kernels.
 //
-// Each item is one block of FA_BLOCK_KV keys of one sequence together with the
-// contiguous range of query tiles that hold at least one admitted pair with a
-// key in that block.  Ranges follow from the mask definitions of the
+// An item is a block of rows of one sequence that a workgroup keeps resident
+// (keys for dK/dV, queries for dQ) together with the contiguous range of
+// tiles of the other side that hold at least one admitted (query, key) pair
+// with it.  The admitted set follows the mask definitions of the
 // "FlashAttention梯度V2" page (parameter table: attenMask with 1 = excluded,
-// preTokens / nextTokens as the window's left / right bounds), with the
-// causal and band windows aligned to the bottom-right corner.  Blocks and tiles
-// that no admitted pair touches are skipped, except that every key block gets
-// an item so its dK / dV rows are written.
+// preTokens / nextTokens as the window's left / right bounds), with the causal
+// and band windows aligned to the bottom-right corner: with off = Lkv - Lq,
+// query i admits key j iff
+//   causal: j <= i + off;   band: i + off - pre <= j <= i + off + next.
+// Tiles outside the range are skipped; blocks whose range is empty still get
+// an item so their outputs are written as zeros.
 #include <algorithm>
 #include <cstring>
 #include <string>
@@ -46,27 +49,40 @@ int check_seqlens(const fa_seqlens_t* s, const char* name) {
     return FA_OK;
 }
 
-// Rows [lo, hi] of a sequence (Lq = lq, Lkv = lkv) that admit at least one key
-// in [j0, j1].  Returns false when no row does.
-static bool admitted_rows(int64_t lq, int64_t lkv, int32_t mode, int64_t pre, int64_t nxt,
-                          int64_t j0, int64_t j1, int64_t& lo, int64_t& hi) {
+// Query rows [lo, hi] (clipped to [0, lq)) admitting at least one key of [j0, j1].
+static bool rows_for_keys(int64_t lq, int64_t lkv, int32_t mode, int64_t pre, int64_t nxt, int64_t j0,
+                          int64_t j1, int64_t& lo, int64_t& hi) {
     const int64_t off = lkv - lq;
     lo = 0;
     hi = lq - 1;
     if (mode == FA_MASK_CAUSAL) {
-        // j <= i + off for some j >= j0  <=>  i >= j0 - off
-        lo = std::max<int64_t>(lo, j0 - off);
+        lo = std::max<int64_t>(lo, j0 - off);  // some j >= j0 with j <= i + off
     } else if (mode == FA_MASK_BAND) {
         if (pre + nxt < 0) return false;  // every window is empty
-        // i + off - pre <= j1  and  i + off + nxt >= j0
         lo = std::max<int64_t>(lo, j0 - off - nxt);
         hi = std::min<int64_t>(hi, j1 - off + pre);
     }
     return lo <= hi;
 }
 
-int64_t build_worklist(const int64_t* cu_q, const int64_t* cu_kv, int64_t batch, int32_t mode,
-                       int64_t pre, int64_t nxt, int64_t heads, int32_t block_q,
+// Keys [lo, hi] (clipped to [0, lkv)) admitted by at least one query of [i0, i1].
+static bool keys_for_rows(int64_t lq, int64_t lkv, int32_t mode, int64_t pre, int64_t nxt, int64_t i0,
+                          int64_t i1, int64_t& lo, int64_t& hi) {
+    const int64_t off = lkv - lq;
+    lo = 0;
+    hi = lkv - 1;
+    if (mode == FA_MASK_CAUSAL) {
+        hi = std::min<int64_t>(hi, i1 + off);
+    } else if (mode == FA_MASK_BAND) {
+        if (pre + nxt < 0) return false;
+        lo = std::max<int64_t>(lo, i0 + off - pre);
+        hi = std::min<int64_t>(hi, i1 + off + nxt);
+    }
+    return lo <= hi;
+}
+
+int64_t build_worklist(const int64_t* cu_q, const int64_t* cu_kv, int64_t batch, int32_t mode, int64_t pre,
+                       int64_t nxt, int64_t heads, int32_t kind, int32_t block_rows, int32_t tile_rows,
                        std::vector<fa_work_item_t>& out) {
     out.clear();
     pre = clamp_window(pre);
@@ -75,26 +91,28 @@ int64_t build_worklist(const int64_t* cu_q, const int64_t* cu_kv, int64_t batch,
     for (int64_t b = 0; b < batch; ++b) {
         const int64_t lq = cu_q[b + 1] - cu_q[b];
         const int64_t lkv = cu_kv[b + 1] - cu_kv[b];
-        const int64_t nblocks = (lkv + FA_BLOCK_KV - 1) / FA_BLOCK_KV;
-        for (int64_t jb = 0; jb < nblocks; ++jb) {
-            const int64_t j0 = jb * FA_BLOCK_KV;
-            const int64_t j1 = std::min<int64_t>(lkv, j0 + FA_BLOCK_KV) - 1;
+        const int64_t resident = kind == FA_ITEMS_KEY_BLOCKS ? lkv : lq;
+        const int64_t walked = kind == FA_ITEMS_KEY_BLOCKS ? lq : lkv;
+        const int64_t nblocks = (resident + block_rows - 1) / block_rows;
+        for (int64_t blk = 0; blk < nblocks; ++blk) {
+            const int64_t r0 = blk * block_rows;
+            const int64_t r1 = std::min<int64_t>(resident, r0 + block_rows) - 1;
             fa_work_item_t it;
             std::memset(&it, 0, sizeof(it));
             it.q_start = static_cast<int32_t>(cu_q[b]);
             it.kv_start = static_cast<int32_t>(cu_kv[b]);
             it.len_q = static_cast<int32_t>(lq);
             it.len_kv = static_cast<int32_t>(lkv);
-            it.kv_block = static_cast<int32_t>(jb);
+            it.block = static_cast<int32_t>(blk);
             it.seq = static_cast<int32_t>(b);
             it.drop_base = drop_base;
-            int64_t lo, hi;
-            if (lq > 0 && admitted_rows(lq, lkv, mode, pre, nxt, j0, j1, lo, hi)) {
-                it.tile_begin = static_cast<int32_t>(lo / block_q);
-                it.tile_end = static_cast<int32_t>(hi / block_q + 1);
-            } else {
-                it.tile_begin = 0;
-                it.tile_end = 0;
+            int64_t lo = 0, hi = -1;
+            const bool any = walked > 0 && (kind == FA_ITEMS_KEY_BLOCKS
+                                                ? rows_for_keys(lq, lkv, mode, pre, nxt, r0, r1, lo, hi)
+                                                : keys_for_rows(lq, lkv, mode, pre, nxt, r0, r1, lo, hi));
+            if (any) {
+                it.tile_begin = static_cast<int32_t>(lo / tile_rows);
+                it.tile_end = static_cast<int32_t>(hi / tile_rows + 1);
             }
             out.push_back(it);
         }
@@ -111,8 +129,8 @@ int64_t build_worklist(const int64_t* cu_q, const int64_t* cu_kv, int64_t batch,
 
 extern "C" int64_t fa_varlen_worklist(const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
                                       int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens,
-                                      int64_t heads, int32_t block_q, fa_work_item_t* items,
-                                      int64_t capacity) {
+                                      int64_t heads, int32_t kind, int32_t block_rows, int32_t tile_rows,
+                                      fa_work_item_t* items, int64_t capacity) {
     fa::clear_error();
     int st = fa::check_seqlens(cu_seqlens_q, "cu_seqlens_q");
     if (st != FA_OK) return -st;
@@ -126,13 +144,17 @@ extern "C" int64_t fa_varlen_worklist(const fa_seqlens_t* cu_seqlens_q, const fa
         fa::set_error("atten_mode must be 0 (none), 1 (causal) or 2 (band)");
         return -FA_ERR_INVALID;
     }
-    if (block_q <= 0 || heads < 1) {
-        fa::set_error("block_q and heads must be positive");
+    if (kind != FA_ITEMS_KEY_BLOCKS && kind != FA_ITEMS_QUERY_BLOCKS) {
+        fa::set_error("kind must be FA_ITEMS_KEY_BLOCKS or FA_ITEMS_QUERY_BLOCKS");
+        return -FA_ERR_INVALID;
+    }
+    if (block_rows <= 0 || tile_rows <= 0 || heads < 1) {
+        fa::set_error("block_rows, tile_rows and heads must be positive");
         return -FA_ERR_INVALID;
     }
     std::vector<fa_work_item_t> list;
-    const int64_t n = fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, cu_seqlens_q->batch,
-                                         atten_mode, pre_tokens, next_tokens, heads, block_q, list);
+    const int64_t n = fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, cu_seqlens_q->batch, atten_mode,
+                                         pre_tokens, next_tokens, heads, kind, block_rows, tile_rows, list);
     if (items != nullptr) {
         const int64_t m = std::min(n, capacity);
         if (m > 0) std::memcpy(items, list.data(), static_cast<size_t>(m) * sizeof(fa_work_item_t));
