@@ -10,9 +10,10 @@ Metric: useful TFLOP/s = 10 * N * D * (admitted query/key pairs) / step time
 (five contractions of 2*D flops per admitted pair and head).
 
 Also reported:
-  roofline      the main kernel's useful flops per launch over its average
-                duration (HIP events on the launch stream, recorded by the
-                library during the timed steps) against the bf16 MFMA peak;
+  roofline      the dominant kernel's algorithmic flops per launch over its
+                average duration (HIP events on the launch stream, recorded by
+                the library during the timed steps) against the bf16 MFMA peak;
+  kernels       the same figure for every kernel (GB/s for the HBM-bound ones);
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
                 same workload (a few (sequence, head) units), as a baseline.
 """
@@ -31,8 +32,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "variable_length_flashattention_fa_amd", "csrc", "fa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_flashattention_fa_amd", "csrc", f)
+                  for f in ("fa_kernels.hip", "fa_bwd16.hip")]
 
 
 def log(msg):
@@ -40,18 +42,21 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str):
-    """HBM bytes per main-kernel launch from committed counter runs, if taken on this kernel source."""
+def traffic_for(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from committed counter runs, if taken on this kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(workload)
+    entry = rec.get(workload, {}).get(kernel)
     if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
@@ -170,26 +175,33 @@ def main(argv=None):
     pairs = pair_count(inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt)
     useful = 10.0 * wl.heads * wl.head_dim * pairs
     value = useful / (ms_per_step * 1e-3) / 1e12
-    main_ms, main_n = prof["bwd_main"]
-    main_avg = main_ms / max(main_n, 1)
-    achieved = useful / (main_avg * 1e-3) / 1e12
     tq, heads, d = q.shape
     esz = q.element_size()
-    pre_bytes = tq * heads * (2 * d * esz + 2 * 4 + 8 + 4 * d)   # dY, Y, m, l in; {delta, beta}, zeroed dQ acc out
-    cvt_bytes = tq * heads * (4 * d + d * esz)                   # fp32 dQ acc in, dQ out
+    pair_flops = 2.0 * wl.heads * wl.head_dim * pairs  # one contraction over all admitted pairs
+    if q.dtype == torch.float32:
+        # one kernel runs all five contractions; dQ goes through an fp32 accumulator
+        mfma = {"bwd_main": ("bwd_main_kernel", 5 * pair_flops)}
+        hbm = {"preprocess": tq * heads * (2 * d * esz + 2 * 4 + 8 + 4 * d),  # + zeroed dQ accumulator
+               "convert_dq": tq * heads * (4 * d + d * esz)}
+    else:
+        # dK/dV kernel: S, dP, dV, dK; dQ kernel: S, dP (recomputed) and dQ
+        mfma = {"bwd_main": ("bwd_dkdv16_kernel", 4 * pair_flops), "bwd_dq": ("bwd_dq16_kernel", 3 * pair_flops)}
+        hbm = {"preprocess": tq * heads * (2 * d * esz + 2 * 4 + 8)}  # dY, Y, max, sum in; {delta, beta} out
     kernels = {}
-    for name, nbytes in (("preprocess", pre_bytes), ("bwd_main", None), ("convert_dq", cvt_bytes)):
+    for name, (kname, flops) in mfma.items():
         ms, n = prof[name]
         avg = ms / max(n, 1)
-        entry = {"avg_ms": avg, "launches": n}
-        if nbytes is not None:
-            entry["algorithmic_bytes"] = nbytes
-            entry["GB/s"] = nbytes / (avg * 1e-3) / 1e9 if avg > 0 else None
-            entry["hbm_frac"] = entry["GB/s"] / PEAK_HBM_GBS if entry["GB/s"] else None
-        else:
-            entry["useful_tflop"] = useful / 1e12
-            entry["TFLOP/s"] = achieved
-        kernels[name] = entry
+        kernels[kname] = {"avg_ms": avg, "launches": n, "algorithmic_tflop": flops / 1e12,
+                          "TFLOP/s": flops / (avg * 1e-3) / 1e12 if avg > 0 else None}
+    for name, nbytes in hbm.items():
+        ms, n = prof[name]
+        avg = ms / max(n, 1)
+        gbs = nbytes / (avg * 1e-3) / 1e9 if avg > 0 else None
+        kernels[name] = {"avg_ms": avg, "launches": n, "algorithmic_bytes": nbytes, "GB/s": gbs,
+                         "hbm_frac": gbs / PEAK_HBM_GBS if gbs else None}
+    dominant = max((k for k in kernels if "TFLOP/s" in kernels[k]), key=lambda k: kernels[k]["avg_ms"])
+    achieved = kernels[dominant]["TFLOP/s"]
+    main_avg = kernels[dominant]["avg_ms"]
 
     dtype_name = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[q.dtype]
     out = {
@@ -210,8 +222,8 @@ def main(argv=None):
                    "next_tokens": wl.nxt, "keep_prob": wl.keep_prob, "admitted_pairs_per_head": pairs},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for(wl.name),
-                     "kernel": "bwd_main_kernel", "avg_ms": main_avg},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for(wl.name, dominant),
+                     "kernel": dominant, "avg_ms": main_avg},
         "kernels": kernels,
     }
 

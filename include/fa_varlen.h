@@ -176,15 +176,15 @@ int64_t fa_varlen_worklist(const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t*
 /*
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
  * fa_varlen_bwd call records a pair of HIP events around each of its kernels
- * on the call's stream: index 0 the row preprocess, 1 the main backward work
- * (for bf16 / fp16 the dK/dV and dQ kernels together), 2 the dQ convert (fp32
- * inputs only).
+ * on the call's stream: index 0 the row preprocess, 1 the main backward
+ * kernel (dK/dV for bf16 / fp16; the whole backward for fp32), 2 the dQ
+ * convert (fp32 only), 3 the dQ kernel (bf16 / fp16 only).
  */
 void fa_profile_enable(int on);
 
 /* Waits for the recorded events, writes the summed milliseconds and launch
  * counts per kernel index into ms[] / launches[] (capacity entries each, may be
- * NULL) and clears the record.  Returns the number of kernel indices (3), or
+ * NULL) and clears the record.  Returns the number of kernel indices (4), or
  * -FA_ERR_RUNTIME if an event could not be read. */
 int fa_profile_read(double* ms, int64_t* launches, int capacity);
 

@@ -51,7 +51,7 @@ _lib = None
 
 EXPORTS = ("fa_varlen_bwd", "fa_last_error", "fa_release", "fa_varlen_worklist", "fa_profile_enable",
            "fa_profile_read")
-KERNEL_NAMES = ("preprocess", "bwd_main", "convert_dq")
+KERNEL_NAMES = ("preprocess", "bwd_main", "convert_dq", "bwd_dq")
 
 
 def load(path: Optional[str] = None):
@@ -193,9 +193,10 @@ def profile_enable(on: bool = True) -> None:
 
 def profile_read() -> dict:
     """{kernel name: (summed ms, launches)} since the last read; clears the record."""
-    ms = (ctypes.c_double * 3)()
-    cnt = (ctypes.c_int64 * 3)()
-    n = load().fa_profile_read(ms, cnt, 3)
+    k = len(KERNEL_NAMES)
+    ms = (ctypes.c_double * k)()
+    cnt = (ctypes.c_int64 * k)()
+    n = load().fa_profile_read(ms, cnt, k)
     if n < 0:
         raise FaError(-n, last_error())
-    return {KERNEL_NAMES[i]: (ms[i], cnt[i]) for i in range(3)}
+    return {KERNEL_NAMES[i]: (ms[i], cnt[i]) for i in range(min(n, k))}

@@ -19,6 +19,9 @@ LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libfa_varlen.so"
 
 HIP_SOURCES = ["fa_kernels.hip", "fa_bwd16.hip", "fa_api.cpp"]
+# The 16-bit kernels feed MFMA results straight into VALU work (exp, dS): keep MFMA
+# destinations in VGPRs instead of accumulation registers that would need copying back.
+PER_SOURCE_FLAGS = {"fa_bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_SOURCES = ["fa_worklist.cpp"]
 
 
@@ -52,7 +55,8 @@ def build(arch: str = "gfx950", verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(objdir, src + ".o")
         lang = [] if src.endswith(".hip") else ["-x", "hip"]
-        jobs.append([hipcc] + common + hip_flags + lang + ["-c", os.path.join(HERE, src), "-o", obj])
+        extra = PER_SOURCE_FLAGS.get(src, [])
+        jobs.append([hipcc] + common + hip_flags + extra + lang + ["-c", os.path.join(HERE, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(objdir, src + ".o")

@@ -82,7 +82,7 @@ std::mutex g_mutex;
 std::unordered_map<int, Workspace> g_ws;
 
 // ---- optional per-kernel event timing ----
-constexpr int kKernels = 3;  // 0 preprocess, 1 main, 2 convert
+constexpr int kKernels = 4;  // 0 preprocess, 1 main / dK-dV, 2 convert, 3 dQ
 struct EventPair {
     int kernel;
     hipEvent_t start;
@@ -163,8 +163,8 @@ extern "C" void fa_profile_enable(int on) {
 
 extern "C" int fa_profile_read(double* ms, int64_t* launches, int capacity) {
     std::lock_guard<std::mutex> lock(g_mutex);
-    double sum[kKernels] = {0, 0, 0};
-    int64_t cnt[kKernels] = {0, 0, 0};
+    double sum[kKernels] = {0, 0, 0, 0};
+    int64_t cnt[kKernels] = {0, 0, 0, 0};
     int status = kKernels;
     for (auto& ev : g_events) {
         float t = 0.f;
@@ -431,10 +431,10 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         a.exp_scale = exp_scale;
         a.inv_keep = inv_keep;
         a.scale = static_cast<float>(scale);
-        e = timed(1, s, [&] {
-            return fa::launch_bwd16(dtype, d, keep_prob < 1.0, a, ws.n_items, ws.n_q_items, s);
-        });
-        if (e != hipSuccess) return runtime_error("backward kernel launch", e);
+        e = timed(1, s, [&] { return fa::launch_dkdv16(dtype, d, keep_prob < 1.0, a, ws.n_items, s); });
+        if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
+        e = timed(3, s, [&] { return fa::launch_dq16(dtype, d, keep_prob < 1.0, a, ws.n_q_items, s); });
+        if (e != hipSuccess) return runtime_error("dQ kernel launch", e);
         return FA_OK;
     }
 

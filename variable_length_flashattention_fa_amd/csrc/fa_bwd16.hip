@@ -340,15 +340,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             accS[mt] = zero16();
             accP[mt] = zero16();
         }
+        // operands of step s + 1 are read while step s runs (two steps live at most)
+        vec aq[2][MT];
+        vec ad[2][MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            aq[0][mt] = lds_row<vec>(cQ + 32 * mt * D, lo_.row[0]);
+            ad[0][mt] = lds_row<vec>(cdY + 32 * mt * D, lo_.row[0]);
+        }
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
+            const int c = s & 1;
+            if (s + 1 < D / 16) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    aq[c ^ 1][mt] = lds_row<vec>(cQ + 32 * mt * D, lo_.row[s + 1]);
+                    ad[c ^ 1][mt] = lds_row<vec>(cdY + 32 * mt * D, lo_.row[s + 1]);
+                }
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const vec aq = lds_row<vec>(cQ + 32 * mt * D, lo_.row[s]);
-                const vec ad = lds_row<vec>(cdY + 32 * mt * D, lo_.row[s]);
-                accS[mt] = Op16<T>::mfma(aq, kreg[s], accS[mt]);
-                accP[mt] = Op16<T>::mfma(ad, vreg[s], accP[mt]);
+                accS[mt] = Op16<T>::mfma(aq[c][mt], kreg[s], accS[mt]);
+                accP[mt] = Op16<T>::mfma(ad[c][mt], vreg[s], accP[mt]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // Ps / Pd into accS, dS into accP; element (query row 32mt + acc_row(a, h), key jw)
@@ -418,25 +433,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 
         // dV += Pd^T dY, dK += dS^T Q: slots 8kk..8kk+3 are rows 32mt + 16kk + 4h + 0..3,
         // slots 8kk+4..8kk+7 rows 32mt + 16kk + 8 + 4h + 0..3
+        // the transposing reads of step i + 1 are issued while step i runs
+        constexpr int NSTEP = MT * 2 * NT;  // (mt, kk, nt)
+        vec bd[2];
+        vec bq[2];
+        auto tr_load = [&](int i, int slot) {
+            const int nt = i % NT;
+            const int rowoff = 16 * (i / NT) * D;  // 32mt + 16kk = 16 * (i / NT)
+            bd[slot] = lds_tr<vec>(cdY + rowoff, lo_.tr[nt][0], lo_.tr[nt][1]);
+            bq[slot] = lds_tr<vec>(cQ + rowoff, lo_.tr[nt][0], lo_.tr[nt][1]);
+        };
+        tr_load(0, 0);
+        vec ap, as;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                vec ap, as;
+        for (int i = 0; i < NSTEP; ++i) {
+            const int nt = i % NT;
+            const int q16 = i / NT;  // 2 * mt + kk
+            if (nt == 0) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    ap[e] = static_cast<T>(accS[mt][8 * kk + e]);
-                    as[e] = static_cast<T>(accP[mt][8 * kk + e]);
-                }
-                const int rowoff = (32 * mt + 16 * kk) * D;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const vec bd = lds_tr<vec>(cdY + rowoff, lo_.tr[nt][0], lo_.tr[nt][1]);
-                    const vec bq = lds_tr<vec>(cQ + rowoff, lo_.tr[nt][0], lo_.tr[nt][1]);
-                    accV[nt] = Op16<T>::mfma(ap, bd, accV[nt]);
-                    accK[nt] = Op16<T>::mfma(as, bq, accK[nt]);
+                    ap[e] = static_cast<T>(accS[q16 >> 1][8 * (q16 & 1) + e]);
+                    as[e] = static_cast<T>(accP[q16 >> 1][8 * (q16 & 1) + e]);
                 }
             }
+            if (i + 1 < NSTEP) tr_load(i + 1, (i + 1) & 1);
+            accV[nt] = Op16<T>::mfma(ap, bd[i & 1], accV[nt]);
+            accK[nt] = Op16<T>::mfma(as, bq[i & 1], accK[nt]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -644,33 +667,40 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 // ------------------------------------------------------------------------------------------------
 
 template <typename T, int D, bool DROP>
-static hipError_t launch16_t(const Bwd16Args& a, int64_t n_kv, int64_t n_q, int heads, hipStream_t stream) {
-    if (n_kv > 0) {
-        bwd_dkdv16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n_kv), static_cast<unsigned>(heads)), dim3(256), 0,
-                                        stream>>>(a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (n_q > 0) {
-        bwd_dq16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n_q), static_cast<unsigned>(heads)), dim3(512), 0,
-                                      stream>>>(a);
-        return hipGetLastError();
-    }
-    return hipSuccess;
+static hipError_t launch_dkdv_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
+    bwd_dkdv16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(256), 0,
+                                    stream>>>(a);
+    return hipGetLastError();
 }
 
-hipError_t launch_bwd16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_kv_items,
-                        int64_t n_q_items, hipStream_t stream) {
-#define FA_B16(T, D)                                                                   \
-    return dropout ? launch16_t<T, D, true>(a, n_kv_items, n_q_items, a.heads, stream) \
-                   : launch16_t<T, D, false>(a, n_kv_items, n_q_items, a.heads, stream)
-    if (dtype == FA_BF16) {
-        if (head_dim == 128) FA_B16(__bf16, 128);
-        FA_B16(__bf16, 64);
-    }
-    if (head_dim == 128) FA_B16(_Float16, 128);
-    FA_B16(_Float16, 64);
-#undef FA_B16
+template <typename T, int D, bool DROP>
+static hipError_t launch_dq_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
+    bwd_dq16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0,
+                                  stream>>>(a);
+    return hipGetLastError();
 }
+
+#define FA_DISPATCH16(FN)                                                                        \
+    if (n_items <= 0) return hipSuccess;                                                         \
+    if (dtype == FA_BF16) {                                                                      \
+        if (head_dim == 128)                                                                     \
+            return dropout ? FN<__bf16, 128, true>(a, n_items, stream) : FN<__bf16, 128, false>(a, n_items, stream); \
+        return dropout ? FN<__bf16, 64, true>(a, n_items, stream) : FN<__bf16, 64, false>(a, n_items, stream);       \
+    }                                                                                            \
+    if (head_dim == 128)                                                                         \
+        return dropout ? FN<_Float16, 128, true>(a, n_items, stream) : FN<_Float16, 128, false>(a, n_items, stream); \
+    return dropout ? FN<_Float16, 64, true>(a, n_items, stream) : FN<_Float16, 64, false>(a, n_items, stream)
+
+hipError_t launch_dkdv16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
+                         hipStream_t stream) {
+    FA_DISPATCH16(launch_dkdv_t);
+}
+
+hipError_t launch_dq16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
+                       hipStream_t stream) {
+    FA_DISPATCH16(launch_dq_t);
+}
+
+#undef FA_DISPATCH16
 
 }  // namespace fa

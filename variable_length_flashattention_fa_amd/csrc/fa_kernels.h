@@ -74,8 +74,12 @@ struct Bwd16Args {
     float exp_scale, inv_keep, scale;
 };
 
-// dK/dV kernel over n_kv_items x heads, then dQ kernel over n_q_items x heads.
-hipError_t launch_bwd16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_kv_items,
-                        int64_t n_q_items, hipStream_t stream);
+// dK/dV kernel over n_items key-block items x heads.
+hipError_t launch_dkdv16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
+                         hipStream_t stream);
+
+// dQ kernel over n_items query-block items x heads.
+hipError_t launch_dq16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
+                       hipStream_t stream);
 
 }  // namespace fa
