@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_flashattention_fa_amd", "csrc", f)
-                  for f in ("fa_kernels.hip", "fa_bwd16.hip")]
+                  for f in ("fa_kernels.hip", "fa_bwd16.hip", "fa_kernels.h", "build.py")]
 
 
 def log(msg):
@@ -111,13 +111,14 @@ def main(argv=None):
     ap.add_argument("--cpu-units", type=int, default=16, help="(sequence, head) units for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
-                    help="copy this many MiB device-to-device once before the timed steps (a plain copy of "
-                         "known size, for scaling HBM byte counters)")
+                    help="copy this many MiB device-to-device once before the timed steps, with the runtime's "
+                         "blit kernel and with an elementwise kernel (plain copies of known size, for "
+                         "scaling HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each (sequence, head) unit is "
-              "independent; see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "independent, so heads or sequences would shard across GPUs with no communication). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -155,7 +156,9 @@ def main(argv=None):
         src = torch.ones(nel, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        dst.copy_(src)          # runtime blit kernel: reads and writes nel*4 bytes
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # elementwise kernel: the same bytes through an ordinary kernel
         torch.cuda.synchronize()
         del src, dst
         log(f"calibration copy of {args.calibration_copy_mib} MiB done")
