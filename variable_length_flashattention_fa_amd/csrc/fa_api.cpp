@@ -423,6 +423,14 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         a.items_kv = ws.items;
         a.items_q = ws.items + ws.n_items;
         a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
+        {
+            // the bit stream holds heads * Lq_b * Lkv_b bits per sequence
+            int64_t bits = 0;
+            for (int64_t b = 0; b < batch; ++b)
+                bits += heads * (cu_seqlens_q->cu[b + 1] - cu_seqlens_q->cu[b]) *
+                        (cu_seqlens_kv->cu[b + 1] - cu_seqlens_kv->cu[b]);
+            a.drop_bytes = keep_prob < 1.0 ? (bits + 7) / 8 : 0;
+        }
         a.tq = static_cast<int32_t>(tq);
         a.heads = static_cast<int32_t>(heads);
         a.mode = atten_mode;

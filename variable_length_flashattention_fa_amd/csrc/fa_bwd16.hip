@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "fa_kernels.h"
 
@@ -121,11 +122,56 @@ __device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
 
 template <typename T>
 __device__ __forceinline__ void dma16_async(T* lds, const i32x4& desc, int voff) {
-    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(m0), "v"(voff), "s"(desc)
-                 : "memory", "m0");
+    // uniform; the read keeps it in a scalar register
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds)));
+    uint32_t saved;
+    // M0 is restored afterwards; the LDS DMA needs one wait state after M0 is written
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0), "v"(voff), "s"(desc)
+        : "memory");
+}
+
+// Copy of two 16-byte-per-lane runs of TW KiB each (Q and dY of a tile): LDS destination
+// m0x + 1 KiB * u + 16 * lane for instruction u, global source desc + voff[u] + 1 KiB * u (the
+// instruction offset moves both addresses).  M0 is restored afterwards.
+template <int TW>
+__device__ __forceinline__ void dma_pair(uint32_t m0a, const i32x4& da, const int* va, uint32_t m0b,
+                                         const i32x4& db, const int* vb) {
+    uint32_t saved;
+    if constexpr (TW == 4) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
+            "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
+            "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
+            "s_mov_b32 m0, %7\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %8, %12, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %9, %12, 0 offen offset:1024 lds\n\t"
+            "buffer_load_dwordx4 %10, %12, 0 offen offset:2048 lds\n\t"
+            "buffer_load_dwordx4 %11, %12, 0 offen offset:3072 lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0a), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "s"(da), "s"(m0b), "v"(vb[0]), "v"(vb[1]),
+              "v"(vb[2]), "v"(vb[3]), "s"(db)
+            : "memory");
+    } else {
+        static_assert(TW == 2, "runs of 2 or 4 KiB");
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
+            "s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %6, %8, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %7, %8, 0 offen offset:1024 lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0a), "v"(va[0]), "v"(va[1]), "s"(da), "s"(m0b), "v"(vb[0]), "v"(vb[1]), "s"(db)
+            : "memory");
+    }
 }
 
 // ---- transposing LDS reads --------------------------------------------------------------------
@@ -159,8 +205,10 @@ __device__ __forceinline__ vec row_operand(const T* tile, int r, int c) {
 
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    T t[2] = {static_cast<T>(a), static_cast<T>(b)};
-    return __builtin_bit_cast(uint32_t, t);
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef T t2 __attribute__((ext_vector_type(2)));
+    const f2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, t2));  // one packed conversion
 }
 
 template <bool V>
@@ -237,24 +285,85 @@ __device__ __forceinline__ uint32_t tile_bytes(int valid, int rows, int64_t st) 
 // ------------------------------------------------------------------------------------------------
 // dK / dV
 // ------------------------------------------------------------------------------------------------
-// Workgroup: 4 waves (one per SIMD), FA16_DKDV_BLOCK = 128 keys; wave w owns keys 32w .. 32w+31
-// and walks 64-row query tiles as two 32-row halves (independent MFMA chains).
+// Workgroup: 4 waves (one per SIMD), FA16_DKDV_BLOCK = 128 keys; wave w owns keys 32w .. 32w+31.
+// The query rows are walked in steps of 32 rows (two per 64-row tile) through a three-stage
+// software pipeline.  Step i of a wave interleaves, slot by slot,
+//   X: S and dP of step i + 1           MFMA; A = Q / dY rows (LDS), B = K / V rows (registers)
+//   the softmax gradient of step i      VALU; P and dS from the S and dP made during step i - 1
+//   Y: dV and dK updates of step i - 1  MFMA; A = packed P / dS, B = transposing LDS reads
+// so that the exponentials and the dS arithmetic of one step run under the matrix products of
+// its neighbours (one wave per SIMD: nothing else would fill the gaps).  dK and dV accumulate
+// in the accumulation registers through MFMAs written in assembly; S and dP use ordinary
+// VGPRs, where the VALU reads them.  Query tiles rotate through three LDS buffers: while tiles
+// t and t + 1 are read, tile t + 2 is copied in; one barrier per tile, between its two steps,
+// hands the buffer of tile t - 1 back.
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(IC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Empty instruction that claims to read and write x.  Volatile asm statements and LDS accesses
+// keep their program order through instruction selection, so fencing the inputs and outputs
+// of a piece of arithmetic pins it between its neighbours in the slot schedule below.
+template <typename X>
+__device__ __forceinline__ void pin(X& x) {
+    asm volatile("" : "+v"(x));
+}
+
+// acc += A B with acc in accumulation registers (volatile: keeps its slot).
+template <typename T>
+struct MfmaAccV;
+template <>
+struct MfmaAccV<__bf16> {
+    static __device__ __forceinline__ void run(f32x16& acc, bf16x8 a, bf16x8 b) {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    }
+};
+template <>
+struct MfmaAccV<_Float16> {
+    static __device__ __forceinline__ void run(f32x16& acc, f16x8 a, f16x8 b) {
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    }
+};
+
+// Kinds of pipeline step.  For the tile in buffer b (tile t):
+//   A: X = rows 32.. of tile t (buffer b), softmax = rows 0.. of tile t, Y = rows 32.. of tile
+//      t - 1 (buffer b + 2); ends with the tile barrier, after which tile t + 2 is fetched into
+//      buffer b + 2
+//   B: X = rows 0.. of tile t + 1 (buffer b + 1), softmax = rows 32.. of tile t, Y = rows 0..
+//      of tile t (buffer b)
+//   FIRST: X = rows 0.. of the first tile (buffer 0) only;  LAST: Y = rows 32.. of the last
+//   tile (buffer b) only.  (buffer indices mod 3)
+enum StepKind { kStepA = 0, kStepB = 1, kStepFirst = 2, kStepLast = 3 };
 
 template <typename T, int D, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     using vec = typename Op16<T>::vec;
     constexpr int NW = 4;
     constexpr int BQ = FA16_DKDV_TILE_Q;  // query tile rows (64)
-    constexpr int MT = BQ / 32;           // 32-row halves
     constexpr int BKV = FA16_DKDV_BLOCK;  // keys per workgroup
-    constexpr int NT = D / 32;
-    constexpr int TI = BQ * D / 8 / 64;   // DMA instructions per query tile and tensor
+    constexpr int NT = D / 32;            // 32-column tiles of dK / dV
+    constexpr int NX = D / 8;             // MFMAs per step for S and dP (as many for dV and dK)
+    constexpr int NOPS = 2 * NX;          // slots per step: X and Y MFMAs alternate
+    constexpr int EPS = NOPS / 16;        // slots per softmax element (16 elements per step)
+    constexpr int LA = 4;                 // LDS reads run LA slots ahead of their MFMA
+    constexpr int NB = 3;                 // query tile buffers
+    constexpr int TILE = BQ * D;
+    constexpr int TI = TILE / 8 / 64;     // DMA instructions per query tile and tensor
     constexpr int TW = TI / NW;           // ... per wave
-    static_assert(BQ == 64 && BKV == 32 * NW && TI % NW == 0, "tile shape");
+    static_assert(BQ == 64 && BKV == 32 * NW && TI % NW == 0 && NOPS >= 16 && LA % 2 == 0 && LA < NOPS,
+                  "tile shape");
 
-    __shared__ __attribute__((aligned(16))) T sQ[2][BQ * D];
-    __shared__ __attribute__((aligned(16))) T sdY[2][BQ * D];
-    __shared__ __attribute__((aligned(16))) float2 sSt[2][BQ];
+    // buffer b: Q tile at sBuf[b][0], dY tile at sBuf[b][1]
+    __shared__ __attribute__((aligned(16))) T sBuf[NB][2][TILE];
+    __shared__ __attribute__((aligned(16))) float2 sSt[NB][BQ];
 
     const fa_work_item_t it = p.items_kv[blockIdx.x];
     const int n = blockIdx.y;
@@ -267,35 +376,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     const int off = K - L;
     const int j0 = it.block * BKV;
     const int jw = j0 + 32 * w + col;  // this lane's key
-
-    LdsOffsets<D> lo_;
-    lo_.init(lane);
-
-    const T* gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
-    const T* gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
-    const float2* gstat = p.rowstat + static_cast<int64_t>(n) * p.tq + it.q_start;
-    int qoff[TW];
-    int dyoff[TW];
-#pragma unroll
-    for (int u = 0; u < TW; ++u) {
-        qoff[u] = dma_offset<D>(w + NW * u, lane, p.q_st);
-        dyoff[u] = dma_offset<D>(w + NW * u, lane, p.dy_st);
-    }
-
-    // this lane's K and V rows: B operands of S = Q K^T and dP = dY V^T
-    vec kreg[D / 16];
-    vec vreg[D / 16];
-    {
-        const bool ok = jw < K;
-        const int64_t row = it.kv_start + (ok ? jw : 0);
-        const vec* kr = reinterpret_cast<const vec*>(static_cast<const T*>(p.k) + row * p.k_st + n * p.k_sh);
-        const vec* vr = reinterpret_cast<const vec*>(static_cast<const T*>(p.v) + row * p.v_st + n * p.v_sh);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            kreg[s] = ok ? kr[2 * s + h] : vec{};
-            vreg[s] = ok ? vr[2 * s + h] : vec{};
-        }
-    }
+    const int tb = it.tile_begin;
+    const int te = it.tile_end;
 
     f32x16 accK[NT];
     f32x16 accV[NT];
@@ -305,163 +387,343 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         accV[i] = zero16();
     }
 
-    // HBM -> LDS copy of query tile t (Q, dY, row statistics) into buffer b
-    auto issue = [&](int t, int b) {
-        const int q0 = t * BQ;
-        const i32x4 rq = buffer_desc(gq + static_cast<int64_t>(q0) * p.q_st, tile_bytes(L - q0, BQ, p.q_st));
-        const i32x4 rd = buffer_desc(gdy + static_cast<int64_t>(q0) * p.dy_st, tile_bytes(L - q0, BQ, p.dy_st));
+    if (tb < te) {
+        LdsOffsets<D> lo_;
+        lo_.init(lane);
+
+        const T* gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
+        const T* gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
+        const float2* gstat = p.rowstat + static_cast<int64_t>(n) * p.tq + it.q_start;
+        int qoff[TW];
+        int dyoff[TW];
+        // wave w copies 1 KiB chunks w*TW .. w*TW + TW - 1 of each tile (one run)
 #pragma unroll
         for (int u = 0; u < TW; ++u) {
-            dma16_async(sQ[b] + (w + NW * u) * 512, rq, qoff[u]);
-            dma16_async(sdY[b] + (w + NW * u) * 512, rd, dyoff[u]);
-        }
-        if (w == NW - 1 && lane < BQ / 2) {
-            const i32x4 rs = buffer_desc(gstat + q0, q0 < L ? static_cast<uint32_t>(min(L - q0, BQ) * 8) : 0u);
-            dma16_async(sSt[b], rs, lane * 16);
-        }
-    };
-
-    if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
-    for (int t = it.tile_begin; t < it.tile_end; ++t) {
-        const int b = (t - it.tile_begin) & 1;
-        const T* cQ = sQ[b];
-        const T* cdY = sdY[b];
-        const float2* cSt = sSt[b];
-        wait_dma();
-        __syncthreads();  // tile t is in buffer b; every wave is done with buffer b ^ 1
-        if (t + 1 < it.tile_end) issue(t + 1, b ^ 1);
-        const int q0 = t * BQ;
-
-        // S = Q K^T and dP = dY V^T (the tile's query rows x this wave's 32 keys)
-        f32x16 accS[MT];
-        f32x16 accP[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            accS[mt] = zero16();
-            accP[mt] = zero16();
-        }
-        // operands of step s + 1 are read while step s runs (two steps live at most)
-        vec aq[2][MT];
-        vec ad[2][MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            aq[0][mt] = lds_row<vec>(cQ + 32 * mt * D, lo_.row[0]);
-            ad[0][mt] = lds_row<vec>(cdY + 32 * mt * D, lo_.row[0]);
-        }
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const int c = s & 1;
-            if (s + 1 < D / 16) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    aq[c ^ 1][mt] = lds_row<vec>(cQ + 32 * mt * D, lo_.row[s + 1]);
-                    ad[c ^ 1][mt] = lds_row<vec>(cdY + 32 * mt * D, lo_.row[s + 1]);
-                }
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                accS[mt] = Op16<T>::mfma(aq[c][mt], kreg[s], accS[mt]);
-                accP[mt] = Op16<T>::mfma(ad[c][mt], vreg[s], accP[mt]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            qoff[u] = dma_offset<D>(w * TW + u, lane, p.q_st) - 1024 * u;
+            dyoff[u] = dma_offset<D>(w * TW + u, lane, p.dy_st) - 1024 * u;
         }
 
-        // Ps / Pd into accS, dS into accP; element (query row 32mt + acc_row(a, h), key jw)
-        bool full = (q0 + BQ <= L) && (j0 + BKV <= K);
-        if (p.mode == FA_MASK_CAUSAL) {
-            full = full && (j0 + BKV - 1 <= q0 + off);
-        } else if (p.mode == FA_MASK_BAND) {
-            full = full && (j0 >= q0 + BQ - 1 + off - p.pre) && (j0 + BKV - 1 <= q0 + off + p.nxt);
-        }
-        auto softmax_grad = [&](auto masked_tag) {
-            constexpr bool MASKED = decltype(masked_tag)::value;
-            int lo = 0;
-            int hi = BQ - 1;
-            if constexpr (MASKED) {
-                hi = min(L - q0, BQ) - 1;
-                if (jw >= K) hi = -1;
-                if (p.mode == FA_MASK_CAUSAL) {
-                    lo = max(lo, jw - off - q0);
-                } else if (p.mode == FA_MASK_BAND) {
-                    lo = max(lo, jw - off - p.nxt - q0);
-                    hi = min(hi, jw - off + p.pre - q0);
-                }
-                lo -= 4 * h;
-                hi -= 4 * h;
+        // this lane's K and V rows: B operands of S = Q K^T and dP = dY V^T
+        vec kreg[D / 16];
+        vec vreg[D / 16];
+        {
+            const bool ok = jw < K;
+            const int64_t row = it.kv_start + (ok ? jw : 0);
+            const vec* kr = reinterpret_cast<const vec*>(static_cast<const T*>(p.k) + row * p.k_st + n * p.k_sh);
+            const vec* vr = reinterpret_cast<const vec*>(static_cast<const T*>(p.v) + row * p.v_st + n * p.v_sh);
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                kreg[s] = ok ? kr[2 * s + h] : vec{};
+                vreg[s] = ok ? vr[2 * s + h] : vec{};
             }
+        }
+
+        // Query rows this lane's key admits, [lo_row, hi_row]; the element of step rows q0s..
+        // in accumulator slot a (query row q0s + 4h + cc(a), cc(a) = 8*(a/4) + a%4) is admitted
+        // iff (unsigned)(cc(a) - (lo_base - q0s)) <= rng.
+        int lo_base;
+        int rng;
+        {
+            int lo_row = 0;
+            int hi_row = L - 1;
+            if (p.mode == FA_MASK_CAUSAL) {
+                lo_row = max(0, jw - off);
+            } else if (p.mode == FA_MASK_BAND) {
+                lo_row = max(0, jw - off - p.nxt);
+                hi_row = min(hi_row, jw - off + p.pre);
+            }
+            if (jw < K && lo_row <= hi_row) {
+                lo_base = lo_row - 4 * h;
+                rng = hi_row - lo_row;
+            } else {
+                lo_base = -(1 << 30);
+                rng = 0;
+            }
+        }
+
+        // HBM -> LDS copy of query tile t (Q, dY, row statistics) into buffer b
+        auto issue = [&](int t, int b) {
+            const int q0 = t * BQ;
+            const i32x4 rq = buffer_desc(gq + static_cast<int64_t>(q0) * p.q_st, tile_bytes(L - q0, BQ, p.q_st));
+            const i32x4 rd = buffer_desc(gdy + static_cast<int64_t>(q0) * p.dy_st, tile_bytes(L - q0, BQ, p.dy_st));
+            const uint32_t mq = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sBuf[b][0] + w * TW * 512)));
+            const uint32_t md = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sBuf[b][1] + w * TW * 512)));
+            dma_pair<TW>(__builtin_amdgcn_readfirstlane(mq), rq, qoff, __builtin_amdgcn_readfirstlane(md), rd, dyoff);
+            if (w == NW - 1 && lane < BQ / 2) {
+                const i32x4 rs = buffer_desc(gstat + q0, q0 < L ? static_cast<uint32_t>(min(L - q0, BQ) * 8) : 0u);
+                dma16_async(sSt[b], rs, lane * 16);
+            }
+        };
+
+        // where a step reads: X rows 32*xm.. of buffer xb, softmax statistics of rows 32*sm..
+        // of buffer sb, Y rows 32*ym.. of buffer yb
+        struct Where {
+            int xb, xm, sb, sm, yb, ym;
+        };
+        auto where = [](int kind, int b) -> Where {
+            const int b1 = b == NB - 1 ? 0 : b + 1;
+            const int b2 = b == 0 ? NB - 1 : b - 1;
+            if (kind == kStepA) return {b, 1, b, 0, b2, 1};
+            if (kind == kStepB) return {b1, 0, b, 1, b, 0};
+            if (kind == kStepFirst) return {0, 0, 0, 0, 0, 0};
+            return {b, 0, b, 0, b, 1};  // last
+        };
+        // operand of slot k of a step: k even -> X (row read of Q or dY), k odd -> Y
+        // (transposing read of dY or Q)
+        auto read_op = [&](const Where& wh, auto kc) -> vec {
+            constexpr int k = decltype(kc)::value;
+            constexpr int j = k / 2;
+            if constexpr (k % 2 == 0) {
+                const T* base = sBuf[wh.xb][j % 2] + 32 * wh.xm * D;
+                return lds_row<vec>(base, lo_.row[j / 2]);
+            } else {
+                constexpr int kk = j / (2 * NT);
+                constexpr int nt = (j / 2) % NT;
+                const T* base = sBuf[wh.yb][1 - j % 2] + (32 * wh.ym + 16 * kk) * D;
+                return lds_tr<vec>(base, lo_.tr[nt][0], lo_.tr[nt][1]);
+            }
+        };
+        // statistics {delta, beta} of rows 32*sm + 8g + 4h + 0..3
+        auto read_stats = [&](const Where& wh, int g, f32x4* dst) {
+            const float2* base = sSt[wh.sb] + 32 * wh.sm + 8 * g + 4 * h;
+            dst[0] = *reinterpret_cast<const f32x4*>(base);
+            dst[1] = *reinterpret_cast<const f32x4*>(base + 2);
+        };
+
+        // pipeline state carried from step to step
+        vec opr[NOPS];         // operand of each slot, read LA slots ahead
+        f32x4 stC[4][2];       // statistics of the softmax rows of the step
+        f32x16 sC = zero16();  // S and dP consumed by this step's softmax gradient
+        f32x16 pC = zero16();
+        vec pkY[2];            // packed P and dS consumed by this step's Y (two 16-row halves)
+        vec dsY[2];
+        uint32_t dbC[16];      // dropout mask bytes and bit base of the softmax rows
+        int dcC = 0;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+        for (int i = 0; i < 2; ++i) {
+            pkY[i] = vec{};
+            dsY[i] = vec{};
+        }
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int rb = 32 * mt + 8 * g + 4 * h;
-                    const f32x4 s01 = *reinterpret_cast<const f32x4*>(&cSt[rb]);
-                    const f32x4 s23 = *reinterpret_cast<const f32x4*>(&cSt[rb + 2]);
-                    const float dl[4] = {s01[0], s01[2], s23[0], s23[2]};
-                    const float bt[4] = {s01[1], s01[3], s23[1], s23[3]};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int a = 4 * g + r;
-                        const int c = 32 * mt + 8 * g + r;
-                        float pv = __builtin_amdgcn_exp2f(accS[mt][a] * p.exp_scale - bt[r]);
-                        bool adm = true;
-                        if constexpr (MASKED) {
-                            adm = (c >= lo) && (c <= hi);
-                            pv = adm ? pv : 0.f;
-                        }
-                        if constexpr (DROP) {
-                            float zk = 0.f;
-                            if (adm) {
-                                const int64_t bit =
-                                    it.drop_base + (static_cast<int64_t>(n) * L + q0 + c + 4 * h) * K + jw;
-                                zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
-                            }
-                            accP[mt][a] = pv * (accP[mt][a] * zk - dl[r]);
-                            accS[mt][a] = pv * zk;
+        for (int i = 0; i < 16; ++i) dbC[i] = 0;
+
+        // One step (see the kinds above) of the tile in buffer b, tile index t; nkind / nb:
+        // the step that follows (its first operands and statistics are read at the end).
+        auto step = [&](auto kc, auto nkc, auto mc, int t, int b, int nb) {
+            constexpr int KIND = decltype(kc)::value;
+            constexpr int NKIND = decltype(nkc)::value;
+            constexpr bool MASKED = decltype(mc)::value != 0;  // tile t has pairs outside the mask
+            constexpr bool HX = KIND != kStepLast;
+            constexpr bool HS = KIND == kStepA || KIND == kStepB;
+            constexpr bool HY = KIND != kStepFirst;
+            const Where wh = where(KIND, b);
+            const Where nw = where(NKIND, nb);
+            const int lo_h = lo_base - (t * BQ + 32 * wh.sm);
+            f32x16 sN = zero16();
+            f32x16 pN = zero16();
+            uint32_t pkw[2][4];
+            uint32_t dsw[2][4];
+            vec nopr[LA];
+            f32x4 stN[2];
+            float pv[16];
+            float pdv[16];
+            float dsv[16];
+            uint32_t dbN[16];
+            int dcN = 0;
+            // dropout bits of the X rows: the bit of (row 4h + cc(a), key jw) sits at bit
+            // dcN + cc(a) * K of the buffer that starts at the step's first mask byte
+            __amdgpu_buffer_rsrc_t drs;
+            if constexpr (DROP && HX) {
+                const int xt = t + (KIND == kStepB ? 1 : 0);
+                const int64_t bits =
+                    it.drop_base + (static_cast<int64_t>(n) * L + xt * BQ + 32 * wh.xm) * K;
+                const int64_t byte0 = bits >> 3;
+                const int64_t left = p.drop_bytes - byte0;
+                drs = raw_rsrc(p.drop_mask + byte0,
+                               left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left)));
+                dcN = static_cast<int>(bits & 7) + 4 * h * K + jw;
+            }
+            static_for<0, NOPS>([&](auto slot) {
+                constexpr int k = decltype(slot)::value;
+                constexpr int j = k / 2;
+                // ---- the MFMA of slot k
+                if constexpr (k % 2 == 0) {
+                    if constexpr (HX) {
+                        constexpr int s = j / 2;
+                        vec a = opr[k];
+                        pin(a);
+                        if constexpr (j % 2 == 0) {
+                            sN = Op16<T>::mfma(a, kreg[s], s == 0 ? zero16() : sN);
+                            pin(sN);
                         } else {
-                            accP[mt][a] = pv * (accP[mt][a] - dl[r]);
-                            accS[mt][a] = pv;
+                            pN = Op16<T>::mfma(a, vreg[s], s == 0 ? zero16() : pN);
+                            pin(pN);
+                        }
+                    }
+                } else {
+                    if constexpr (HY) {
+                        constexpr int kk = j / (2 * NT);
+                        constexpr int nt = (j / 2) % NT;
+                        if constexpr (j % 2 == 0) {
+                            MfmaAccV<T>::run(accV[nt], pkY[kk], opr[k]);
+                        } else {
+                            MfmaAccV<T>::run(accK[nt], dsY[kk], opr[k]);
                         }
                     }
                 }
-            }
-        };
-        if (full) {
-            softmax_grad(Tag<false>{});
-        } else {
-            softmax_grad(Tag<true>{});
-        }
-
-        // dV += Pd^T dY, dK += dS^T Q: slots 8kk..8kk+3 are rows 32mt + 16kk + 4h + 0..3,
-        // slots 8kk+4..8kk+7 rows 32mt + 16kk + 8 + 4h + 0..3
-        // the transposing reads of step i + 1 are issued while step i runs
-        constexpr int NSTEP = MT * 2 * NT;  // (mt, kk, nt)
-        vec bd[2];
-        vec bq[2];
-        auto tr_load = [&](int i, int slot) {
-            const int nt = i % NT;
-            const int rowoff = 16 * (i / NT) * D;  // 32mt + 16kk = 16 * (i / NT)
-            bd[slot] = lds_tr<vec>(cdY + rowoff, lo_.tr[nt][0], lo_.tr[nt][1]);
-            bq[slot] = lds_tr<vec>(cQ + rowoff, lo_.tr[nt][0], lo_.tr[nt][1]);
-        };
-        tr_load(0, 0);
-        vec ap, as;
+                // ---- softmax gradient of element a = k / EPS: P in part one, dS in part two
+                if constexpr (HS) {
+                    constexpr int a = k / EPS;
+                    constexpr int cc = 8 * (a / 4) + (a % 4);
+                    if constexpr (k % EPS == 0) {
+                        float x = sC[a];
+                        pin(x);
+                        const float bt = stC[a / 4][(a % 4) / 2][2 * (a % 2) + 1];
+                        const float e = __builtin_amdgcn_exp2f(x * p.exp_scale - bt);
+                        if constexpr (MASKED) {
+                            const bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(rng);
+                            pv[a] = adm ? e : 0.f;
+                        } else {
+                            pv[a] = e;
+                        }
+                        pin(pv[a]);
+                    }
+                    if constexpr (k % EPS == EPS - 1) {
+                        float y = pC[a];
+                        pin(y);
+                        const float dl = stC[a / 4][(a % 4) / 2][2 * (a % 2)];
+                        if constexpr (DROP) {
+                            const int u = dcC + cc * K;
+                            const bool keep = __builtin_amdgcn_ubfe(dbC[a], u & 7, 1) != 0;
+                            pdv[a] = keep ? pv[a] * p.inv_keep : 0.f;
+                            dsv[a] = pv[a] * ((keep ? y * p.inv_keep : 0.f) - dl);
+                        } else {
+                            pdv[a] = pv[a];
+                            dsv[a] = pv[a] * (y - dl);
+                        }
+                        if constexpr (a % 2 == 1) {
+                            pkw[a / 8][(a % 8) / 2] = pack2<T>(pdv[a - 1], pdv[a]);
+                            dsw[a / 8][(a % 8) / 2] = pack2<T>(dsv[a - 1], dsv[a]);
+                            pin(pkw[a / 8][(a % 8) / 2]);
+                            pin(dsw[a / 8][(a % 8) / 2]);
+                        }
+                    }
+                }
+                // ---- tile barrier: tile t + 1 has landed and every wave is done with the buffer
+                // of tile t - 1, which then receives tile t + 2
+                if constexpr (KIND == kStepA && k == NOPS - LA) {
+                    wait_dma();
+                    __syncthreads();
+                    if (t + 2 < te) issue(t + 2, wh.yb);
+                }
+                // ---- LDS reads for slot k + LA (of the next step near the end)
+                constexpr int kr = k + LA;
+                if constexpr (kr < NOPS) {
+                    if constexpr ((kr % 2 == 0 && HX) || (kr % 2 == 1 && HY)) opr[kr] = read_op(wh, IC<kr>{});
+                    if constexpr (HS && kr % (4 * EPS) == 0) read_stats(wh, kr / (4 * EPS), stC[kr / (4 * EPS)]);
+                } else if constexpr (KIND != kStepLast) {
+                    nopr[kr - NOPS] = read_op(nw, IC<kr - NOPS>{});
+                    if constexpr (kr == NOPS && (NKIND == kStepA || NKIND == kStepB)) read_stats(nw, 0, stN);
+                }
+                // ---- dropout mask byte of X element k
+                if constexpr (DROP && HX && k < 16) {
+                    constexpr int cc = 8 * (k / 4) + (k % 4);
+                    const int u = dcN + cc * K;
+                    dbN[k] = __builtin_amdgcn_raw_buffer_load_b8(drs, u >> 3, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // hand the pipeline over to the next step
+            if constexpr (HX) {
+                sC = sN;
+                pC = pN;
+                if constexpr (DROP) {
 #pragma unroll
-        for (int i = 0; i < NSTEP; ++i) {
-            const int nt = i % NT;
-            const int q16 = i / NT;  // 2 * mt + kk
-            if (nt == 0) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    ap[e] = static_cast<T>(accS[q16 >> 1][8 * (q16 & 1) + e]);
-                    as[e] = static_cast<T>(accP[q16 >> 1][8 * (q16 & 1) + e]);
+                    for (int i = 0; i < 16; ++i) dbC[i] = dbN[i];
+                    dcC = dcN;
                 }
             }
-            if (i + 1 < NSTEP) tr_load(i + 1, (i + 1) & 1);
-            accV[nt] = Op16<T>::mfma(ap, bd[i & 1], accV[nt]);
-            accK[nt] = Op16<T>::mfma(as, bq[i & 1], accK[nt]);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (HS) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint4 pw = make_uint4(pkw[i][0], pkw[i][1], pkw[i][2], pkw[i][3]);
+                    const uint4 dw = make_uint4(dsw[i][0], dsw[i][1], dsw[i][2], dsw[i][3]);
+                    pkY[i] = __builtin_bit_cast(vec, pw);
+                    dsY[i] = __builtin_bit_cast(vec, dw);
+                    // formed here, well before the Y MFMAs of the next step read them
+                    pin(pkY[i]);
+                    pin(dsY[i]);
+                }
+            }
+            if constexpr (KIND != kStepLast) {
+#pragma unroll
+                for (int i = 0; i < LA; ++i) opr[i] = nopr[i];
+                if constexpr (NKIND == kStepA || NKIND == kStepB) {
+                    stC[0][0] = stN[0];
+                    stC[0][1] = stN[1];
+                }
+            }
+        };
+
+        // prologue: tiles tb and tb + 1 in flight, zeros in the third buffer (read by the Y of
+        // the step before the first, whose packed P / dS are zero)
+        issue(tb, 0);
+        if (tb + 1 < te) issue(tb + 1, 1);
+        for (int i = threadIdx.x; i < 2 * TILE / 8; i += 64 * NW) reinterpret_cast<vec*>(sBuf[2][0])[i] = vec{};
+        wait_dma();
+        __syncthreads();
+        {
+            const Where w0 = where(kStepFirst, 0);
+            static_for<0, LA>([&](auto kc) {
+                if constexpr (decltype(kc)::value % 2 == 0) opr[decltype(kc)::value] = read_op(w0, kc);
+            });
         }
+        // Tiles whose 64 rows all see all 128 keys of the block need no mask.  For the causal and
+        // band windows they form one run [f0, f1): rows in range (t < L / 64), keys in range, and
+        // the window admits the block's corner pairs.
+        int f0 = tb;
+        int f1 = tb;
+        {
+            auto floor_div = [](int a) { return a >= 0 ? a / BQ : -((-a + BQ - 1) / BQ); };
+            auto ceil_div = [&](int a) { return -floor_div(-a); };
+            int lo = tb;
+            int hi = min(te, L / BQ);
+            if (j0 + BKV > K) hi = lo;
+            if (p.mode == FA_MASK_CAUSAL) {
+                lo = max(lo, ceil_div(j0 + BKV - 1 - off));
+            } else if (p.mode == FA_MASK_BAND) {
+                lo = max(lo, ceil_div(j0 + BKV - 1 - off - p.nxt));
+                hi = min(hi, floor_div(j0 - (BQ - 1) - off + p.pre) + 1);
+            }
+            f0 = min(max(lo, tb), te);
+            f1 = min(max(hi, f0), te);
+        }
+        step(IC<kStepFirst>{}, IC<kStepA>{}, IC<0>{}, tb, 0, 0);
+        int b = 0;
+        auto next_buf = [](int x) { return x == NB - 1 ? 0 : x + 1; };
+        for (int t = tb; t < f0; ++t) {
+            step(IC<kStepA>{}, IC<kStepB>{}, IC<1>{}, t, b, b);
+            step(IC<kStepB>{}, IC<kStepA>{}, IC<1>{}, t, b, next_buf(b));
+            b = next_buf(b);
+        }
+        for (int t = f0; t < f1; ++t) {
+            step(IC<kStepA>{}, IC<kStepB>{}, IC<0>{}, t, b, b);
+            step(IC<kStepB>{}, IC<kStepA>{}, IC<0>{}, t, b, next_buf(b));
+            b = next_buf(b);
+        }
+        for (int t = f1; t < te; ++t) {
+            step(IC<kStepA>{}, IC<kStepB>{}, IC<1>{}, t, b, b);
+            step(IC<kStepB>{}, IC<kStepA>{}, IC<1>{}, t, b, next_buf(b));
+            b = next_buf(b);
+        }
+        // Y of the last tile's second half (buffer of tile te - 1)
+        step(IC<kStepLast>{}, IC<kStepLast>{}, IC<0>{}, te - 1, b == 0 ? NB - 1 : b - 1, 0);
     }
+
+    // the accumulators were last written by MFMAs the compiler does not see: wait them out
+    // before any other instruction reads them
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(accK[nt]), "+a"(accV[nt]));
 
     // epilogue: dK = scale * sum dS^T Q, dV = sum Pd^T dY; the lane holds column nt*32 + col
     // of key rows 8g + 4h + r

@@ -70,6 +70,7 @@ struct Bwd16Args {
     const fa_work_item_t* items_kv;  // key-block items (FA16_DKDV_BLOCK keys, FA16_DKDV_TILE_Q tiles)
     const fa_work_item_t* items_q;   // query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles)
     const uint8_t* drop_mask;
+    int64_t drop_bytes;  // size of the dropout mask in bytes (bounds its reads)
     int32_t tq, heads, mode, pre, nxt;
     float exp_scale, inv_keep, scale;
 };
