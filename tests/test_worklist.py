@@ -43,7 +43,7 @@ def _check(lq, lkv, mode, pre, nxt, heads, block_rows, tile_rows, kind):
             assert got == tiles, (b, blk, sorted(got), sorted(tiles))
 
 
-KINDS = [(B.FA_ITEMS_KEY_BLOCKS, 128, 64), (B.FA_ITEMS_KEY_BLOCKS, 128, 32),
+KINDS = [(B.FA_ITEMS_KEY_BLOCKS, 128, 64), (B.FA_ITEMS_KEY_BLOCKS, 128, 32), (B.FA_ITEMS_QUERY_BLOCKS, 256, 64),
          (B.FA_ITEMS_QUERY_BLOCKS, 256, 32), (B.FA_ITEMS_QUERY_BLOCKS, 64, 64)]
 
 

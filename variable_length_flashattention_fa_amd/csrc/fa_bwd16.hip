@@ -72,17 +72,18 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ int acc_row(int a, int h) { return 8 * (a >> 2) + 4 * h + (a & 3); }
 
 // ---- swizzled [rows][D] tiles -----------------------------------------------------------------
-// Chunk c (16 bytes) of row r is stored at chunk c ^ swz(r).  For D = 128 a row fills
-// all 64 banks; for D = 64 two rows share them.  Both functions make 16 consecutive
-// rows read at one logical chunk land on 16 distinct chunk positions, and make
-// 4 consecutive rows (first one a multiple of 4) read at two adjacent logical chunks
-// land on 8 distinct positions.
+// Chunk c (16 bytes) of row r is stored at chunk c ^ swz(r).  For D = 128 a row fills all 64
+// banks; for D = 64 two rows share them.  The swizzle is a bijection on the chunk positions of
+// 16 consecutive rows (so 16 lanes reading one logical chunk of 16 rows hit 16 distinct bank
+// groups), and gives the four rows r0 .. r0+3 (r0 a multiple of 4) that a transposing read
+// touches chunk blocks that do not overlap for logical chunks 0..3 (32 lanes, 16 distinct
+// bank groups).
 template <int D>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (D == 128) {
-        return ((row & 7) << 1) | ((row >> 3) & 1);
+        return ((row & 3) << 2) | ((row >> 2) & 3);
     } else {
-        return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
     }
 }
 
@@ -158,8 +159,18 @@ __device__ __forceinline__ void dma_pair(uint32_t m0a, const i32x4& da, const in
             : "s"(m0a), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "s"(da), "s"(m0b), "v"(vb[0]), "v"(vb[1]),
               "v"(vb[2]), "v"(vb[3]), "s"(db)
             : "memory");
+    } else if constexpr (TW == 1) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+            "s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %5, %6, 0 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0a), "v"(va[0]), "s"(da), "s"(m0b), "v"(vb[0]), "s"(db)
+            : "memory");
     } else {
-        static_assert(TW == 2, "runs of 2 or 4 KiB");
+        static_assert(TW == 2, "runs of 1, 2 or 4 KiB");
         asm volatile(
             "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
             "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
@@ -745,22 +756,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 // ------------------------------------------------------------------------------------------------
 // dQ
 // ------------------------------------------------------------------------------------------------
-// Workgroup: 8 waves, FA16_DQ_BLOCK = 256 queries; wave w owns queries 32w .. 32w+31.
+// Workgroup: 8 waves (two per SIMD), FA16_DQ_BLOCK = 256 queries; wave w owns queries 32w ..
+// 32w+31 and keeps their Q and dY rows (in accumulation registers), statistics and dQ^T
+// accumulator.  Key tiles of FA16_DQ_TILE_K = 64 rows are walked as two 32-key steps:
+//   S^T = K Q^T, dP^T = V dY^T   (A = K / V rows from LDS, B = Q / dY)
+//   dS^T = Ps (dP Z/kp - D)      (each lane holds one query: its D and beta are scalars)
+//   dQ^T += K^T dS^T             (A = transposing reads of K, B = dS^T straight from registers)
 
 template <typename T, int D, bool DROP>
 __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     using vec = typename Op16<T>::vec;
     constexpr int NW = 8;
     constexpr int BQ = FA16_DQ_BLOCK;    // queries per workgroup
-    constexpr int BK = FA16_DQ_TILE_K;   // key tile rows (32)
+    constexpr int BK = FA16_DQ_TILE_K;   // key tile rows (64): two steps of 32
     constexpr int ND = D / 32;           // 32-row head-dim tiles of dQ^T
     constexpr int TI = BK * D / 8 / 64;  // DMA instructions per key tile and tensor
-    static_assert(BQ == 32 * NW && BK == 32 && TI <= NW, "tile shape");
+    constexpr int TW = TI / NW;          // ... per wave
+    static_assert(BQ == 32 * NW && BK == 64 && TI % NW == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) T sK0[BK * D];
-    __shared__ __attribute__((aligned(16))) T sK1[BK * D];
-    __shared__ __attribute__((aligned(16))) T sV0[BK * D];
-    __shared__ __attribute__((aligned(16))) T sV1[BK * D];
+    __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
+    __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
 
     const fa_work_item_t it = p.items_q[blockIdx.x];
     const int n = blockIdx.y;
@@ -779,8 +794,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 
     const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + n * p.k_sh;
     const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + n * p.v_sh;
-    const int koff = w < TI ? dma_offset<D>(w, lane, p.k_st) : 0;
-    const int voff = w < TI ? dma_offset<D>(w, lane, p.v_st) : 0;
+    // wave w copies 1 KiB chunks w*TW .. w*TW + TW - 1 of each key tile (one run)
+    int koff[TW];
+    int voff[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+        koff[u] = dma_offset<D>(w * TW + u, lane, p.k_st) - 1024 * u;
+        voff[u] = dma_offset<D>(w * TW + u, lane, p.v_st) - 1024 * u;
+    }
+    auto issue = [&](int kt, int b) {
+        const int k0 = kt * BK;
+        const i32x4 rk = buffer_desc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st));
+        const i32x4 rv = buffer_desc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st));
+        const uint32_t mk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TW * 512)));
+        const uint32_t mv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TW * 512)));
+        dma_pair<TW>(__builtin_amdgcn_readfirstlane(mk), rk, koff, __builtin_amdgcn_readfirstlane(mv), rv, voff);
+    };
 
     // this lane's Q and dY rows (B operands of S^T = K Q^T and dP^T = V dY^T) and statistics
     vec qreg[D / 16];
@@ -796,6 +825,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         for (int s = 0; s < D / 16; ++s) {
             qreg[s] = ok ? qr[2 * s + h] : vec{};
             dyreg[s] = ok ? dr[2 * s + h] : vec{};
+            asm volatile("" : "+a"(qreg[s]), "+a"(dyreg[s]));
         }
         if (ok) {
             const float2 st = p.rowstat[static_cast<int64_t>(n) * p.tq + it.q_start + qi];
@@ -803,16 +833,28 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             beta = st.y;
         }
     }
-    // keys this lane's query admits: [klo, khi]
-    int klo = 0;
-    int khi = qi < L ? K - 1 : -1;
-    if (p.mode == FA_MASK_CAUSAL) {
-        khi = min(khi, qi + off);
-    } else if (p.mode == FA_MASK_BAND) {
-        klo = max(klo, qi + off - p.pre);
-        khi = min(khi, qi + off + p.nxt);
+    // keys this lane's query admits, [klo, khi]; element a of a step starting at key k0s
+    // (key k0s + 4h + cc(a)) is admitted iff (unsigned)(cc(a) - (kbase - k0s)) <= krng
+    int kbase;
+    int krng;
+    {
+        int klo = 0;
+        int khi = K - 1;
+        if (p.mode == FA_MASK_CAUSAL) {
+            khi = min(khi, qi + off);
+        } else if (p.mode == FA_MASK_BAND) {
+            klo = max(klo, qi + off - p.pre);
+            khi = min(khi, qi + off + p.nxt);
+        }
+        if (qi < L && klo <= khi) {
+            kbase = klo - 4 * h;
+            krng = khi - klo;
+        } else {
+            kbase = -(1 << 30);
+            krng = 0;
+        }
     }
-    // keys admitted by every query of the wave (uniform): tiles inside need no mask
+    // keys admitted by every query of the wave (uniform): steps inside need no mask
     const bool wave_rows_full = i0 + 31 < L;
     int wlo = 0;
     int whi = K - 1;
@@ -827,21 +869,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 #pragma unroll
     for (int i = 0; i < ND; ++i) accQ[i] = zero16();
 
-    auto issue = [&](int kt, T* dK, T* dV) {
-        const int k0 = kt * BK;
-        if (w < TI) {
-            dma_issue(dK, w, raw_rsrc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st)), koff);
-            dma_issue(dV, w, raw_rsrc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st)), voff);
-        }
-    };
-
-    auto body = [&](int kt, const T* cK, const T* cV, T* nK, T* nV) {
-        wait_dma();
-        __syncthreads();
-        if (kt + 1 < it.tile_end) issue(kt + 1, nK, nV);
-        const int k0 = kt * BK;
-
-        // S^T = K Q^T, dP^T = V dY^T (32 keys x this wave's 32 queries)
+    // one 32-key step (keys k0s .. k0s + 31, rows 32 kh of the tile in cK / cV)
+    auto kstep = [&](const T* cK, const T* cV, int k0s) {
         f32x16 accS = zero16();
         f32x16 accP = zero16();
 #pragma unroll
@@ -851,37 +880,36 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             accS = Op16<T>::mfma(ak, qreg[s], accS);
             accP = Op16<T>::mfma(av, dyreg[s], accP);
         }
-
-        // dS^T = Ps (dP Z/kp - D) into accP; element (key k0 + acc_row(a, h), query qi)
-        const bool full = wave_rows_full && (k0 >= wlo) && (k0 + BK - 1 <= whi);
+        // dS^T = Ps (dP Z/kp - D); element (key k0s + 4h + cc(a), query qi)
+        const bool full = wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
+        uint32_t dsw[2][4];
         auto softmax_grad = [&](auto masked_tag) {
             constexpr bool MASKED = decltype(masked_tag)::value;
-            int lo = 0;
-            int hi = 0;
-            if constexpr (MASKED) {
-                lo = klo - k0 - 4 * h;
-                hi = khi - k0 - 4 * h;
-            }
+            const int lo_h = kbase - k0s;
 #pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                const int c = 8 * (a >> 2) + (a & 3);
-                float pv = __builtin_amdgcn_exp2f(accS[a] * p.exp_scale - beta);
-                bool adm = true;
-                if constexpr (MASKED) {
-                    adm = (c >= lo) && (c <= hi);
-                    pv = adm ? pv : 0.f;
-                }
-                if constexpr (DROP) {
-                    float zk = 0.f;
-                    if (adm) {
-                        const int64_t bit =
-                            it.drop_base + (static_cast<int64_t>(n) * L + qi) * K + k0 + c + 4 * h;
-                        zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
+            for (int a = 0; a < 16; a += 2) {
+                float ds[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int cc = 8 * ((a + e) >> 2) + ((a + e) & 3);
+                    float pv = __builtin_amdgcn_exp2f(accS[a + e] * p.exp_scale - beta);
+                    if constexpr (MASKED) {
+                        const bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(krng);
+                        pv = adm ? pv : 0.f;
                     }
-                    accP[a] = pv * (accP[a] * zk - delta);
-                } else {
-                    accP[a] = pv * (accP[a] - delta);
+                    if constexpr (DROP) {
+                        float zk = 0.f;
+                        if (pv != 0.f) {
+                            const int64_t bit =
+                                it.drop_base + (static_cast<int64_t>(n) * L + qi) * K + k0s + cc + 4 * h;
+                            zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
+                        }
+                        ds[e] = pv * (accP[a + e] * zk - delta);
+                    } else {
+                        ds[e] = pv * (accP[a + e] - delta);
+                    }
                 }
+                dsw[a >> 3][(a & 7) >> 1] = pack2<T>(ds[0], ds[1]);
             }
         };
         if (full) {
@@ -889,13 +917,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         } else {
             softmax_grad(Tag<true>{});
         }
-
-        // dQ^T[d][q] += sum_key K[key][d] dS^T[key][q]
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            vec bs;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bs[e] = static_cast<T>(accP[8 * kk + e]);
+            const vec bs = __builtin_bit_cast(vec, make_uint4(dsw[kk][0], dsw[kk][1], dsw[kk][2], dsw[kk][3]));
 #pragma unroll
             for (int nd = 0; nd < ND; ++nd) {
                 const vec ak = lds_tr<vec>(cK + 16 * kk * D, lo_.tr[nd][0], lo_.tr[nd][1]);
@@ -904,10 +928,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         }
     };
 
-    if (it.tile_begin < it.tile_end) issue(it.tile_begin, sK0, sV0);
-    for (int kt = it.tile_begin; kt < it.tile_end; kt += 2) {
-        body(kt, sK0, sV0, sK1, sV1);
-        if (kt + 1 < it.tile_end) body(kt + 1, sK1, sV1, sK0, sV0);
+    if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
+    int b = 0;
+    for (int kt = it.tile_begin; kt < it.tile_end; ++kt) {
+        wait_dma();
+        __syncthreads();  // tile kt is in buffer b; every wave is done with buffer b ^ 1
+        if (kt + 1 < it.tile_end) issue(kt + 1, b ^ 1);
+        kstep(sK[b], sV[b], kt * BK);
+        kstep(sK[b] + 32 * D, sV[b] + 32 * D, kt * BK + 32);
+        b ^= 1;
     }
 
     // epilogue: dQ = scale * (dQ^T)^T; the lane holds query qi, head-dim rows

@@ -54,7 +54,7 @@ hipError_t launch_convert(int32_t dtype, int head_dim, const float* dq_acc, void
 constexpr int FA16_DKDV_BLOCK = 128;  // keys per dK/dV workgroup
 constexpr int FA16_DKDV_TILE_Q = 64;  // query rows per dK/dV step
 constexpr int FA16_DQ_BLOCK = 256;    // queries per dQ workgroup
-constexpr int FA16_DQ_TILE_K = 32;    // key rows per dQ step
+constexpr int FA16_DQ_TILE_K = 64;    // key rows per dQ tile (two steps of 32)
 
 struct Bwd16Args {
     const void* q;
