@@ -164,16 +164,22 @@ def main(argv=None):
         log(f"calibration copy of {args.calibration_copy_mib} MiB done")
     B.profile_read()  # drop anything recorded before the timed region
     B.profile_enable(True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     B.profile_enable(False)
     prof = B.profile_read()
     ms_per_step = elapsed * 1e3 / args.steps
+    call_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    measured_peak = {w: B.mfma_peak(w) for w in (1, 2)}
+    log(f"measured bf16 MFMA rate: {measured_peak[1]:.0f} TFLOP/s (1 wave/SIMD), {measured_peak[2]:.0f} (2 waves/SIMD)")
 
     pairs = pair_count(inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt)
     useful = 10.0 * wl.heads * wl.head_dim * pairs
@@ -205,6 +211,9 @@ def main(argv=None):
     dominant = max((k for k in kernels if "TFLOP/s" in kernels[k]), key=lambda k: kernels[k]["avg_ms"])
     achieved = kernels[dominant]["TFLOP/s"]
     main_avg = kernels[dominant]["avg_ms"]
+    if q.dtype != torch.float32:
+        kernels["bwd_dkdv16_kernel"]["frac_of_measured_peak"] = kernels["bwd_dkdv16_kernel"]["TFLOP/s"] / max(measured_peak.values())
+        kernels["bwd_dq16_kernel"]["frac_of_measured_peak"] = kernels["bwd_dq16_kernel"]["TFLOP/s"] / max(measured_peak.values())
 
     dtype_name = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[q.dtype]
     out = {
@@ -224,6 +233,10 @@ def main(argv=None):
                    "head_dim": wl.head_dim, "mask": ["none", "causal", "band"][wl.mode], "pre_tokens": wl.pre,
                    "next_tokens": wl.nxt, "keep_prob": wl.keep_prob, "admitted_pairs_per_head": pairs},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "max": call_ms[-1]},
+        "measured_mfma_peak": {"tflops_1_wave_per_simd": measured_peak[1], "tflops_2_waves_per_simd": measured_peak[2],
+                               "frac_of_measured": value / max(measured_peak.values()),
+                               "dominant_kernel_frac_of_measured": achieved / max(measured_peak.values())},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for(wl.name, dominant),
                      "kernel": dominant, "avg_ms": main_avg},

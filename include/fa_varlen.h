@@ -188,6 +188,13 @@ void fa_profile_enable(int on);
  * -FA_ERR_RUNTIME if an event could not be read. */
 int fa_profile_read(double* ms, int64_t* launches, int capacity);
 
+/* Measured matrix-core ceiling of the current device (a diagnostic, not part of the
+ * operator): runs a kernel of independent bf16 32x32x16 MFMAs, one workgroup per compute
+ * unit with waves_per_simd (1 or 2) waves on each SIMD, on the null stream, synchronously,
+ * and writes its rate in TFLOP/s to *tflops.  Returns FA_OK, FA_ERR_NULLPTR (tflops null),
+ * FA_ERR_INVALID (waves_per_simd not 1 or 2) or FA_ERR_RUNTIME. */
+int fa_mfma_peak(int32_t waves_per_simd, double* tflops);
+
 #ifdef __cplusplus
 }
 #endif

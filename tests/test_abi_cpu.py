@@ -135,3 +135,11 @@ def test_empty_query_returns_ok_without_device_work():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         B.load(str(tmp_path / "libfa_varlen.so"))
+
+
+def test_mfma_peak_rejects_bad_arguments():
+    lib = B.load()
+    out = ctypes.c_double(0.0)
+    assert lib.fa_mfma_peak(2, None) == 1  # FA_ERR_NULLPTR
+    assert lib.fa_mfma_peak(3, ctypes.byref(out)) == 2  # FA_ERR_INVALID
+    assert lib.fa_mfma_peak(0, ctypes.byref(out)) == 2

@@ -281,3 +281,12 @@ def test_full_size_sampled(number):
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
     log(f"  workload {number} sampled parity ok ({time.time() - t0:.1f}s)")
+
+
+@pytest.mark.gpu
+def test_measured_mfma_peak_is_plausible():
+    """The matrix-core probe runs and lands between a fraction of the published dense bf16 rate and
+    that rate (2.5 PFLOP/s)."""
+    for waves in (1, 2):
+        r = B.mfma_peak(waves)
+        assert 1000.0 < r < 2600.0, (waves, r)

@@ -1,0 +1,84 @@
+"""Static check of the generated gfx950 assembly of the 16-bit kernels.
+
+The dK/dV kernel issues its accumulating MFMAs (dK, dV in accumulation registers) from inline
+assembly, so the compiler's hazard recognizer does not see them.  gfx950 needs two wait states
+between a VALU write of a VGPR and an MFMA reading it as a source.  This test compiles the
+kernels to assembly with the library's flags and fails if any such MFMA reads a VGPR that one
+of the two preceding instructions wrote (an s_nop counts its wait states).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "variable_length_flashattention_fa_amd", "csrc")
+
+
+def _regs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _hazards(asm_text):
+    found = []
+    for m in re.finditer(r"^(_ZN2fa\w+):", asm_text, re.M):
+        start = m.end()
+        end = asm_text.index(".Lfunc_end", start)
+        ins = []
+        for line in asm_text[start:end].splitlines():
+            t = line.split(";")[0].strip()
+            if not t or t.startswith(".") or t.endswith(":"):
+                continue
+            ins.append(t)
+        for k, t in enumerate(ins):
+            if not t.startswith("v_mfma") or " a[" not in t.split(",")[0] + " ":
+                continue
+            ops = [x.strip() for x in t.split(None, 1)[1].split(",")]
+            srcs = _regs(ops[1]) | _regs(ops[2])
+            waits = 0
+            for back in range(k - 1, max(k - 6, -1), -1):
+                u = ins[back]
+                op = u.split()[0]
+                if op == "s_nop":
+                    waits += int(u.split()[1], 0) + 1
+                elif op.startswith("v_") and not op.startswith("v_mfma"):
+                    dst = _regs(u.split(None, 1)[1].split(",")[0].strip()) if " " in u else set()
+                    if dst & srcs:
+                        found.append((m.group(1), u, t))
+                    waits += 1
+                else:
+                    waits += 1
+                if waits >= 2:
+                    break
+    return found
+
+
+def test_checker_flags_a_planted_hazard():
+    text = ("\n_ZN2fa_probe:\n\tv_mov_b32_e32 v70, v1\n"
+            "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[70:73], v[8:11], a[0:15]\n"
+            "\tv_mov_b32_e32 v9, v1\n\ts_nop 1\n"
+            "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[70:73], v[8:11], a[0:15]\n.Lfunc_end0:\n")
+    assert len(_hazards(text)) == 1
+
+
+@pytest.mark.slow
+def test_no_valu_to_asm_mfma_hazard(tmp_path):
+    hipcc = os.environ.get("HIPCC") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc"))
+    if not hipcc:
+        pytest.skip("hipcc not available")
+    out = tmp_path / "bwd16.s"
+    cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+           "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form", "--cuda-device-only", "-S", "-o", str(out),
+           os.path.join(CSRC, "fa_bwd16.hip")]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout[-2000:]
+    text = out.read_text()
+    assert "v_mfma_f32_32x32x16_bf16 a[" in text  # the asm MFMAs are there
+    assert _hazards(text) == []

@@ -50,7 +50,7 @@ class FaError(RuntimeError):
 _lib = None
 
 EXPORTS = ("fa_varlen_bwd", "fa_last_error", "fa_release", "fa_varlen_worklist", "fa_profile_enable",
-           "fa_profile_read")
+           "fa_profile_read", "fa_mfma_peak")
 KERNEL_NAMES = ("preprocess", "bwd_main", "convert_dq", "bwd_dq")
 
 
@@ -81,6 +81,8 @@ def load(path: Optional[str] = None):
     lib.fa_profile_enable.restype = None
     lib.fa_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     lib.fa_profile_read.restype = ctypes.c_int
+    lib.fa_mfma_peak.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
+    lib.fa_mfma_peak.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -200,3 +202,12 @@ def profile_read() -> dict:
     if n < 0:
         raise FaError(-n, last_error())
     return {KERNEL_NAMES[i]: (ms[i], cnt[i]) for i in range(min(n, k))}
+
+
+def mfma_peak(waves_per_simd: int = 2) -> float:
+    """Measured bf16 MFMA rate of the current device in TFLOP/s (see fa_mfma_peak)."""
+    out = ctypes.c_double(0.0)
+    st = load().fa_mfma_peak(int(waves_per_simd), ctypes.byref(out))
+    if st != 0:
+        raise FaError(st, last_error())
+    return out.value
