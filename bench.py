@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_flashattention_fa_amd", "csrc", f)
-                  for f in ("fa_kernels.hip", "fa_bwd16.hip", "fa_kernels.h", "build.py")]
+                  for f in ("fa_kernels.hip", "fa_bwd16.hip", "fa_device.h", "fa_kernels.h", "build.py")]
 
 
 def log(msg):
@@ -178,6 +178,27 @@ def main(argv=None):
     ms_per_step = elapsed * 1e3 / args.steps
     call_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    # the varlen forward on the same inputs (Y and statistics into scratch tensors)
+    y_f = torch.empty_like(y)
+    smax_f, ssum_f = torch.empty_like(smax), torch.empty_like(ssum)
+
+    def fwd_step():
+        B.fa_varlen_fwd(q, k, v, inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt, wl.keep_prob, drop, wl.scale,
+                        wl.heads, y_f, smax_f, ssum_f, stream=stream)
+
+    for _ in range(args.warmup):
+        fwd_step()
+    torch.cuda.synchronize()
+    B.profile_read()
+    B.profile_enable(True)
+    t_f = time.perf_counter()
+    for _ in range(args.steps):
+        fwd_step()
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t_f) * 1e3 / args.steps
+    B.profile_enable(False)
+    fwd_prof = B.profile_read()
+    log(f"forward: {fwd_ms:.3f} ms/call")
     measured_peak = {w: B.mfma_peak(w) for w in (1, 2)}
     log(f"measured bf16 MFMA rate: {measured_peak[1]:.0f} TFLOP/s (1 wave/SIMD), {measured_peak[2]:.0f} (2 waves/SIMD)")
 
@@ -241,6 +262,13 @@ def main(argv=None):
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for(wl.name, dominant),
                      "kernel": dominant, "avg_ms": main_avg},
         "kernels": kernels,
+        "forward": {
+            "ms_per_call": fwd_ms,
+            "kernel_avg_ms": fwd_prof["fwd"][0] / max(fwd_prof["fwd"][1], 1),
+            "useful_TFLOP/s": 4.0 * wl.heads * wl.head_dim * pairs / (fwd_ms * 1e-3) / 1e12,
+            "pct_of_bf16_peak": 100.0 * 4.0 * wl.heads * wl.head_dim * pairs / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "note": "Y and statistics for the same inputs; useful work 4*N*D per admitted pair (two contractions)",
+        },
     }
 
     if not args.no_cpu_baseline:

@@ -175,18 +175,39 @@ int64_t fa_varlen_worklist(const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t*
 
 /*
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
- * fa_varlen_bwd call records a pair of HIP events around each of its kernels
- * on the call's stream: index 0 the row preprocess, 1 the main backward
- * kernel (dK/dV for bf16 / fp16; the whole backward for fp32), 2 the dQ
- * convert (fp32 only), 3 the dQ kernel (bf16 / fp16 only).
+ * fa_varlen_bwd / fa_varlen_fwd call records a pair of HIP events around each
+ * of its kernels on the call's stream: index 0 the row preprocess, 1 the main
+ * backward kernel (dK/dV for bf16 / fp16; the whole backward for fp32), 2 the
+ * dQ convert (fp32 only), 3 the dQ kernel (bf16 / fp16 only), 4 the forward.
  */
 void fa_profile_enable(int on);
 
 /* Waits for the recorded events, writes the summed milliseconds and launch
  * counts per kernel index into ms[] / launches[] (capacity entries each, may be
- * NULL) and clears the record.  Returns the number of kernel indices (4), or
+ * NULL) and clears the record.  Returns the number of kernel indices (5), or
  * -FA_ERR_RUNTIME if an event could not be read. */
 int fa_profile_read(double* ms, int64_t* launches, int capacity);
+
+/*
+ * Varlen forward: the operator whose outputs the backward consumes ("FlashAttention梯度V2"
+ * page, 功能说明 and 计算公式 sections: the forward definition the gradient formulas refer to).
+ *   S = scale * Q K^T with the mask of atten_mode / pre_tokens / next_tokens (as in
+ *   fa_varlen_bwd), P = softmax of S over the admitted keys of each row, Y = (P o Z / keep_prob) V.
+ * Arguments q, k, v, cu_seqlens_*, atten_mode, pre_tokens, next_tokens, keep_prob, drop_mask,
+ * scale, head_num and stream mean what they mean for fa_varlen_bwd.  Outputs (caller-owned
+ * device memory): y, a TND view with q's tokens and heads and v's head_dim, in q's dtype;
+ * softmax_max and softmax_sum, [N, Tq, 8] fp32 (16-byte aligned), each row holding the row's
+ * max of the admitted scaled scores and its sum of exp(S - max), repeated 8 times.  A row with
+ * no admitted key gets max -inf, sum 0 and a zero Y row.  The statistics are those of the
+ * softmax before dropout, which is what fa_varlen_bwd expects.
+ * Returns the status codes of fa_varlen_bwd.  FA_ERR_UNSUPPORTED also when dropout is on and
+ * a sequence has Lq * Lkv >= 2^34.  Asynchronous on stream; the same workspace rules apply.
+ */
+int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                  const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
+                  int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens, double keep_prob,
+                  const uint8_t* drop_mask, double scale, int64_t head_num, const fa_tensor_t* y,
+                  float* softmax_max, float* softmax_sum, void* stream);
 
 /* Measured matrix-core ceiling of the current device (a diagnostic, not part of the
  * operator): runs a kernel of independent bf16 32x32x16 MFMAs, one workgroup per compute

@@ -128,26 +128,48 @@ def forward_unit(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    lq, lkv = q.shape[0], k.shape[0]
+    lq = q.shape[0]
     y = np.zeros((lq, v.shape[1]), dtype=np.float64)
     m = np.full(lq, -np.inf, dtype=np.float64)
     l = np.zeros(lq, dtype=np.float64)
     for c0 in range(0, lq, _ROW_CHUNK):
         rows = np.arange(c0, min(lq, c0 + _ROW_CHUNK))
-        s = scale * (q[rows] @ k.T)
-        a = admit_mask(lq, lkv, mode, pre, nxt, rows)
-        has = a.any(axis=1)
-        sm = np.where(a, s, -np.inf)
-        mc = sm.max(axis=1, initial=-np.inf)
-        e = np.exp(np.where(a, s - np.where(has, mc, 0.0)[:, None], -np.inf))
-        lc = e.sum(axis=1)
-        ps = np.where(has[:, None], e / np.where(has, lc, 1.0)[:, None], 0.0)
-        if keep_prob < 1.0:
-            ps = ps * dropout_keep(drop_mask, bit0, rows, lkv) / keep_prob
-        y[rows] = ps @ v
-        m[rows] = mc
-        l[rows] = lc
+        y[rows], m[rows], l[rows] = _forward_rows(q[rows], k, v, lq, rows, scale, mode, pre, nxt,
+                                                  keep_prob, drop_mask, bit0)
     return y, m, l
+
+
+def _forward_rows(qr, k, v, lq: int, rows, scale, mode, pre, nxt, keep_prob, drop_mask, bit0):
+    """Y, m, l of the given query rows (sequence-relative), with qr their Q rows (fp64)."""
+    lkv = k.shape[0]
+    s = scale * (qr @ k.T)
+    a = admit_mask(lq, lkv, mode, pre, nxt, rows)
+    has = a.any(axis=1)
+    sm = np.where(a, s, -np.inf)
+    mc = sm.max(axis=1, initial=-np.inf)
+    e = np.exp(np.where(a, s - np.where(has, mc, 0.0)[:, None], -np.inf))
+    lc = e.sum(axis=1)
+    ps = np.where(has[:, None], e / np.where(has, lc, 1.0)[:, None], 0.0)
+    if keep_prob < 1.0:
+        ps = ps * dropout_keep(drop_mask, bit0, rows, lkv) / keep_prob
+    return ps @ v, mc, lc
+
+
+def forward_rows(q, k, v, cu_q, cu_kv, b: int, n: int, rows, *, mode: int = MASK_NONE, pre: int = 0,
+                 nxt: int = 0, keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int):
+    """Forward of selected query rows (sequence-relative) of one (b, n): Y [len(rows), D], m, l.
+
+    The same definition as forward_unit restricted to those rows (each row needs only its own
+    row of S).
+    """
+    q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+    k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
+    bit0 = int(dropout_bit_bases(cu_q, cu_kv, head_num)[b]) + n * (q1 - q0) * (k1 - k0)
+    rows = np.asarray(rows, dtype=np.int64)
+    qr = np.asarray(q[q0:q1, n], dtype=np.float64)[rows]
+    ks = np.asarray(k[k0:k1, n], dtype=np.float64)
+    vs = np.asarray(v[k0:k1, n], dtype=np.float64)
+    return _forward_rows(qr, ks, vs, q1 - q0, rows, scale, mode, pre, nxt, keep_prob, drop_mask, bit0)
 
 
 def forward(q, k, v, cu_q, cu_kv, *, mode: int = MASK_NONE, pre: int = 0, nxt: int = 0,

@@ -143,3 +143,58 @@ def test_mfma_peak_rejects_bad_arguments():
     assert lib.fa_mfma_peak(2, None) == 1  # FA_ERR_NULLPTR
     assert lib.fa_mfma_peak(3, ctypes.byref(out)) == 2  # FA_ERR_INVALID
     assert lib.fa_mfma_peak(0, ctypes.byref(out)) == 2
+
+
+# --- forward entry point ----------------------------------------------------------------------
+
+def _fwd(q=None, k=None, v=None, y=None, smax=FAKE, ssum=FAKE, cu_q=(0, 10), cu_kv=(0, 10), mode=0, pre=0,
+         nxt=0, kp=1.0, drop=None, scale=0.125, head_num=2):
+    tq, tk = cu_q[-1], cu_kv[-1]
+    q = q if q is not None else _t(tq)
+    k = k if k is not None else _t(tk)
+    v = v if v is not None else _t(tk)
+    y = y if y is not None else _t(tq)
+    aq = np.asarray(cu_q, dtype=np.int64)
+    ak = np.asarray(cu_kv, dtype=np.int64)
+    sq = B.FaSeqlens(aq.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), aq.size - 1)
+    sk = B.FaSeqlens(ak.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ak.size - 1)
+    lib = B.load()
+    ref = lambda x: None if x is None else ctypes.byref(x)  # noqa: E731
+    st = lib.fa_varlen_fwd(ref(q), ref(k), ref(v), ctypes.byref(sq), ctypes.byref(sk), mode, pre, nxt, kp,
+                           None if drop is None else ctypes.c_void_p(drop), scale, head_num, ref(y),
+                           None if smax is None else ctypes.c_void_p(smax),
+                           None if ssum is None else ctypes.c_void_p(ssum), None)
+    return st, lib.fa_last_error().decode()
+
+
+def test_forward_null_pointers():
+    lib = B.load()
+    assert lib.fa_varlen_fwd(None, None, None, None, None, 0, 0, 0, 1.0, None, 1.0, 1, None, None, None,
+                             None) == B.FA_ERR_NULLPTR
+    assert _fwd(y=_t(10, data=0))[0] == B.FA_ERR_NULLPTR
+    assert _fwd(smax=None)[0] == B.FA_ERR_NULLPTR
+    assert _fwd(kp=0.9, drop=None)[0] == B.FA_ERR_NULLPTR
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(kp=0.0), B.FA_ERR_INVALID),
+    (dict(kp=1.5), B.FA_ERR_INVALID),
+    (dict(mode=3), B.FA_ERR_INVALID),
+    (dict(scale=float("inf")), B.FA_ERR_INVALID),
+    (dict(head_num=3), B.FA_ERR_INVALID),
+    (dict(y=_t(10, dtype=B.FA_F16)), B.FA_ERR_INVALID),
+    (dict(y=_t(11)), B.FA_ERR_INVALID),
+    (dict(cu_q=(0, 4, 10), cu_kv=(0, 10)), B.FA_ERR_INVALID),
+    (dict(cu_q=(0, 12, 10), cu_kv=(0, 5, 10)), B.FA_ERR_INVALID),
+    (dict(k=_t(10, heads=1), v=_t(10, heads=1)), B.FA_ERR_UNSUPPORTED),
+    (dict(q=_t(10, dim=96), k=_t(10, dim=96), v=_t(10, dim=96), y=_t(10, dim=96)), B.FA_ERR_UNSUPPORTED),
+    (dict(smax=FAKE + 4), B.FA_ERR_UNSUPPORTED),
+])
+def test_forward_invalid_arguments(kwargs, status):
+    st, msg = _fwd(**kwargs)
+    assert st == status, msg
+    assert msg
+
+
+def test_forward_empty_input_is_ok():
+    assert _fwd(q=_t(0), y=_t(0), cu_q=(0, 0), cu_kv=(0, 10), smax=None, ssum=None)[0] == B.FA_OK

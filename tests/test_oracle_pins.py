@@ -343,6 +343,11 @@ def test_sampled_outputs_equal_full(mode, pre, nxt):
             gk, gv = O.backward_dkdv_cols(q, k, v, dy, y, m, l, cu_q, cu_kv, b, n, cols, **kw)
             np.testing.assert_allclose(gk, dk[cu_kv[b] + cols, n], rtol=0, atol=1e-13)
             np.testing.assert_allclose(gv, dv[cu_kv[b] + cols, n], rtol=0, atol=1e-13)
+            yr, mr, lr = O.forward_rows(q, k, v, cu_q, cu_kv, b, n, rows, **kw)
+            yf, mf, lf = O.forward(q, k, v, cu_q, cu_kv, **kw)
+            np.testing.assert_array_equal(yr, yf[cu_q[b] + rows, n])
+            np.testing.assert_array_equal(mr, mf[n, cu_q[b] + rows])
+            np.testing.assert_array_equal(lr, lf[n, cu_q[b] + rows])
 
 
 # --- the dropout bit layout agrees with the independent generator ---------------------------

@@ -49,9 +49,9 @@ class FaError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ("fa_varlen_bwd", "fa_last_error", "fa_release", "fa_varlen_worklist", "fa_profile_enable",
-           "fa_profile_read", "fa_mfma_peak")
-KERNEL_NAMES = ("preprocess", "bwd_main", "convert_dq", "bwd_dq")
+EXPORTS = ("fa_varlen_bwd", "fa_varlen_fwd", "fa_last_error", "fa_release", "fa_varlen_worklist",
+           "fa_profile_enable", "fa_profile_read", "fa_mfma_peak")
+KERNEL_NAMES = ("preprocess", "bwd_main", "convert_dq", "bwd_dq", "fwd")
 
 
 def load(path: Optional[str] = None):
@@ -69,6 +69,10 @@ def load(path: Optional[str] = None):
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p,
                                   ctypes.c_double, ctypes.c_int64, T, T, T, ctypes.c_void_p]
     lib.fa_varlen_bwd.restype = ctypes.c_int
+    lib.fa_varlen_fwd.argtypes = [T, T, T, S, S, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                  ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, T, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_varlen_fwd.restype = ctypes.c_int
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_release.argtypes = []
@@ -169,6 +173,55 @@ def varlen_bwd(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlen
     fa_varlen_bwd(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
                   pre_tokens, next_tokens, keep_prob, drop_mask, scale, head_num, dq, dk, dv)
     return dq, dk, dv
+
+
+def fa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q, cu_seqlens_kv,
+                  atten_mode: int, pre_tokens: int, next_tokens: int, keep_prob: float,
+                  drop_mask: Optional[torch.Tensor], scale: float, head_num: int, y: torch.Tensor,
+                  softmax_max: torch.Tensor, softmax_sum: torch.Tensor, stream=None) -> None:
+    """Same arguments as the C entry point; tensors are device tensors, cu_seqlens host sequences.
+
+    Enqueues the forward on `stream` (default: torch's current stream) and raises FaError on a
+    non-OK status.
+    """
+    lib = load()
+    tq, tk, tv, ty = (tensor_desc(x) for x in (q, k, v, y))
+    sq, aq = _seqlens(cu_seqlens_q)
+    sk, ak = _seqlens(cu_seqlens_kv)
+    for st in (softmax_max, softmax_sum):
+        if st is not None and not st.is_contiguous():
+            raise ValueError("softmax statistics must be contiguous [N, T, 8] fp32")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+
+    def ref(x):
+        return None if x is None else ctypes.byref(x)
+
+    status = lib.fa_varlen_fwd(ref(tq), ref(tk), ref(tv), ctypes.byref(sq), ctypes.byref(sk), int(atten_mode),
+                               int(pre_tokens), int(next_tokens), float(keep_prob), _ptr(drop_mask), float(scale),
+                               int(head_num), ref(ty), _ptr(softmax_max), _ptr(softmax_sum),
+                               ctypes.c_void_p(int(stream)))
+    del aq, ak
+    if status != FA_OK:
+        raise FaError(status, last_error())
+
+
+def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, atten_mode: int = FA_MASK_NONE, pre_tokens: int = 0,
+               next_tokens: int = 0, keep_prob: float = 1.0, drop_mask=None, scale: Optional[float] = None,
+               head_num=None):
+    """Convenience wrapper: allocates y like q and the [N, T, 8] statistics; returns (y, max, sum)."""
+    if scale is None:
+        scale = 1.0 / float(q.shape[2]) ** 0.5
+    if head_num is None:
+        head_num = q.shape[1]
+    y = torch.empty(q.shape[0], q.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
+    smax = torch.empty(q.shape[1], q.shape[0], 8, dtype=torch.float32, device=q.device)
+    ssum = torch.empty_like(smax)
+    fa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, atten_mode, pre_tokens, next_tokens, keep_prob, drop_mask,
+                  scale, head_num, y, smax, ssum)
+    return y, smax, ssum
 
 
 def worklist(cu_seqlens_q, cu_seqlens_kv, atten_mode: int, pre_tokens: int, next_tokens: int, heads: int,

@@ -18,10 +18,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libfa_varlen.so"
 
-HIP_SOURCES = ["fa_kernels.hip", "fa_bwd16.hip", "fa_probe.hip", "fa_api.cpp"]
+HIP_SOURCES = ["fa_kernels.hip", "fa_bwd16.hip", "fa_fwd.hip", "fa_probe.hip", "fa_api.cpp"]
 # The 16-bit kernels feed MFMA results straight into VALU work (exp, dS): keep MFMA
 # destinations in VGPRs instead of accumulation registers that would need copying back.
-PER_SOURCE_FLAGS = {"fa_bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+PER_SOURCE_FLAGS = {"fa_bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_SOURCES = ["fa_worklist.cpp"]
 
 

@@ -76,13 +76,18 @@ struct Workspace {
     std::vector<int64_t> key;
     int64_t n_items = 0;
     int64_t n_q_items = 0;
+    // the forward's query-block list, cached the same way
+    fa_work_item_t* fwd_items = nullptr;
+    size_t fwd_items_cap = 0;
+    std::vector<int64_t> fwd_key;
+    int64_t n_fwd_items = 0;
 };
 
 std::mutex g_mutex;
 std::unordered_map<int, Workspace> g_ws;
 
 // ---- optional per-kernel event timing ----
-constexpr int kKernels = 4;  // 0 preprocess, 1 main / dK-dV, 2 convert, 3 dQ
+constexpr int kKernels = 5;  // 0 preprocess, 1 main / dK-dV, 2 convert, 3 dQ, 4 forward
 struct EventPair {
     int kernel;
     hipEvent_t start;
@@ -151,6 +156,7 @@ extern "C" void fa_release(void) {
         if (kv.second.dq_acc) (void)hipFree(kv.second.dq_acc);
         if (kv.second.rowstat) (void)hipFree(kv.second.rowstat);
         if (kv.second.items) (void)hipFree(kv.second.items);
+        if (kv.second.fwd_items) (void)hipFree(kv.second.fwd_items);
     }
     g_ws.clear();
     (void)hipSetDevice(cur);
@@ -163,8 +169,8 @@ extern "C" void fa_profile_enable(int on) {
 
 extern "C" int fa_profile_read(double* ms, int64_t* launches, int capacity) {
     std::lock_guard<std::mutex> lock(g_mutex);
-    double sum[kKernels] = {0, 0, 0, 0};
-    int64_t cnt[kKernels] = {0, 0, 0, 0};
+    double sum[kKernels] = {0, 0, 0, 0, 0};
+    int64_t cnt[kKernels] = {0, 0, 0, 0, 0};
     int status = kKernels;
     for (auto& ev : g_events) {
         float t = 0.f;
@@ -479,5 +485,216 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
                                   static_cast<float>(scale), s);
     });
     if (e != hipSuccess) return runtime_error("convert launch", e);
+    return FA_OK;
+}
+
+// Forward: validation as in the backward (same page constraints, same codes), then one kernel
+// over query-block items.
+extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                             const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
+                             int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens, double keep_prob,
+                             const uint8_t* drop_mask, double scale, int64_t head_num, const fa_tensor_t* y,
+                             float* softmax_max, float* softmax_sum, void* stream) {
+    fa::clear_error();
+    const fa_tensor_t* all[4] = {q, k, v, y};
+    const char* names[4] = {"q", "k", "v", "y"};
+    for (int i = 0; i < 4; ++i) {
+        if (all[i] == nullptr || (all[i]->data == nullptr && all[i]->tokens != 0)) {
+            set_error(std::string(names[i]) + " is null");
+            return FA_ERR_NULLPTR;
+        }
+    }
+    if ((softmax_max == nullptr || softmax_sum == nullptr) && q->tokens != 0) {
+        set_error("softmax_max / softmax_sum is null");
+        return FA_ERR_NULLPTR;
+    }
+    if (cu_seqlens_q == nullptr || cu_seqlens_q->cu == nullptr || cu_seqlens_kv == nullptr ||
+        cu_seqlens_kv->cu == nullptr) {
+        set_error("cu_seqlens_q / cu_seqlens_kv is null");
+        return FA_ERR_NULLPTR;
+    }
+    if (!(keep_prob > 0.0 && keep_prob <= 1.0)) {
+        set_error("keep_prob must be in (0, 1]");
+        return FA_ERR_INVALID;
+    }
+    if (keep_prob < 1.0 && drop_mask == nullptr) {
+        set_error("drop_mask is null while keep_prob < 1");
+        return FA_ERR_NULLPTR;
+    }
+    for (int i = 0; i < 4; ++i) {
+        int st = check_tensor(all[i], names[i]);
+        if (st != FA_OK) return st;
+    }
+    for (int i = 1; i < 4; ++i) {
+        if (all[i]->dtype != q->dtype) {
+            set_error(std::string(names[i]) + ": dtype differs from q (all tensors share one dtype)");
+            return FA_ERR_INVALID;
+        }
+    }
+    if (head_num != q->heads) {
+        set_error("head_num must equal the N axis of q");
+        return FA_ERR_INVALID;
+    }
+    if (k->heads != v->heads || k->tokens != v->tokens) {
+        set_error("k and v must have equal shapes apart from D");
+        return FA_ERR_INVALID;
+    }
+    if (q->heads % k->heads != 0) {
+        set_error("q heads must be a multiple of k/v heads");
+        return FA_ERR_INVALID;
+    }
+    if (q->head_dim != k->head_dim || k->head_dim < v->head_dim) {
+        set_error("head dims must satisfy qD == kD >= vD");
+        return FA_ERR_INVALID;
+    }
+    if (y->tokens != q->tokens || y->heads != q->heads || y->head_dim != v->head_dim) {
+        set_error("y must have q's tokens and heads and v's head_dim");
+        return FA_ERR_INVALID;
+    }
+    if (atten_mode < FA_MASK_NONE || atten_mode > FA_MASK_BAND) {
+        set_error("atten_mode must be 0 (none), 1 (causal) or 2 (band)");
+        return FA_ERR_INVALID;
+    }
+    if (!std::isfinite(scale)) {
+        set_error("scale must be finite");
+        return FA_ERR_INVALID;
+    }
+    int st = fa::check_seqlens(cu_seqlens_q, "cu_seqlens_q");
+    if (st != FA_OK) return st;
+    st = fa::check_seqlens(cu_seqlens_kv, "cu_seqlens_kv");
+    if (st != FA_OK) return st;
+    if (cu_seqlens_q->batch != cu_seqlens_kv->batch) {
+        set_error("cu_seqlens_q and cu_seqlens_kv must have equal batch counts");
+        return FA_ERR_INVALID;
+    }
+    const int64_t batch = cu_seqlens_q->batch;
+    if (cu_seqlens_q->cu[batch] != q->tokens || cu_seqlens_kv->cu[batch] != k->tokens) {
+        set_error("cu_seqlens must end at the token counts of q and k");
+        return FA_ERR_INVALID;
+    }
+    if (q->heads != k->heads) {
+        set_error("grouped heads (k/v heads < q heads) are not supported");
+        return FA_ERR_UNSUPPORTED;
+    }
+    if (v->head_dim != k->head_dim) {
+        set_error("v head_dim < k head_dim is not supported");
+        return FA_ERR_UNSUPPORTED;
+    }
+    if (q->head_dim != 64 && q->head_dim != 128) {
+        set_error("head_dim must be 64 or 128");
+        return FA_ERR_UNSUPPORTED;
+    }
+    for (int i = 0; i < 4; ++i) {
+        if (!aligned16(all[i])) {
+            set_error(std::string(names[i]) + ": data and strides must be 16-byte aligned");
+            return FA_ERR_UNSUPPORTED;
+        }
+    }
+    if (reinterpret_cast<uintptr_t>(softmax_max) % 16 != 0 || reinterpret_cast<uintptr_t>(softmax_sum) % 16 != 0) {
+        set_error("softmax_max / softmax_sum must be 16-byte aligned");
+        return FA_ERR_UNSUPPORTED;
+    }
+    int64_t drop_bits = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t lq = cu_seqlens_q->cu[b + 1] - cu_seqlens_q->cu[b];
+        const int64_t lk = cu_seqlens_kv->cu[b + 1] - cu_seqlens_kv->cu[b];
+        // the 16-bit kernel addresses one (sequence, head) region of the bit stream with 32-bit
+        // byte offsets
+        if (keep_prob < 1.0 && lq * lk >= (int64_t(1) << 34)) {
+            set_error("dropout: a sequence's Lq * Lkv must stay below 2^34");
+            return FA_ERR_UNSUPPORTED;
+        }
+        drop_bits += q->heads * lq * lk;
+    }
+
+    const int64_t tq = q->tokens;
+    const int64_t heads = q->heads;
+    const int d = static_cast<int>(q->head_dim);
+    if (tq == 0) return FA_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t dtype = q->dtype;
+    const bool wide = dtype == FA_F32;
+    const int64_t pre = atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0;
+    const int64_t nxt = atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0;
+
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return runtime_error("hipGetDevice", e);
+    Workspace& ws = g_ws[dev];
+
+    std::vector<int64_t> key;
+    key.reserve(2 * (batch + 1) + 5);
+    key.push_back(atten_mode);
+    key.push_back(pre);
+    key.push_back(nxt);
+    key.push_back(heads);
+    key.push_back(wide ? 1 : 0);
+    key.insert(key.end(), cu_seqlens_q->cu, cu_seqlens_q->cu + batch + 1);
+    key.insert(key.end(), cu_seqlens_kv->cu, cu_seqlens_kv->cu + batch + 1);
+    if (key != ws.fwd_key) {
+        std::vector<fa_work_item_t> list;
+        fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
+                           FA_ITEMS_QUERY_BLOCKS, wide ? fa::FA32_FWD_BLOCK : fa::FA16_DQ_BLOCK,
+                           wide ? fa::FA32_FWD_BLOCK : fa::FA16_DQ_TILE_K, list);
+        const int64_t n = static_cast<int64_t>(list.size());
+        size_t cap_bytes = ws.fwd_items_cap * sizeof(fa_work_item_t);
+        void* ptr = ws.fwd_items;
+        int g = grow(&ptr, &cap_bytes, static_cast<size_t>(n) * sizeof(fa_work_item_t), "forward work list");
+        ws.fwd_items = static_cast<fa_work_item_t*>(ptr);
+        ws.fwd_items_cap = cap_bytes / sizeof(fa_work_item_t);
+        if (g != FA_OK) {
+            ws.fwd_key.clear();
+            return g;
+        }
+        if (n > 0) {
+            e = hipStreamSynchronize(s);
+            if (e != hipSuccess) {
+                ws.fwd_key.clear();
+                return runtime_error("stream synchronize", e);
+            }
+            e = hipMemcpy(ws.fwd_items, list.data(), static_cast<size_t>(n) * sizeof(fa_work_item_t),
+                          hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                ws.fwd_key.clear();
+                return runtime_error("forward work list upload", e);
+            }
+        }
+        ws.fwd_key = key;
+        ws.n_fwd_items = n;
+    }
+
+    fa::FwdArgs a;
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.q_st = q->stride_t;
+    a.q_sh = q->stride_h;
+    a.k_st = k->stride_t;
+    a.k_sh = k->stride_h;
+    a.v_st = v->stride_t;
+    a.v_sh = v->stride_h;
+    a.y = y->data;
+    a.y_st = y->stride_t;
+    a.y_sh = y->stride_h;
+    a.smax = softmax_max;
+    a.ssum = softmax_sum;
+    a.items = ws.fwd_items;
+    a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
+    a.drop_bytes = keep_prob < 1.0 ? (drop_bits + 7) / 8 : 0;
+    a.tq = static_cast<int32_t>(tq);
+    a.heads = static_cast<int32_t>(heads);
+    a.mode = atten_mode;
+    a.pre = static_cast<int32_t>(pre);
+    a.nxt = static_cast<int32_t>(nxt);
+    a.scale = static_cast<float>(scale);
+    a.exp_scale = static_cast<float>(scale * 1.4426950408889634);
+    a.inv_keep = static_cast<float>(1.0 / keep_prob);
+    e = timed(4, s, [&] {
+        return wide ? fa::launch_fwd32(d, keep_prob < 1.0, a, ws.n_fwd_items, s)
+                    : fa::launch_fwd16(dtype, d, keep_prob < 1.0, a, ws.n_fwd_items, s);
+    });
+    if (e != hipSuccess) return runtime_error("forward kernel launch", e);
     return FA_OK;
 }

@@ -1,0 +1,375 @@
+// Varlen attention forward for gfx950: the operator the backward's inputs come from.
+//
+// Formulas section of the "FlashAttention梯度V2" page (forward part): S = scale Q K^T with the
+// mask applied, P = Softmax(S), Y = Dropout(P, keepProb) V.  The row statistics softmaxMax
+// (max of the admitted scaled scores) and softmaxSum (sum of exp(S - max) over admitted keys)
+// are written as [N, T, 8] fp32 with the value repeated over the last axis; a row with no
+// admitted key gets max -inf, sum 0 and Y = 0.  Dropout keeps a pair when its mask bit is 1 and
+// scales it by 1 / keepProb; the statistics are those of the softmax before dropout.
+#include <cmath>
+
+#include "fa_device.h"
+
+namespace fa {
+
+// ------------------------------------------------------------------------------------------------
+// bf16 / fp16.  Workgroup: 8 waves (two per SIMD), FA16_DQ_BLOCK = 256 queries; wave w owns
+// queries 32w .. 32w+31 and keeps their Q rows (B operands, in accumulation registers), the
+// online-softmax state and an O^T accumulator.  Key tiles of FA16_DQ_TILE_K = 64 rows are
+// walked as two 32-key steps:
+//   S^T = K Q^T                            (A = K rows from LDS)
+//   P^T = exp2(S^T scale log2e - mref)     (each lane holds one query, so its running max and
+//                                           sum are scalars; the two lane halves hold 16 keys
+//                                           each and combine their max every step)
+//   O^T += V^T (P^T o Z / kp)              (A = transposing reads of V, B = P^T from registers)
+// O^T is rescaled only when a query's max grows past its reference mref by more than 8 (in
+// log2 units: P stays below 256), decided per wave, so most steps skip the rescale.
+
+template <typename T, int D, bool DROP>
+__global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
+    using vec = typename Op16<T>::vec;
+    constexpr int NW = 8;
+    constexpr int BQ = FA16_DQ_BLOCK;
+    constexpr int BK = FA16_DQ_TILE_K;
+    constexpr int ND = D / 32;
+    constexpr int NS = D / 16;
+    constexpr int TI = BK * D / 8 / 64;
+    constexpr int TW = TI / NW;
+    static_assert(BQ == 32 * NW && BK == 64 && TI % NW == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
+    __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
+
+    const fa_work_item_t it = p.items[blockIdx.x];
+    const int n = blockIdx.y;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 31;
+    const int h = lane >> 5;
+    const int L = it.len_q;
+    const int K = it.len_kv;
+    const int off = K - L;
+    const int i0 = it.block * BQ + 32 * w;
+    const int qi = i0 + col;
+
+    LdsOffsets<D> lo_;
+    lo_.init(lane);
+
+    const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + n * p.k_sh;
+    const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + n * p.v_sh;
+    int koff[TW];
+    int voff[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+        koff[u] = dma_offset<D>(w * TW + u, lane, p.k_st) - 1024 * u;
+        voff[u] = dma_offset<D>(w * TW + u, lane, p.v_st) - 1024 * u;
+    }
+    auto issue = [&](int kt, int b) {
+        const int k0 = kt * BK;
+        const i32x4 rk = buffer_desc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st));
+        const i32x4 rv = buffer_desc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st));
+        const uint32_t mk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TW * 512)));
+        const uint32_t mv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TW * 512)));
+        dma_pair<TW>(__builtin_amdgcn_readfirstlane(mk), rk, koff, __builtin_amdgcn_readfirstlane(mv), rv, voff);
+    };
+
+    // this lane's Q row
+    vec qreg[NS];
+    {
+        const bool ok = qi < L;
+        const int64_t row = it.q_start + (ok ? qi : 0);
+        const vec* qr = reinterpret_cast<const vec*>(static_cast<const T*>(p.q) + row * p.q_st + n * p.q_sh);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            qreg[s] = ok ? qr[2 * s + h] : vec{};
+            asm volatile("" : "+a"(qreg[s]));
+        }
+    }
+    // keys this lane's query admits, [klo, khi]: element a of a step at key k0s (key
+    // k0s + 4h + cc(a), cc(a) = 8*(a/4) + a%4) is admitted iff
+    // (unsigned)(cc(a) - (kbase - k0s)) <= krng
+    int kbase;
+    int krng;
+    {
+        int klo = 0;
+        int khi = K - 1;
+        if (p.mode == FA_MASK_CAUSAL) {
+            khi = min(khi, qi + off);
+        } else if (p.mode == FA_MASK_BAND) {
+            klo = max(klo, qi + off - p.pre);
+            khi = min(khi, qi + off + p.nxt);
+        }
+        if (qi < L && klo <= khi) {
+            kbase = klo - 4 * h;
+            krng = khi - klo;
+        } else {
+            kbase = -(1 << 30);
+            krng = 0;
+        }
+    }
+    const bool wave_rows_full = i0 + 31 < L;
+    int wlo = 0;
+    int whi = K - 1;
+    if (p.mode == FA_MASK_CAUSAL) {
+        whi = min(whi, i0 + off);
+    } else if (p.mode == FA_MASK_BAND) {
+        wlo = max(wlo, i0 + 31 + off - p.pre);
+        whi = min(whi, i0 + off + p.nxt);
+    }
+
+    // dropout: the (sequence, head) region of the bit stream starts at bit rb; the bits of this
+    // lane's query row start rbit bits past the region's first byte
+    __amdgpu_buffer_rsrc_t drs;
+    int64_t rbit = 0;
+    if constexpr (DROP) {
+        const int64_t rb = it.drop_base + static_cast<int64_t>(n) * L * K;
+        const int64_t byte0 = rb >> 3;
+        const int64_t left = p.drop_bytes - byte0;
+        drs = raw_rsrc(p.drop_mask + byte0,
+                       left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left)));
+        rbit = (rb & 7) + static_cast<int64_t>(qi < L ? qi : 0) * K;
+    }
+
+    f32x16 accO[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) accO[i] = zero16();
+    float mtrue = -INFINITY;  // running max of the admitted scaled scores of this query (log2 units)
+    float mref = -INFINITY;   // the max the P values and O^T are relative to
+    float lsum = 0.f;         // sum of P over this lane's keys (relative to mref)
+
+    auto kstep = [&](const T* cK, const T* cV, int k0s) {
+        f32x16 accS = zero16();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const vec ak = lds_row<vec>(cK, lo_.row[s]);
+            accS = Op16<T>::mfma(ak, qreg[s], accS);
+        }
+        const bool full = wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
+        float x[16];
+        auto scores = [&](auto masked_tag) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
+            const int lo_h = kbase - k0s;
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                x[a] = accS[a] * p.exp_scale;
+                if constexpr (MASKED) {
+                    const int cc = 8 * (a >> 2) + (a & 3);
+                    const bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(krng);
+                    x[a] = adm ? x[a] : -INFINITY;
+                }
+            }
+        };
+        if (full) {
+            scores(Tag<false>{});
+        } else {
+            scores(Tag<true>{});
+        }
+        float mloc = x[0];
+#pragma unroll
+        for (int a = 1; a < 16; ++a) mloc = fmaxf(mloc, x[a]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        mtrue = fmaxf(mtrue, mloc);
+        // rescale when the max outgrew the reference (never when it is still -inf)
+        const bool need = mtrue > mref + 8.f;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float alpha = need ? (mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - mtrue)) : 1.f;
+#pragma unroll
+            for (int nd = 0; nd < ND; ++nd) {
+#pragma unroll
+                for (int a = 0; a < 16; ++a) accO[nd][a] *= alpha;
+            }
+            lsum *= alpha;
+            mref = need ? mtrue : mref;
+        }
+        // mref is -inf only while every score so far was masked; those give P = 0
+        const float mb = mref == -INFINITY ? 0.f : mref;
+        uint32_t win = 0;
+        if constexpr (DROP) {
+            // bits of keys k0s .. k0s + 31 of this query: the five bytes that hold them, read one
+            // by one (a read that straddles the end of the mask would return zeros for the whole
+            // word, while bytes past the end read as zero individually)
+            const int64_t b0 = rbit + k0s;
+            const uint32_t byte = static_cast<uint32_t>(b0 >> 3);
+            uint32_t lo = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lo |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(drs, byte + i, 0, 0)) << (8 * i);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b8(drs, byte + 4, 0, 0);
+            win = __builtin_amdgcn_alignbit(hi, lo, static_cast<uint32_t>(b0 & 7));
+        }
+        uint32_t pw[2][4];
+#pragma unroll
+        for (int a = 0; a < 16; a += 2) {
+            float pd[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(x[a + e] - mb);
+                lsum += pv;
+                if constexpr (DROP) {
+                    const int cc = 8 * ((a + e) >> 2) + ((a + e) & 3);
+                    const bool keep = __builtin_amdgcn_ubfe(win, cc + 4 * h, 1) != 0;
+                    pd[e] = keep ? pv * p.inv_keep : 0.f;
+                } else {
+                    pd[e] = pv;
+                }
+            }
+            pw[a >> 3][(a & 7) >> 1] = pack2<T>(pd[0], pd[1]);
+        }
+        // O^T[d][q] += sum_key V[key][d] Pd^T[key][q]
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const vec bp = __builtin_bit_cast(vec, make_uint4(pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]));
+#pragma unroll
+            for (int nd = 0; nd < ND; ++nd) {
+                const vec av = lds_tr<vec>(cV + 16 * kk * D, lo_.tr[nd][0], lo_.tr[nd][1]);
+                accO[nd] = Op16<T>::mfma(av, bp, accO[nd]);
+            }
+        }
+    };
+
+    if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
+    int b = 0;
+    for (int kt = it.tile_begin; kt < it.tile_end; ++kt) {
+        wait_dma();
+        __syncthreads();
+        if (kt + 1 < it.tile_end) issue(kt + 1, b ^ 1);
+        kstep(sK[b], sV[b], kt * BK);
+        kstep(sK[b] + 32 * D, sV[b] + 32 * D, kt * BK + 32);
+        b ^= 1;
+    }
+
+    // epilogue: the two lane halves' sums; Y = O / l; statistics in natural units
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (qi < L) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        T* dst = static_cast<T*>(p.y) + static_cast<int64_t>(it.q_start + qi) * p.y_st + n * p.y_sh;
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t w0 = pack2<T>(accO[nd][4 * g] * inv, accO[nd][4 * g + 1] * inv);
+                const uint32_t w1 = pack2<T>(accO[nd][4 * g + 2] * inv, accO[nd][4 * g + 3] * inv);
+                *reinterpret_cast<uint2*>(dst + nd * 32 + 8 * g + 4 * h) = make_uint2(w0, w1);
+            }
+        }
+        const bool empty = mtrue == -INFINITY;
+        const float mnat = empty ? -INFINITY : mtrue * 0.69314718055994531f;
+        const float lnat = empty ? 0.f : ltot * __builtin_amdgcn_exp2f(mref - mtrue);
+        const float val = h == 0 ? mnat : lnat;
+        float* srow = (h == 0 ? p.smax : p.ssum) + (static_cast<int64_t>(n) * p.tq + it.q_start + qi) * 8;
+        const float4 v4 = make_float4(val, val, val, val);
+        reinterpret_cast<float4*>(srow)[0] = v4;
+        reinterpret_cast<float4*>(srow)[1] = v4;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// fp32: one thread per (query, head) with an online softmax over its admitted keys, the O row in
+// registers.  Made for small problems.
+
+template <int D, bool DROP>
+__global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) {
+    const fa_work_item_t it = p.items[blockIdx.x];
+    const int n = blockIdx.y;
+    const int L = it.len_q;
+    const int K = it.len_kv;
+    const int qi = it.block * FA32_FWD_BLOCK + static_cast<int>(threadIdx.x);
+    if (qi >= L) return;
+    const int off = K - L;
+    int klo = 0;
+    int khi = K - 1;
+    if (p.mode == FA_MASK_CAUSAL) {
+        khi = min(khi, qi + off);
+    } else if (p.mode == FA_MASK_BAND) {
+        klo = max(klo, qi + off - p.pre);
+        khi = min(khi, qi + off + p.nxt);
+    }
+    const float* q = static_cast<const float*>(p.q) + static_cast<int64_t>(it.q_start + qi) * p.q_st + n * p.q_sh;
+    const float* kb = static_cast<const float*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + n * p.k_sh;
+    const float* vb = static_cast<const float*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + n * p.v_sh;
+    float qr[D];
+    float o[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qr[d] = q[d];
+        o[d] = 0.f;
+    }
+    const int64_t bit0 = it.drop_base + (static_cast<int64_t>(n) * L + qi) * K;
+    float m = -INFINITY;
+    float l = 0.f;
+    for (int j = klo; j <= khi; ++j) {
+        const float* kr = kb + static_cast<int64_t>(j) * p.k_st;
+        float s = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) s = fmaf(qr[d], kr[d], s);
+        s *= p.scale;
+        if (s > m) {
+            const float alpha = m == -INFINITY ? 0.f : expf(m - s);
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < D; ++d) o[d] *= alpha;
+            m = s;
+        }
+        const float pj = expf(s - m);
+        l += pj;
+        float z = 1.f;
+        if constexpr (DROP) {
+            const int64_t bit = bit0 + j;
+            z = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
+        }
+        const float c = pj * z;
+        const float* vr = vb + static_cast<int64_t>(j) * p.v_st;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] = fmaf(c, vr[d], o[d]);
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* y = static_cast<float*>(p.y) + static_cast<int64_t>(it.q_start + qi) * p.y_st + n * p.y_sh;
+#pragma unroll
+    for (int d = 0; d < D; ++d) y[d] = o[d] * inv;
+    const int64_t srow = (static_cast<int64_t>(n) * p.tq + it.q_start + qi) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p.smax[srow + e] = m;
+        p.ssum[srow + e] = l;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+
+template <typename T, int D, bool DROP>
+static hipError_t launch_fwd16_t(const FwdArgs& a, int64_t n, hipStream_t stream) {
+    fwd16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd16(int32_t dtype, int head_dim, bool dropout, const FwdArgs& a, int64_t n_items,
+                        hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    if (dtype == FA_BF16) {
+        if (head_dim == 128)
+            return dropout ? launch_fwd16_t<__bf16, 128, true>(a, n_items, stream)
+                           : launch_fwd16_t<__bf16, 128, false>(a, n_items, stream);
+        return dropout ? launch_fwd16_t<__bf16, 64, true>(a, n_items, stream)
+                       : launch_fwd16_t<__bf16, 64, false>(a, n_items, stream);
+    }
+    if (head_dim == 128)
+        return dropout ? launch_fwd16_t<_Float16, 128, true>(a, n_items, stream)
+                       : launch_fwd16_t<_Float16, 128, false>(a, n_items, stream);
+    return dropout ? launch_fwd16_t<_Float16, 64, true>(a, n_items, stream)
+                   : launch_fwd16_t<_Float16, 64, false>(a, n_items, stream);
+}
+
+hipError_t launch_fwd32(int head_dim, bool dropout, const FwdArgs& a, int64_t n_items, hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(n_items), static_cast<unsigned>(a.heads));
+    if (head_dim == 128) {
+        if (dropout) fwd32_kernel<128, true><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
+        else fwd32_kernel<128, false><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
+    } else {
+        if (dropout) fwd32_kernel<64, true><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
+        else fwd32_kernel<64, false><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fa

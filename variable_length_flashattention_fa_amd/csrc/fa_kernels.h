@@ -83,4 +83,30 @@ hipError_t launch_dkdv16(int32_t dtype, int head_dim, bool dropout, const Bwd16A
 hipError_t launch_dq16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
                        hipStream_t stream);
 
+// ---- forward ----------------------------------------------------------------------------------
+// Y = Dropout(Softmax(Mask(scale Q K^T))) V and the row statistics, over query-block items.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;
+    void* y;
+    int64_t y_st, y_sh;
+    float* smax;  // [N, Tq, 8]
+    float* ssum;  // [N, Tq, 8]
+    const fa_work_item_t* items;  // query-block items
+    const uint8_t* drop_mask;
+    int64_t drop_bytes;  // size of the dropout mask in bytes (bounds its reads)
+    int32_t tq, heads, mode, pre, nxt;
+    float scale, exp_scale, inv_keep;
+};
+
+constexpr int FA32_FWD_BLOCK = 64;  // queries per fp32 forward workgroup (one per thread)
+
+// bf16 / fp16 forward over n_items query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles).
+hipError_t launch_fwd16(int32_t dtype, int head_dim, bool dropout, const FwdArgs& a, int64_t n_items,
+                        hipStream_t stream);
+// fp32 forward over n_items query-block items (FA32_FWD_BLOCK queries).
+hipError_t launch_fwd32(int head_dim, bool dropout, const FwdArgs& a, int64_t n_items, hipStream_t stream);
+
 }  // namespace fa
