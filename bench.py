@@ -34,7 +34,10 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_flashattention_fa_amd", "csrc", f)
-                  for f in ("fa_kernels.hip", "fa_bwd16.hip", "fa_device.h", "fa_kernels.h", "build.py")]
+                  for f in ("fa_kernels.hip", "fa_bwd16.hip", "fa_fwd.hip", "fa_device.h", "fa_kernels.h", "build.py")]
+# kernel name fragment in a counter trace -> the name bench reports it under
+PMC_KERNELS = {"bwd_dkdv16_kernel": "bwd_dkdv16_kernel", "bwd_dq16_kernel": "bwd_dq16_kernel",
+               "preprocess_kernel": "preprocess", "bwd_main_kernel": "bwd_main_kernel", "fwd16_kernel": "fwd16_kernel"}
 
 
 def log(msg):
@@ -60,6 +63,63 @@ def traffic_for(workload: str, kernel: str):
     if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def ingest_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int) -> dict:
+    """Turn two rocprofv3 --pmc CSV runs (FETCH_SIZE, then WRITE_SIZE) of this script into HBM bytes per launch.
+
+    Both runs must have been made with --calibration-copy-mib `copy_mib`: the copy through torch's elementwise
+    kernel (``neg``) of known size gives the factor from counter KiB to bytes moved.
+    """
+    import collections
+    import csv
+
+    def load(d, counter):
+        per = collections.OrderedDict()
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] != counter:
+                continue
+            k = int(r["Dispatch_Id"])
+            per.setdefault(k, [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+        return [per[k] for k in sorted(per)]
+
+    def calib(rows):
+        for i, (n, v) in enumerate(rows):
+            if "neg_kernel" in n:
+                return rows[i - 1][1], v  # the blit copy right before, and the elementwise copy
+        raise SystemExit("no calibration copy in the counter trace")
+
+    f, w = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    cf_blit, cf_elem = calib(f)
+    cw_blit, cw_elem = calib(w)
+    kib = copy_mib * 1024.0
+    ff, wf = kib / cf_elem, kib / cw_elem
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {}
+    rec["_calibration"] = {
+        "copy_mib": copy_mib,
+        "fetch_size_kib": {"runtime_blit_copy": cf_blit, "elementwise_copy": cf_elem},
+        "write_size_kib": {"runtime_blit_copy": cw_blit, "elementwise_copy": cw_elem},
+        "fetch_factor": ff, "write_factor": wf,
+        "note": "a plain copy of copy_mib MiB reads and writes copy_mib MiB; factor = true KiB / counter KiB"}
+    ent = rec.setdefault(workload, {})
+    for frag, label in PMC_KERNELS.items():
+        fv = [v for n, v in f if frag in n]
+        wv = [v for n, v in w if frag in n]
+        if not fv or not wv:
+            continue
+        fa, wa = sum(fv) / len(fv), sum(wv) / len(wv)
+        ent[label] = {"fetch_size_kib_per_dispatch": fv, "write_size_kib_per_dispatch": wv,
+                      "hbm_read_bytes_per_launch": fa * 1024 * ff, "hbm_write_bytes_per_launch": wa * 1024 * wf,
+                      "hbm_bytes_per_launch": (fa * ff + wa * wf) * 1024,
+                      "kernel_source_sha256_16": kernel_source_hash()}
+        log(f"{label}: read {fa * 1024 * ff / 1e9:.3f} GB, write {wa * 1024 * wf / 1e9:.3f} GB per launch")
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
 
 
 def cpu_baseline(inp, y_host, smax_h, ssum_h, wl, units_wanted: int):
@@ -114,7 +174,16 @@ def main(argv=None):
                     help="copy this many MiB device-to-device once before the timed steps, with the runtime's "
                          "blit kernel and with an elementwise kernel (plain copies of known size, for "
                          "scaling HBM byte counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script, run with --calibration-copy-mib, into per-launch HBM bytes in profiles/")
     args = ap.parse_args(argv)
+    if args.ingest_pmc:
+        from variable_length_flashattention_fa_amd import synth
+        if args.calibration_copy_mib <= 0:
+            ap.error("--ingest-pmc needs the --calibration-copy-mib the counter runs used")
+        ingest_pmc(*args.ingest_pmc, synth.workload(args.workload).name, args.calibration_copy_mib)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each (sequence, head) unit is "
@@ -265,6 +334,7 @@ def main(argv=None):
         "forward": {
             "ms_per_call": fwd_ms,
             "kernel_avg_ms": fwd_prof["fwd"][0] / max(fwd_prof["fwd"][1], 1),
+            "traffic": traffic_for(wl.name, "fwd16_kernel"),
             "useful_TFLOP/s": 4.0 * wl.heads * wl.head_dim * pairs / (fwd_ms * 1e-3) / 1e12,
             "pct_of_bf16_peak": 100.0 * 4.0 * wl.heads * wl.head_dim * pairs / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "note": "Y and statistics for the same inputs; useful work 4*N*D per admitted pair (two contractions)",
