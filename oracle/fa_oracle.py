@@ -34,6 +34,13 @@ Readings of points the page leaves open (each one is listed in the design doc):
   R10 a row with no admitted key has P == 0 exactly (dQ row 0, no dK/dV
       contribution); its stats are never read.
   R11 cu_seqlens are prefix sums with a leading 0 (B + 1 entries).
+  R15 grouped heads (N query heads over Nkv key/value heads, N a multiple of
+      Nkv, 约束说明): query head n reads key/value head n // (N / Nkv), so
+      each key/value head serves a contiguous group of query heads; its dK and
+      dV are the sums of the group's per-head contributions.  The dropout mask
+      is indexed by the query head.
+  R16 Dv < Dk (参数说明: V may have a smaller head dim than Q and K): Y, dY
+      and dV have V's head dim, dQ and dK have Q's; nothing else changes.
 
 Every function below computes the plain definition (one library matmul per
 contraction, no blocking beyond splitting query rows into chunks, which only
@@ -112,6 +119,11 @@ def dropout_keep(drop_mask: np.ndarray, bit0: int, rows: np.ndarray, lkv: int) -
     return out
 
 
+def kv_head(n: int, head_num: int, kv_heads: int) -> int:
+    """Key/value head read by query head n (R15): contiguous groups of head_num // kv_heads."""
+    return n // (head_num // kv_heads)
+
+
 # ---------------------------------------------------------------------------
 # forward (used only to produce consistent Y and statistics for tests)
 # ---------------------------------------------------------------------------
@@ -166,15 +178,19 @@ def forward_rows(q, k, v, cu_q, cu_kv, b: int, n: int, rows, *, mode: int = MASK
     k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
     bit0 = int(dropout_bit_bases(cu_q, cu_kv, head_num)[b]) + n * (q1 - q0) * (k1 - k0)
     rows = np.asarray(rows, dtype=np.int64)
+    hk = kv_head(n, head_num, k.shape[1])
     qr = np.asarray(q[q0:q1, n], dtype=np.float64)[rows]
-    ks = np.asarray(k[k0:k1, n], dtype=np.float64)
-    vs = np.asarray(v[k0:k1, n], dtype=np.float64)
+    ks = np.asarray(k[k0:k1, hk], dtype=np.float64)
+    vs = np.asarray(v[k0:k1, hk], dtype=np.float64)
     return _forward_rows(qr, ks, vs, q1 - q0, rows, scale, mode, pre, nxt, keep_prob, drop_mask, bit0)
 
 
 def forward(q, k, v, cu_q, cu_kv, *, mode: int = MASK_NONE, pre: int = 0, nxt: int = 0,
             keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int):
-    """Varlen forward over TND tensors; returns Y [T, N, D], m [N, T], l [N, T] (fp64)."""
+    """Varlen forward over TND tensors; returns Y [T, N, Dv], m [N, T], l [N, T] (fp64).
+
+    q is [Tq, N, Dk]; k and v are [Tkv, Nkv, Dk] and [Tkv, Nkv, Dv] with N a multiple of Nkv (R15).
+    """
     tq = q.shape[0]
     y = np.zeros((tq, head_num, v.shape[2]), dtype=np.float64)
     m = np.full((head_num, tq), -np.inf, dtype=np.float64)
@@ -187,7 +203,8 @@ def forward(q, k, v, cu_q, cu_kv, *, mode: int = MASK_NONE, pre: int = 0, nxt: i
             continue
         for n in range(head_num):
             bit0 = int(bases[b]) + n * (q1 - q0) * (k1 - k0)
-            yb, mb, lb = forward_unit(q[q0:q1, n], k[k0:k1, n], v[k0:k1, n], scale,
+            hk = kv_head(n, head_num, k.shape[1])
+            yb, mb, lb = forward_unit(q[q0:q1, n], k[k0:k1, hk], v[k0:k1, hk], scale,
                                       mode, pre, nxt, keep_prob, drop_mask, bit0)
             y[q0:q1, n] = yb
             m[n, q0:q1] = mb
@@ -273,10 +290,12 @@ def _stat0(stat):
 
 
 def _unit_args(b, n, q, k, v, dy, y, mstat, lstat, cu_q, cu_kv, bases):
+    """Slices of query head n of sequence b, with the key/value head it reads (R15)."""
     q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
     k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
     bit0 = int(bases[b]) + n * (q1 - q0) * (k1 - k0)
-    return (q[q0:q1, n], k[k0:k1, n], v[k0:k1, n], dy[q0:q1, n], y[q0:q1, n],
+    hk = kv_head(n, q.shape[1], k.shape[1])
+    return (q[q0:q1, n], k[k0:k1, hk], v[k0:k1, hk], dy[q0:q1, n], y[q0:q1, n],
             mstat[n, q0:q1], lstat[n, q0:q1], bit0)
 
 
@@ -301,11 +320,12 @@ def _pool_unit(job):
 def backward(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, *, mode: int = MASK_NONE,
              pre: int = 0, nxt: int = 0, keep_prob: float = 1.0, drop_mask=None,
              scale: float, head_num: int, workers: int = 1, units=None):
-    """Varlen backward over TND tensors; returns dQ, dK, dV [T, N, D] in fp64.
+    """Varlen backward over TND tensors; returns dQ [Tq, N, Dk], dK [Tkv, Nkv, Dk], dV [Tkv, Nkv, Dv] in fp64.
 
     Rows or keys that no admitted pair touches stay exactly 0.  `units` may
-    restrict the work to a list of (b, n) pairs (their slices are written, the
-    rest stays 0).  With workers > 1 the (b, n) units run in a fork-based
+    restrict the work to a list of (b, n) pairs of sequence and query head
+    (their contributions are written, the rest stays 0).  A key/value head
+    shared by several query heads receives the sum of their dK and dV (R15).  With workers > 1 the (b, n) units run in a fork-based
     process pool, each unit computed exactly as with workers == 1.
     """
     mstat, lstat = _stat0(softmax_max), _stat0(softmax_sum)
@@ -321,9 +341,10 @@ def backward(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, *, mode: int
                  if cu_q[b + 1] > cu_q[b] and cu_kv[b + 1] > cu_kv[b]]
 
     def put(b, n, dqs, dks, dvs):
+        hk = kv_head(n, head_num, k.shape[1])
         dq[cu_q[b]:cu_q[b + 1], n] = dqs
-        dk[cu_kv[b]:cu_kv[b + 1], n] = dks
-        dv[cu_kv[b]:cu_kv[b + 1], n] = dvs
+        dk[cu_kv[b]:cu_kv[b + 1], hk] += dks
+        dv[cu_kv[b]:cu_kv[b + 1], hk] += dvs
 
     if workers <= 1 or len(units) <= 1:
         for b, n in units:
@@ -344,7 +365,7 @@ def backward(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, *, mode: int
         os.environ[key] = "1"
     try:
         with ctx.Pool(processes=workers, initializer=_pool_init, initargs=(state,)) as pool:
-            for b, n, dqs, dks, dvs in pool.imap_unordered(_pool_unit, units):
+            for b, n, dqs, dks, dvs in pool.imap(_pool_unit, units):
                 put(b, n, dqs, dks, dvs)
     finally:
         for key, val in old.items():
@@ -392,16 +413,31 @@ def backward_dq_rows(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b: i
 def backward_dkdv_cols(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b: int, n: int,
                        cols, *, mode: int = MASK_NONE, pre: int = 0, nxt: int = 0,
                        keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int):
-    """dK and dV for selected keys (sequence-relative) of one (b, n): two [len(cols), D] fp64.
+    """dK and dV for selected keys (sequence-relative) of key/value head n of sequence b.
 
-    The same definition as backward_unit restricted to those keys: each needs
-    its column of S, Ps, dPd over all query rows, with every row's Delta.
+    Returns two [len(cols), Dk] and [len(cols), Dv] fp64 arrays: the sums over the query heads
+    that read head n (R15) of the same definition as backward_unit restricted to those keys.
+    Each needs its column of S, Ps, dPd over all query rows, with every row's Delta.
     """
+    group = head_num // k.shape[1]
+    cols = np.asarray(cols, dtype=np.int64)
+    dk = np.zeros((cols.size, k.shape[2]), dtype=np.float64)
+    dv = np.zeros((cols.size, v.shape[2]), dtype=np.float64)
+    for nq in range(n * group, (n + 1) * group):
+        a, c = _dkdv_cols_one_head(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b, nq, cols,
+                                   mode, pre, nxt, keep_prob, drop_mask, scale, head_num)
+        dk += a
+        dv += c
+    return dk, dv
+
+
+def _dkdv_cols_one_head(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b, n, cols, mode, pre, nxt,
+                        keep_prob, drop_mask, scale, head_num):
+    """Contribution of query head n to dK and dV of the selected keys of its key/value head."""
     mstat, lstat = _stat0(softmax_max), _stat0(softmax_sum)
     bases = dropout_bit_bases(cu_q, cu_kv, head_num)
     qs, ks, vs, dys, ys, ms, ls, bit0 = _unit_args(b, n, q, k, v, dy, y, mstat, lstat,
                                                    np.asarray(cu_q), np.asarray(cu_kv), bases)
-    cols = np.asarray(cols, dtype=np.int64)
     lq, lkv = qs.shape[0], ks.shape[0]
     qs = np.asarray(qs, dtype=np.float64)
     kc = np.asarray(ks, dtype=np.float64)[cols]

@@ -18,15 +18,17 @@ from oracle import fa_oracle as O
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _rand_case(rng, lq, lkv=None, heads=2, dim=4, keep_prob=1.0):
+def _rand_case(rng, lq, lkv=None, heads=2, dim=4, keep_prob=1.0, kv_heads=None, dim_v=None):
     lkv = lq if lkv is None else lkv
+    kv_heads = heads if kv_heads is None else kv_heads
+    dim_v = dim if dim_v is None else dim_v
     cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
     cu_kv = np.concatenate([[0], np.cumsum(lkv)]).astype(np.int64)
     tq, tk = int(cu_q[-1]), int(cu_kv[-1])
     q = rng.standard_normal((tq, heads, dim))
-    k = rng.standard_normal((tk, heads, dim))
-    v = rng.standard_normal((tk, heads, dim))
-    dy = rng.standard_normal((tq, heads, dim))
+    k = rng.standard_normal((tk, kv_heads, dim))
+    v = rng.standard_normal((tk, kv_heads, dim_v))
+    dy = rng.standard_normal((tq, heads, dim_v))
     drop = None
     if keep_prob < 1.0:
         nbits = int(sum(heads * a * c for a, c in zip(lq, lkv)))
@@ -86,6 +88,38 @@ def test_p1_finite_differences(mode, pre, nxt, kp, lens):
         assert np.max(np.abs(fd - g)) / denom <= 1e-6, name
 
 
+@pytest.mark.parametrize("mode,pre,nxt", [(O.MASK_NONE, 0, 0), (O.MASK_CAUSAL, 0, 0), (O.MASK_BAND, 2, 1)])
+@pytest.mark.parametrize("heads,kv_heads,dim,dim_v,kp", [(4, 2, 4, 4, 1.0), (3, 1, 4, 2, 0.7), (2, 2, 6, 3, 1.0)])
+def test_p1_finite_differences_grouped_heads_and_narrow_v(mode, pre, nxt, heads, kv_heads, dim, dim_v, kp):
+    # grouped heads (R15) and Dv < Dk (R16): the gradient of L = sum(dY o Y) by central differences
+    rng = np.random.default_rng(31 + 5 * mode + heads)
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, (4, 5), (6, 3), heads=heads, dim=dim, keep_prob=kp,
+                                                kv_heads=kv_heads, dim_v=dim_v)
+    scale = 0.6
+    (dq, dk, dv), _ = _full_backward(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, heads)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+
+    def loss(qq, kk, vv):
+        y, _, _ = O.forward(qq, kk, vv, cu_q, cu_kv, mode=mode, pre=pre, nxt=nxt, keep_prob=kp,
+                            drop_mask=drop, scale=scale, head_num=heads)
+        return float(np.sum(dy * y))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args[name] = xp
+            fp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            fm = loss(args["q"], args["k"], args["v"])
+            fd[idx] = (fp - fm) / (2 * h)
+        denom = max(np.max(np.abs(fd)), 1e-12)
+        assert np.max(np.abs(fd - g)) / denom <= 1e-6, name
+
+
 # --- P2/P4: torch fp64 autograd of a dense padded formulation -----------------------------
 
 def _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, heads):
@@ -98,11 +132,11 @@ def _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scal
     lq = np.diff(cu_q)
     lkv = np.diff(cu_kv)
     sq, sk = int(lq.max()), int(lkv.max())
-    d = q.shape[2]
+    d, dvd, hkv = q.shape[2], v.shape[2], k.shape[1]
     tq = torch.zeros(b_count, heads, sq, d, dtype=torch.float64)
-    tk = torch.zeros(b_count, heads, sk, d, dtype=torch.float64)
-    tv = torch.zeros(b_count, heads, sk, d, dtype=torch.float64)
-    tdy = torch.zeros(b_count, heads, sq, d, dtype=torch.float64)
+    tk = torch.zeros(b_count, hkv, sk, d, dtype=torch.float64)
+    tv = torch.zeros(b_count, hkv, sk, dvd, dtype=torch.float64)
+    tdy = torch.zeros(b_count, heads, sq, dvd, dtype=torch.float64)
     allow = torch.zeros(b_count, heads, sq, sk, dtype=torch.bool)
     zmul = torch.zeros(b_count, heads, sq, sk, dtype=torch.float64)
     allbits = None
@@ -135,12 +169,16 @@ def _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scal
                 zmul[b, n, :a, :c] = 1.0
     for t in (tq, tk, tv):
         t.requires_grad_(True)
-    s = scale * torch.matmul(tq, tk.transpose(-1, -2).contiguous())
+    # grouped heads: each key/value head repeated for its contiguous group of query heads; autograd
+    # sums the group's gradients back onto the shared head
+    ek = torch.repeat_interleave(tk, heads // hkv, dim=1)
+    ev = torch.repeat_interleave(tv, heads // hkv, dim=1)
+    s = scale * torch.matmul(tq, ek.transpose(-1, -2).contiguous())
     s = s.masked_fill(~allow, float("-inf"))
     rows_any = allow.any(dim=-1, keepdim=True)
     p = torch.softmax(torch.where(rows_any, s, torch.zeros_like(s)), dim=-1)
     p = torch.where(allow, p, torch.zeros_like(p))
-    y = torch.matmul(p * zmul, tv)
+    y = torch.matmul(p * zmul, ev)
     (tdy * y).sum().backward()
     dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v)
     for b in range(b_count):
@@ -162,6 +200,21 @@ def test_p2_p4_torch_autograd_padded(mode, pre, nxt, kp, lens):
     (dq, dk, dv), _ = _full_backward(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, 2)
     rq, rk, rv = _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, 2)
     for g, r in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.max(np.abs(g - r)) <= 1e-12 * max(1.0, np.max(np.abs(r)))
+
+
+@pytest.mark.parametrize("mode,pre,nxt", [(O.MASK_CAUSAL, 0, 0), (O.MASK_BAND, 5, 2)])
+@pytest.mark.parametrize("heads,kv_heads,dim,dim_v,kp", [(4, 2, 16, 16, 1.0), (6, 2, 16, 8, 0.8),
+                                                         (4, 1, 16, 8, 1.0)])
+def test_p2_torch_autograd_grouped_heads_and_narrow_v(mode, pre, nxt, heads, kv_heads, dim, dim_v, kp):
+    rng = np.random.default_rng(70 + heads + kv_heads)
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, (23, 9, 40), (31, 9, 12), heads=heads, dim=dim,
+                                                keep_prob=kp, kv_heads=kv_heads, dim_v=dim_v)
+    scale = 0.3
+    (dq, dk, dv), _ = _full_backward(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, heads)
+    rq, rk, rv = _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, heads)
+    for g, r in ((dq, rq), (dk, rk), (dv, rv)):
+        assert g.shape == r.shape
         assert np.max(np.abs(g - r)) <= 1e-12 * max(1.0, np.max(np.abs(r)))
 
 
@@ -348,6 +401,50 @@ def test_sampled_outputs_equal_full(mode, pre, nxt):
             np.testing.assert_array_equal(yr, yf[cu_q[b] + rows, n])
             np.testing.assert_array_equal(mr, mf[n, cu_q[b] + rows])
             np.testing.assert_array_equal(lr, lf[n, cu_q[b] + rows])
+
+
+def test_sampled_outputs_equal_full_grouped_heads():
+    # grouped heads with a narrower V: sampled dQ rows per query head, dK/dV columns per
+    # key/value head (summed over its group), forward rows per query head
+    rng = np.random.default_rng(41)
+    kp, heads, kv_heads = 0.85, 6, 2
+    lq, lkv = (21, 14), (17, 25)
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, lq, lkv, heads=heads, dim=8, keep_prob=kp,
+                                                kv_heads=kv_heads, dim_v=4)
+    mode, pre, nxt = O.MASK_BAND, 6, 2
+    (dq, dk, dv), (y, m, l) = _full_backward(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, 0.3, heads)
+    kw = dict(mode=mode, pre=pre, nxt=nxt, keep_prob=kp, drop_mask=drop, scale=0.3, head_num=heads)
+    yf, mf, lf = O.forward(q, k, v, cu_q, cu_kv, **kw)
+    for b in range(2):
+        rows = np.array([0, 4, lq[b] - 1])
+        cols = np.array([0, 7, lkv[b] - 1])
+        for n in range(heads):
+            r = O.backward_dq_rows(q, k, v, dy, y, m, l, cu_q, cu_kv, b, n, rows, **kw)
+            np.testing.assert_allclose(r, dq[cu_q[b] + rows, n], rtol=0, atol=1e-13)
+            yr, mr, lr = O.forward_rows(q, k, v, cu_q, cu_kv, b, n, rows, **kw)
+            np.testing.assert_array_equal(yr, yf[cu_q[b] + rows, n])
+        for hk in range(kv_heads):
+            gk, gv = O.backward_dkdv_cols(q, k, v, dy, y, m, l, cu_q, cu_kv, b, hk, cols, **kw)
+            np.testing.assert_allclose(gk, dk[cu_kv[b] + cols, hk], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(gv, dv[cu_kv[b] + cols, hk], rtol=0, atol=1e-13)
+
+
+def test_grouped_heads_equal_repeated_heads():
+    # R15 as an identity: grouped heads == every query head with its own copy of its key/value
+    # head, dK and dV summed over each group afterwards
+    rng = np.random.default_rng(43)
+    heads, kv_heads = 4, 2
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, (9, 13), (11, 13), heads=heads, dim=8, keep_prob=0.75,
+                                                kv_heads=kv_heads)
+    (dq, dk, dv), (y, _, _) = _full_backward(q, k, v, dy, cu_q, cu_kv, O.MASK_CAUSAL, 0, 0, 0.75, drop, 0.4,
+                                             heads)
+    ke, ve = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    (dq2, dk2, dv2), (y2, _, _) = _full_backward(q, ke, ve, dy, cu_q, cu_kv, O.MASK_CAUSAL, 0, 0, 0.75, drop,
+                                                 0.4, heads)
+    np.testing.assert_array_equal(y, y2)
+    np.testing.assert_array_equal(dq, dq2)
+    np.testing.assert_allclose(dk, dk2.reshape(dk2.shape[0], kv_heads, 2, -1).sum(axis=2), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(dv2.shape[0], kv_heads, 2, -1).sum(axis=2), rtol=0, atol=1e-13)
 
 
 # --- the dropout bit layout agrees with the independent generator ---------------------------
