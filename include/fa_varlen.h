@@ -87,7 +87,10 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BAND = 2 };
  * fa_varlen_bwd -- dQ, dK, dV of varlen attention.
  *
  * q, dy, y          [Tq, N, D] inputs (y is the forward output attentionIn).
- * k, v              [Tkv, N, D] inputs.
+ * k, v              [Tkv, Nkv, D] inputs.  Nkv divides N (grouped heads,
+ *                   constraints section of the page): query head n reads
+ *                   key/value head n / (N / Nkv), and dk, dv of a shared
+ *                   head hold the sum over the query heads that read it.
  * softmax_max/sum   [N, Tq, 8] contiguous fp32 device arrays: the forward's
  *                   row max and row sum of exp, replicated over the last
  *                   axis (element 0 is read).  Rows with no admitted key are
@@ -107,8 +110,8 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BAND = 2 };
  * stream            hipStream_t (NULL = the null stream).
  *
  * Supported: all tensors one dtype (FA_F32, FA_F16 or FA_BF16); D in {64,128};
- * k/v heads == q heads; v head_dim == q head_dim.  Other values the page
- * allows (grouped heads, Dv < Dk, other D) return FA_ERR_UNSUPPORTED.
+ * v head_dim == q head_dim.  Other values the page allows (Dv < Dk, other D)
+ * return FA_ERR_UNSUPPORTED.
  * Tq == 0 returns FA_OK with nothing launched.
  *
  * Calls on different streams share one library workspace per device and

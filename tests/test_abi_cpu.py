@@ -115,14 +115,26 @@ def test_unsupported_variants():
     # head dims outside {64, 128}
     args = {n: _t(10, dim=96) for n in ("q", "k", "v", "dy", "y", "dq", "dk", "dv")}
     assert _call(**args)[0] == B.FA_ERR_UNSUPPORTED
-    # grouped heads: 4 query heads over 2 key/value heads
-    args = {n: _t(10, heads=4) for n in ("q", "dy", "y", "dq")}
-    args.update({n: _t(10, heads=2) for n in ("k", "v", "dk", "dv")})
-    assert _call(head_num=4, **args)[0] == B.FA_ERR_UNSUPPORTED
     # v head dim smaller than k's
     assert _call(v=_t(10, dim=32), dv=_t(10, dim=32))[0] == B.FA_ERR_UNSUPPORTED
     # misaligned base address
     assert _call(q=_t(10, data=FAKE + 2))[0] == B.FA_ERR_UNSUPPORTED
+
+
+def test_grouped_heads_validation():
+    # 4 query heads over 3 key/value heads: not a multiple
+    args = {n: _t(10, heads=4) for n in ("q", "dy", "y", "dq")}
+    args.update({n: _t(10, heads=3) for n in ("k", "v", "dk", "dv")})
+    assert _call(head_num=4, **args)[0] == B.FA_ERR_INVALID
+    # dk / dv must have the key/value head count
+    args = {n: _t(10, heads=4) for n in ("q", "dy", "y", "dq", "dk")}
+    args.update({n: _t(10, heads=2) for n in ("k", "v", "dv")})
+    assert _call(head_num=4, **args)[0] == B.FA_ERR_INVALID
+    # a valid grouped layout with no query tokens passes validation and returns before device work
+    args = {n: _t(0, heads=4, data=0) for n in ("q", "dy", "y", "dq")}
+    args.update({n: _t(0, heads=2, data=0) for n in ("k", "v", "dk", "dv")})
+    st, msg = _call(head_num=4, cu_q=(0, 0), cu_kv=(0, 0), **args)
+    assert st == B.FA_OK, msg
 
 
 def test_empty_query_returns_ok_without_device_work():
@@ -186,7 +198,8 @@ def test_forward_null_pointers():
     (dict(y=_t(11)), B.FA_ERR_INVALID),
     (dict(cu_q=(0, 4, 10), cu_kv=(0, 10)), B.FA_ERR_INVALID),
     (dict(cu_q=(0, 12, 10), cu_kv=(0, 5, 10)), B.FA_ERR_INVALID),
-    (dict(k=_t(10, heads=1), v=_t(10, heads=1)), B.FA_ERR_UNSUPPORTED),
+    (dict(k=_t(10, heads=3), v=_t(10, heads=3)), B.FA_ERR_INVALID),
+    (dict(k=_t(10, heads=1), v=_t(10, heads=2)), B.FA_ERR_INVALID),
     (dict(q=_t(10, dim=96), k=_t(10, dim=96), v=_t(10, dim=96), y=_t(10, dim=96)), B.FA_ERR_UNSUPPORTED),
     (dict(smax=FAKE + 4), B.FA_ERR_UNSUPPORTED),
 ])

@@ -23,11 +23,9 @@ def gpu_forward(inp, mode, pre, nxt, kp, scale, views=None):
     dev = torch.device(DEV)
     q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
     drop = torch.from_numpy(inp.drop_mask).to(dev) if inp.drop_mask is not None else None
+    y = torch.empty(q.shape[0], q.shape[1], v.shape[2], dtype=q.dtype, device=dev)  # v's head dim
     if views is not None:
-        q, k, v = (views(x) for x in (q, k, v))
-        y = views(torch.empty_like(q))
-    else:
-        y = torch.empty_like(q)
+        q, k, v, y = (views(x) for x in (q, k, v, y))
     smax = torch.empty(q.shape[1], q.shape[0], 8, dtype=torch.float32, device=dev)
     ssum = torch.empty_like(smax)
     for t in (y, smax, ssum):

@@ -7,13 +7,13 @@ Inputs come from the seeded generator; Y and the statistics from the oracle's
 forward (small cases) or from a plain torch forward on the device (full-size
 cases, where the oracle then checks sampled rows and keys).
 """
-import sys
 import time
 
 import numpy as np
 import pytest
 import torch
 
+from gpu_common import assert_close, gpu_backward, log, make, run_small
 from oracle import fa_oracle as O
 from variable_length_flashattention_fa_amd import binding as B
 from variable_length_flashattention_fa_amd import synth
@@ -22,93 +22,6 @@ from variable_length_flashattention_fa_amd.inputs_forward import forward_stats
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-
-
-def log(msg):
-    print(msg, file=sys.stderr, flush=True)
-
-
-def tol_for(dtype):
-    return 1e-5 if dtype == torch.float32 else 1e-2
-
-
-def assert_close(name, g, o, dtype):
-    g = np.asarray(g, dtype=np.float64)
-    o = np.asarray(o, dtype=np.float64)
-    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
-    ref = np.linalg.norm(o)
-    err = np.linalg.norm(g - o)
-    mx = np.max(np.abs(o)) if o.size else 0.0
-    if ref == 0.0:
-        # The relative criterion is undefined for an all-zero reference.  Where the
-        # zero comes from cancellation (dP - D with Ps = 1) fp32 leaves a residue of
-        # order 1e-7; rows with no admitted key are checked for exact zeros separately.
-        assert np.max(np.abs(g)) <= 1e-5, f"{name}: expected zeros, max |gpu| = {np.max(np.abs(g)):.3e}"
-        return
-    rel = err / ref
-    assert rel <= tol_for(dtype), f"{name}: relative Frobenius error {rel:.3e}"
-    assert np.max(np.abs(g - o)) <= 5e-2 * mx, f"{name}: max abs error {np.max(np.abs(g - o)):.3e} vs {mx:.3e}"
-
-
-def oracle_forward(inp, mode, pre, nxt, kp, scale):
-    q, k, v = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v))
-    y, m, l = O.forward(q, k, v, inp.cu_q, inp.cu_kv, mode=mode, pre=pre, nxt=nxt, keep_prob=kp,
-                        drop_mask=inp.drop_mask, scale=scale, head_num=inp.q.shape[1])
-    yt = torch.from_numpy(y).to(inp.q.dtype)
-    smax, ssum = O.stats_to_page_layout(m, l)
-    return yt, smax, ssum
-
-
-def oracle_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, workers=4):
-    q, k, v, dy = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v, inp.dy))
-    y = synth.as_float_array(yt)
-    return O.backward(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, mode=mode, pre=pre, nxt=nxt,
-                      keep_prob=kp, drop_mask=inp.drop_mask, scale=scale, head_num=inp.q.shape[1],
-                      workers=workers)
-
-
-def gpu_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, views=None):
-    dev = torch.device(DEV)
-    q, k, v, dy, y = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.dy, yt))
-    smax_d = torch.as_tensor(np.ascontiguousarray(smax)).to(dev)
-    ssum_d = torch.as_tensor(np.ascontiguousarray(ssum)).to(dev)
-    drop = torch.from_numpy(inp.drop_mask).to(dev) if inp.drop_mask is not None else None
-    if views is not None:
-        q, k, v, dy, y = (views(x) for x in (q, k, v, dy, y))
-        dq, dk, dv = views(torch.empty_like(q)), views(torch.empty_like(k)), views(torch.empty_like(v))
-    else:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    # poison the outputs: every element must be written by the library
-    for t in (dq, dk, dv):
-        t.fill_(float("nan"))
-    B.fa_varlen_bwd(q, k, v, dy, y, smax_d, ssum_d, inp.cu_q, inp.cu_kv, mode, pre, nxt, kp, drop, scale,
-                    q.shape[1], dq, dk, dv)
-    torch.cuda.synchronize()
-    return dq.cpu(), dk.cpu(), dv.cpu()
-
-
-def run_small(inp, mode, pre=0, nxt=0, kp=1.0, scale=None, poison_empty=False, views=None):
-    scale = scale if scale is not None else 1.0 / np.sqrt(inp.q.shape[2])
-    log(f"case T={inp.q.shape[0]} N={inp.q.shape[1]} D={inp.q.shape[2]} {inp.q.dtype} mode={mode} "
-        f"pre={pre} nxt={nxt} kp={kp} lens={np.diff(inp.cu_q).tolist()[:12]}")
-    yt, smax, ssum = oracle_forward(inp, mode, pre, nxt, kp, scale)
-    if poison_empty:
-        empty = ~np.isfinite(smax[:, :, 0]) | (ssum[:, :, 0] == 0)
-        assert empty.any()
-        smax = smax.copy(); ssum = ssum.copy()
-        smax[empty] = np.nan
-        ssum[empty] = np.nan
-    ref = oracle_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale)
-    got = gpu_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, views=views)
-    for name, g, o in zip(("dq", "dk", "dv"), got, ref):
-        assert_close(name, g.double().numpy(), o, inp.q.dtype)
-    return got, ref, (yt, smax, ssum)
-
-
-def make(lens, heads, dim, dtype, mode=0, pre=0, nxt=0, kp=1.0, seed=0, kv_lens=None, dy_scale=0.1):
-    wl = synth.Workload("edge", dtype, tuple(lens), heads, dim, mode, pre, nxt, kp, dy_scale, seed,
-                        kv_lengths=None if kv_lens is None else tuple(kv_lens))
-    return synth.make(wl)
 
 
 # --- the five workloads at oracle-sized shapes ---------------------------------------------

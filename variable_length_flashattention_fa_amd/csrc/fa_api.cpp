@@ -287,10 +287,6 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         return FA_ERR_INVALID;
     }
     // ---- allowed by the page, not built ----
-    if (q->heads != k->heads) {
-        set_error("grouped heads (k/v heads < q heads) are not supported");
-        return FA_ERR_UNSUPPORTED;
-    }
     if (v->head_dim != k->head_dim) {
         set_error("v head_dim < k head_dim is not supported");
         return FA_ERR_UNSUPPORTED;
@@ -439,6 +435,7 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         }
         a.tq = static_cast<int32_t>(tq);
         a.heads = static_cast<int32_t>(heads);
+        a.group = static_cast<int32_t>(heads / k->heads);
         a.mode = atten_mode;
         a.pre = static_cast<int32_t>(pre);
         a.nxt = static_cast<int32_t>(nxt);
@@ -470,6 +467,7 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
         a.tq = static_cast<int32_t>(tq);
         a.heads = static_cast<int32_t>(heads);
+        a.group = static_cast<int32_t>(heads / k->heads);
         a.mode = atten_mode;
         a.pre = static_cast<int32_t>(pre);
         a.nxt = static_cast<int32_t>(nxt);
@@ -571,10 +569,6 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     if (cu_seqlens_q->cu[batch] != q->tokens || cu_seqlens_kv->cu[batch] != k->tokens) {
         set_error("cu_seqlens must end at the token counts of q and k");
         return FA_ERR_INVALID;
-    }
-    if (q->heads != k->heads) {
-        set_error("grouped heads (k/v heads < q heads) are not supported");
-        return FA_ERR_UNSUPPORTED;
     }
     if (v->head_dim != k->head_dim) {
         set_error("v head_dim < k head_dim is not supported");
@@ -685,6 +679,7 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     a.drop_bytes = keep_prob < 1.0 ? (drop_bits + 7) / 8 : 0;
     a.tq = static_cast<int32_t>(tq);
     a.heads = static_cast<int32_t>(heads);
+    a.group = static_cast<int32_t>(heads / k->heads);
     a.mode = atten_mode;
     a.pre = static_cast<int32_t>(pre);
     a.nxt = static_cast<int32_t>(nxt);

@@ -7,9 +7,10 @@
 // beta_i = max_i * log2 e + log2(sum_i) (computed by the row preprocess).
 //
 // Two kernels; each wave owns 32 rows of the resident block:
-//   dkdv: 4 waves (one per SIMD), one workgroup per (block of 128 keys, head).  Each
-//         wave keeps its keys' K and V rows and dK / dV accumulators in registers,
-//         and walks the 64-row query tiles that can see the block:
+//   dkdv: 4 waves (one per SIMD), one workgroup per (block of 128 keys, key/value head).
+//         Each wave keeps its keys' K and V rows and dK / dV accumulators in registers,
+//         and walks, for every query head that reads the key/value head, the 64-row
+//         query tiles that can see the block:
 //           S = Q K^T, dP = dY V^T        (A from the Q / dY tile, B from K / V regs)
 //           dV += Pd^T dY, dK += dS^T Q   (A straight from the S / dP accumulators)
 //   dq:   8 waves (two per SIMD), one workgroup per (block of 256 queries, head).  Each wave keeps its
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     __shared__ __attribute__((aligned(16))) float2 sSt[NB][BQ];
 
     const fa_work_item_t it = p.items_kv[blockIdx.x];
-    const int n = blockIdx.y;
+    const int hk = blockIdx.y;  // key/value head; query heads hk * group .. hk * group + group - 1 read it
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
     const int lane = threadIdx.x & 63;
     const int col = lane & 31;
@@ -102,9 +103,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         LdsOffsets<D> lo_;
         lo_.init(lane);
 
-        const T* gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
-        const T* gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
-        const float2* gstat = p.rowstat + static_cast<int64_t>(n) * p.tq + it.q_start;
+        // the query head being walked (set per head below) and its tensors
+        int n = hk * p.group;
+        const T* gq = nullptr;
+        const T* gdy = nullptr;
+        const float2* gstat = nullptr;
         int qoff[TW];
         int dyoff[TW];
         // wave w copies 1 KiB chunks w*TW .. w*TW + TW - 1 of each tile (one run)
@@ -120,8 +123,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         {
             const bool ok = jw < K;
             const int64_t row = it.kv_start + (ok ? jw : 0);
-            const vec* kr = reinterpret_cast<const vec*>(static_cast<const T*>(p.k) + row * p.k_st + n * p.k_sh);
-            const vec* vr = reinterpret_cast<const vec*>(static_cast<const T*>(p.v) + row * p.v_st + n * p.v_sh);
+            const vec* kr = reinterpret_cast<const vec*>(static_cast<const T*>(p.k) + row * p.k_st + hk * p.k_sh);
+            const vec* vr = reinterpret_cast<const vec*>(static_cast<const T*>(p.v) + row * p.v_st + hk * p.v_sh);
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) {
                 kreg[s] = ok ? kr[2 * s + h] : vec{};
@@ -376,19 +379,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             }
         };
 
-        // prologue: tiles tb and tb + 1 in flight, zeros in the third buffer (read by the Y of
-        // the step before the first, whose packed P / dS are zero)
-        issue(tb, 0);
-        if (tb + 1 < te) issue(tb + 1, 1);
-        for (int i = threadIdx.x; i < 2 * TILE / 8; i += 64 * NW) reinterpret_cast<vec*>(sBuf[2][0])[i] = vec{};
-        wait_dma();
-        __syncthreads();
-        {
-            const Where w0 = where(kStepFirst, 0);
-            static_for<0, LA>([&](auto kc) {
-                if constexpr (decltype(kc)::value % 2 == 0) opr[decltype(kc)::value] = read_op(w0, kc);
-            });
-        }
         // Tiles whose 64 rows all see all 128 keys of the block need no mask.  For the causal and
         // band windows they form one run [f0, f1): rows in range (t < L / 64), keys in range, and
         // the window admits the block's corner pairs.
@@ -409,26 +399,54 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             f0 = min(max(lo, tb), te);
             f1 = min(max(hi, f0), te);
         }
-        step(IC<kStepFirst>{}, IC<kStepA>{}, IC<0>{}, tb, 0, 0);
-        int b = 0;
-        auto next_buf = [](int x) { return x == NB - 1 ? 0 : x + 1; };
-        for (int t = tb; t < f0; ++t) {
-            step(IC<kStepA>{}, IC<kStepB>{}, IC<1>{}, t, b, b);
-            step(IC<kStepB>{}, IC<kStepA>{}, IC<1>{}, t, b, next_buf(b));
-            b = next_buf(b);
+        for (int r = 0; r < p.group; ++r) {
+            n = hk * p.group + r;
+            gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
+            gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
+            gstat = p.rowstat + static_cast<int64_t>(n) * p.tq + it.q_start;
+            if (r > 0) {
+                // every wave is done with the previous head's tiles before they are overwritten
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    pkY[i] = vec{};
+                    dsY[i] = vec{};
+                }
+            }
+            // prologue: tiles tb and tb + 1 in flight, zeros in the third buffer (read by the Y of
+            // the step before the first, whose packed P / dS are zero)
+            issue(tb, 0);
+            if (tb + 1 < te) issue(tb + 1, 1);
+            for (int i = threadIdx.x; i < 2 * TILE / 8; i += 64 * NW) reinterpret_cast<vec*>(sBuf[2][0])[i] = vec{};
+            wait_dma();
+            __syncthreads();
+            {
+                const Where w0 = where(kStepFirst, 0);
+                static_for<0, LA>([&](auto kc) {
+                    if constexpr (decltype(kc)::value % 2 == 0) opr[decltype(kc)::value] = read_op(w0, kc);
+                });
+            }
+            step(IC<kStepFirst>{}, IC<kStepA>{}, IC<0>{}, tb, 0, 0);
+            int b = 0;
+            auto next_buf = [](int x) { return x == NB - 1 ? 0 : x + 1; };
+            for (int t = tb; t < f0; ++t) {
+                step(IC<kStepA>{}, IC<kStepB>{}, IC<1>{}, t, b, b);
+                step(IC<kStepB>{}, IC<kStepA>{}, IC<1>{}, t, b, next_buf(b));
+                b = next_buf(b);
+            }
+            for (int t = f0; t < f1; ++t) {
+                step(IC<kStepA>{}, IC<kStepB>{}, IC<0>{}, t, b, b);
+                step(IC<kStepB>{}, IC<kStepA>{}, IC<0>{}, t, b, next_buf(b));
+                b = next_buf(b);
+            }
+            for (int t = f1; t < te; ++t) {
+                step(IC<kStepA>{}, IC<kStepB>{}, IC<1>{}, t, b, b);
+                step(IC<kStepB>{}, IC<kStepA>{}, IC<1>{}, t, b, next_buf(b));
+                b = next_buf(b);
+            }
+            // Y of the last tile's second half (buffer of tile te - 1)
+            step(IC<kStepLast>{}, IC<kStepLast>{}, IC<0>{}, te - 1, b == 0 ? NB - 1 : b - 1, 0);
         }
-        for (int t = f0; t < f1; ++t) {
-            step(IC<kStepA>{}, IC<kStepB>{}, IC<0>{}, t, b, b);
-            step(IC<kStepB>{}, IC<kStepA>{}, IC<0>{}, t, b, next_buf(b));
-            b = next_buf(b);
-        }
-        for (int t = f1; t < te; ++t) {
-            step(IC<kStepA>{}, IC<kStepB>{}, IC<1>{}, t, b, b);
-            step(IC<kStepB>{}, IC<kStepA>{}, IC<1>{}, t, b, next_buf(b));
-            b = next_buf(b);
-        }
-        // Y of the last tile's second half (buffer of tile te - 1)
-        step(IC<kStepLast>{}, IC<kStepLast>{}, IC<0>{}, te - 1, b == 0 ? NB - 1 : b - 1, 0);
     }
 
     // the accumulators were last written by MFMAs the compiler does not see: wait them out
@@ -438,8 +456,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 
     // epilogue: dK = scale * sum dS^T Q, dV = sum Pd^T dY; the lane holds column nt*32 + col
     // of key rows 8g + 4h + r
-    T* gdk = static_cast<T*>(p.dk) + static_cast<int64_t>(it.kv_start) * p.dk_st + n * p.dk_sh;
-    T* gdv = static_cast<T*>(p.dv) + static_cast<int64_t>(it.kv_start) * p.dv_st + n * p.dv_sh;
+    T* gdk = static_cast<T*>(p.dk) + static_cast<int64_t>(it.kv_start) * p.dk_st + hk * p.dk_sh;
+    T* gdv = static_cast<T*>(p.dv) + static_cast<int64_t>(it.kv_start) * p.dv_st + hk * p.dv_sh;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -492,8 +510,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     LdsOffsets<D> lo_;
     lo_.init(lane);
 
-    const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + n * p.k_sh;
-    const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + n * p.v_sh;
+    const int hk = n / p.group;  // the key/value head this query head reads
+    const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh;
+    const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + hk * p.v_sh;
     // wave w copies 1 KiB chunks w*TW .. w*TW + TW - 1 of each key tile (one run)
     int koff[TW];
     int voff[TW];
@@ -659,7 +678,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 
 template <typename T, int D, bool DROP>
 static hipError_t launch_dkdv_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
-    bwd_dkdv16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(256), 0,
+    bwd_dkdv16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads / a.group)), dim3(256), 0,
                                     stream>>>(a);
     return hipGetLastError();
 }

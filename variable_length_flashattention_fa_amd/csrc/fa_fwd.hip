@@ -55,8 +55,9 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     LdsOffsets<D> lo_;
     lo_.init(lane);
 
-    const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + n * p.k_sh;
-    const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + n * p.v_sh;
+    const int hk = n / p.group;  // the key/value head this query head reads
+    const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh;
+    const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + hk * p.v_sh;
     int koff[TW];
     int voff[TW];
 #pragma unroll
@@ -285,8 +286,9 @@ __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) 
         khi = min(khi, qi + off + p.nxt);
     }
     const float* q = static_cast<const float*>(p.q) + static_cast<int64_t>(it.q_start + qi) * p.q_st + n * p.q_sh;
-    const float* kb = static_cast<const float*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + n * p.k_sh;
-    const float* vb = static_cast<const float*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + n * p.v_sh;
+    const int hk = n / p.group;  // the key/value head this query head reads
+    const float* kb = static_cast<const float*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh;
+    const float* vb = static_cast<const float*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + hk * p.v_sh;
     float qr[D];
     float o[D];
 #pragma unroll

@@ -33,7 +33,8 @@ struct MainArgs {
     const fa_work_item_t* items;
     const uint8_t* drop_mask;
     int32_t tq;
-    int32_t heads;
+    int32_t heads;   // query heads
+    int32_t group;   // query heads per key/value head
     int32_t mode;
     int32_t pre;     // clamped window bounds
     int32_t nxt;
@@ -42,7 +43,7 @@ struct MainArgs {
     float scale;      // folded into dK
 };
 
-// KV-block-major backward over n_items work items x heads.
+// KV-block-major backward over n_items work items x key/value heads.
 hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs& a, int64_t n_items,
                        hipStream_t stream);
 
@@ -71,11 +72,11 @@ struct Bwd16Args {
     const fa_work_item_t* items_q;   // query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles)
     const uint8_t* drop_mask;
     int64_t drop_bytes;  // size of the dropout mask in bytes (bounds its reads)
-    int32_t tq, heads, mode, pre, nxt;
+    int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float exp_scale, inv_keep, scale;
 };
 
-// dK/dV kernel over n_items key-block items x heads.
+// dK/dV kernel over n_items key-block items x key/value heads (each sums its group of query heads).
 hipError_t launch_dkdv16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
                          hipStream_t stream);
 
@@ -97,7 +98,7 @@ struct FwdArgs {
     const fa_work_item_t* items;  // query-block items
     const uint8_t* drop_mask;
     int64_t drop_bytes;  // size of the dropout mask in bytes (bounds its reads)
-    int32_t tq, heads, mode, pre, nxt;
+    int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float scale, exp_scale, inv_keep;
 };
 

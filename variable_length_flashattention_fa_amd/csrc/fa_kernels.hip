@@ -174,7 +174,7 @@ struct DevArgs {
     float* dq_acc;
     const fa_work_item_t* items;
     const uint8_t* drop_mask;
-    int32_t tq, heads, mode, pre, nxt;
+    int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float exp_scale, inv_keep, scale;
 };
 
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     __shared__ float2 sStat[BQ];
 
     const fa_work_item_t it = p.items[blockIdx.x];
-    const int n = blockIdx.y;
+    const int hk = blockIdx.y;  // key/value head; its group of query heads is walked in turn
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -216,16 +216,13 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     const int j0 = it.block * BKV;
     const int jw = j0 + 32 * w + col;  // this lane's key (sequence coordinates) in S / P
 
-    const T* __restrict__ gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
-    const T* __restrict__ gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
-
     // K and V rows of this lane as B operands of S = Q K^T and dP = dY V^T
     vec kreg[D / KS];
     vec vreg[D / KS];
     {
         const bool ok = jw < K;
-        const T* kr = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start + (ok ? jw : 0)) * p.k_st + n * p.k_sh;
-        const T* vr = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start + (ok ? jw : 0)) * p.v_st + n * p.v_sh;
+        const T* kr = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start + (ok ? jw : 0)) * p.k_st + hk * p.k_sh;
+        const T* vr = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start + (ok ? jw : 0)) * p.v_st + hk * p.v_sh;
 #pragma unroll
         for (int s = 0; s < D / KS; ++s) {
 #pragma unroll
@@ -254,161 +251,166 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
         accV[i] = zero16();
     }
 
-    const int64_t drop_row0 = DROP ? it.drop_base + static_cast<int64_t>(n) * L * K : 0;
+    for (int r = 0; r < p.group; ++r) {
+        const int n = hk * p.group + r;  // query head
+        const T* __restrict__ gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
+        const T* __restrict__ gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
+        const int64_t drop_row0 = DROP ? it.drop_base + static_cast<int64_t>(n) * L * K : 0;
 
-    for (int t = it.tile_begin; t < it.tile_end; ++t) {
-        const int q0 = t * BQ;
-        __syncthreads();  // previous tile's LDS reads are done
-        for (int idx = tid; idx < BQ * VPR; idx += 256) {
-            const int r = idx / VPR;
-            const int cv = idx - r * VPR;
-            const int qi = q0 + r;
-            Chunk<T> xq, xd;
-            if (qi < L) {
-                xq = *reinterpret_cast<const Chunk<T>*>(gq + static_cast<int64_t>(qi) * p.q_st + cv * VEC);
-                xd = *reinterpret_cast<const Chunk<T>*>(gdy + static_cast<int64_t>(qi) * p.dy_st + cv * VEC);
-            } else {
+        for (int t = it.tile_begin; t < it.tile_end; ++t) {
+            const int q0 = t * BQ;
+            __syncthreads();  // previous tile's LDS reads are done
+            for (int idx = tid; idx < BQ * VPR; idx += 256) {
+                const int r = idx / VPR;
+                const int cv = idx - r * VPR;
+                const int qi = q0 + r;
+                Chunk<T> xq, xd;
+                if (qi < L) {
+                    xq = *reinterpret_cast<const Chunk<T>*>(gq + static_cast<int64_t>(qi) * p.q_st + cv * VEC);
+                    xd = *reinterpret_cast<const Chunk<T>*>(gdy + static_cast<int64_t>(qi) * p.dy_st + cv * VEC);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        xq.e[e] = static_cast<T>(0.f);
+                        xd.e[e] = static_cast<T>(0.f);
+                    }
+                }
+                *reinterpret_cast<Chunk<T>*>(&sQ[r * PQ + cv * VEC]) = xq;
+                *reinterpret_cast<Chunk<T>*>(&sdY[r * PQ + cv * VEC]) = xd;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    xq.e[e] = static_cast<T>(0.f);
-                    xd.e[e] = static_cast<T>(0.f);
+                    sQt[(cv * VEC + e) * PT + r] = xq.e[e];
+                    sdYt[(cv * VEC + e) * PT + r] = xd.e[e];
                 }
             }
-            *reinterpret_cast<Chunk<T>*>(&sQ[r * PQ + cv * VEC]) = xq;
-            *reinterpret_cast<Chunk<T>*>(&sdY[r * PQ + cv * VEC]) = xd;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                sQt[(cv * VEC + e) * PT + r] = xq.e[e];
-                sdYt[(cv * VEC + e) * PT + r] = xd.e[e];
+            if (tid < BQ) {
+                const int qi = q0 + tid;
+                sStat[tid] = qi < L ? p.rowstat[static_cast<int64_t>(n) * p.tq + it.q_start + qi] : make_float2(0.f, 0.f);
             }
-        }
-        if (tid < BQ) {
-            const int qi = q0 + tid;
-            sStat[tid] = qi < L ? p.rowstat[static_cast<int64_t>(n) * p.tq + it.q_start + qi] : make_float2(0.f, 0.f);
-        }
-        __syncthreads();
+            __syncthreads();
 
-        // S = Q K^T and dP = dY V^T for this wave's 32 keys
-        f32x16 accS[MT];
-        f32x16 accP[MT];
+            // S = Q K^T and dP = dY V^T for this wave's 32 keys
+            f32x16 accS[MT];
+            f32x16 accP[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            accS[mt] = zero16();
-            accP[mt] = zero16();
+            for (int mt = 0; mt < MT; ++mt) {
+                accS[mt] = zero16();
+                accP[mt] = zero16();
 #pragma unroll
-            for (int s = 0; s < D / KS; ++s) {
-                const vec aq = *reinterpret_cast<const vec*>(&sQ[(mt * 32 + col) * PQ + s * KS + h * KL]);
-                const vec ad = *reinterpret_cast<const vec*>(&sdY[(mt * 32 + col) * PQ + s * KS + h * KL]);
-                accS[mt] = E::mfma(aq, kreg[s], accS[mt]);
-                accP[mt] = E::mfma(ad, vreg[s], accP[mt]);
+                for (int s = 0; s < D / KS; ++s) {
+                    const vec aq = *reinterpret_cast<const vec*>(&sQ[(mt * 32 + col) * PQ + s * KS + h * KL]);
+                    const vec ad = *reinterpret_cast<const vec*>(&sdY[(mt * 32 + col) * PQ + s * KS + h * KL]);
+                    accS[mt] = E::mfma(aq, kreg[s], accS[mt]);
+                    accP[mt] = E::mfma(ad, vreg[s], accP[mt]);
+                }
             }
-        }
 
-        // Is every pair of the (tile, block) admitted and in range?
-        bool full = (q0 + BQ <= L) && (j0 + BKV <= K);
-        if (p.mode == FA_MASK_CAUSAL) {
-            full = full && (j0 + BKV - 1 <= q0 + off);
-        } else if (p.mode == FA_MASK_BAND) {
-            full = full && (j0 >= q0 + BQ - 1 + off - p.pre) && (j0 + BKV - 1 <= q0 + off + p.nxt);
-        }
+            // Is every pair of the (tile, block) admitted and in range?
+            bool full = (q0 + BQ <= L) && (j0 + BKV <= K);
+            if (p.mode == FA_MASK_CAUSAL) {
+                full = full && (j0 + BKV - 1 <= q0 + off);
+            } else if (p.mode == FA_MASK_BAND) {
+                full = full && (j0 >= q0 + BQ - 1 + off - p.pre) && (j0 + BKV - 1 <= q0 + off + p.nxt);
+            }
 
-        // Ps, Pd = Ps Z / kp and dS = Ps (dP Z / kp - D), in place of S and dP
+            // Ps, Pd = Ps Z / kp and dS = Ps (dP Z / kp - D), in place of S and dP
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                const int il = mt * 32 + acc_row(a, h);
-                const float2 st = sStat[il];
-                float pv = __builtin_amdgcn_exp2f(accS[mt][a] * p.exp_scale - st.y);
-                float zk = 1.f;
-                if (!full) {
-                    const int i = q0 + il;
-                    bool adm = (i < L) && (jw < K);
-                    if (p.mode == FA_MASK_CAUSAL) {
-                        adm = adm && (jw <= i + off);
-                    } else if (p.mode == FA_MASK_BAND) {
-                        adm = adm && (jw >= i + off - p.pre) && (jw <= i + off + p.nxt);
-                    }
-                    pv = adm ? pv : 0.f;
-                    if constexpr (DROP) {
-                        if (adm) {
-                            const int64_t bit = drop_row0 + static_cast<int64_t>(i) * K + jw;
-                            zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
+                for (int a = 0; a < 16; ++a) {
+                    const int il = mt * 32 + acc_row(a, h);
+                    const float2 st = sStat[il];
+                    float pv = __builtin_amdgcn_exp2f(accS[mt][a] * p.exp_scale - st.y);
+                    float zk = 1.f;
+                    if (!full) {
+                        const int i = q0 + il;
+                        bool adm = (i < L) && (jw < K);
+                        if (p.mode == FA_MASK_CAUSAL) {
+                            adm = adm && (jw <= i + off);
+                        } else if (p.mode == FA_MASK_BAND) {
+                            adm = adm && (jw >= i + off - p.pre) && (jw <= i + off + p.nxt);
                         }
+                        pv = adm ? pv : 0.f;
+                        if constexpr (DROP) {
+                            if (adm) {
+                                const int64_t bit = drop_row0 + static_cast<int64_t>(i) * K + jw;
+                                zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
+                            }
+                        }
+                    } else if constexpr (DROP) {
+                        const int i = q0 + il;
+                        const int64_t bit = drop_row0 + static_cast<int64_t>(i) * K + jw;
+                        zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
                     }
-                } else if constexpr (DROP) {
-                    const int i = q0 + il;
-                    const int64_t bit = drop_row0 + static_cast<int64_t>(i) * K + jw;
-                    zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
+                    const float ds = pv * (accP[mt][a] * zk - st.x);
+                    accS[mt][a] = pv * zk;
+                    accP[mt][a] = ds;
                 }
-                const float ds = pv * (accP[mt][a] * zk - st.x);
-                accS[mt][a] = pv * zk;
-                accP[mt][a] = ds;
             }
-        }
 
-        // dV += Pd^T dY and dK += dS^T Q: contraction over the tile's query rows,
-        // taken straight from the accumulator layout (lane = key, slots = rows)
+            // dV += Pd^T dY and dK += dS^T Q: contraction over the tile's query rows,
+            // taken straight from the accumulator layout (lane = key, slots = rows)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-            for (int kk = 0; kk < 32 / KS; ++kk) {
-                vec ap, as;
-#pragma unroll
-                for (int e = 0; e < KL; ++e) {
-                    vset(ap, e, cvt<T>(accS[mt][kk * KL + e]));
-                    vset(as, e, cvt<T>(accP[mt][kk * KL + e]));
-                }
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    vec bd, bq;
+                for (int kk = 0; kk < 32 / KS; ++kk) {
+                    vec ap, as;
 #pragma unroll
                     for (int e = 0; e < KL; ++e) {
-                        const int qr = mt * 32 + acc_row(kk * KL + e, h);
-                        vset(bd, e, sdYt[(nt * 32 + col) * PT + qr]);
-                        vset(bq, e, sQt[(nt * 32 + col) * PT + qr]);
+                        vset(ap, e, cvt<T>(accS[mt][kk * KL + e]));
+                        vset(as, e, cvt<T>(accP[mt][kk * KL + e]));
                     }
-                    accV[nt] = E::mfma(ap, bd, accV[nt]);
-                    accK[nt] = E::mfma(as, bq, accK[nt]);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        vec bd, bq;
+#pragma unroll
+                        for (int e = 0; e < KL; ++e) {
+                            const int qr = mt * 32 + acc_row(kk * KL + e, h);
+                            vset(bd, e, sdYt[(nt * 32 + col) * PT + qr]);
+                            vset(bq, e, sQt[(nt * 32 + col) * PT + qr]);
+                        }
+                        accV[nt] = E::mfma(ap, bd, accV[nt]);
+                        accK[nt] = E::mfma(as, bq, accK[nt]);
+                    }
+                }
+            }
+
+            // dS to LDS as [query][key] so dQ can contract over all 128 keys
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                for (int a = 0; a < 16; ++a) {
+                    sdS[(mt * 32 + acc_row(a, h)) * PS + 32 * w + col] = cvt<T>(accP[mt][a]);
+                }
+            }
+            __syncthreads();
+
+            // dQ_acc[tile] += dS K  (unscaled; the convert pass applies scale)
+            for (int tt = w; tt < MT * NT; tt += 4) {
+                const int mq = tt / NT;
+                const int nd = tt - mq * NT;
+                f32x16 acc = zero16();
+#pragma unroll
+                for (int s = 0; s < BKV / KS; ++s) {
+                    const vec a = *reinterpret_cast<const vec*>(&sdS[(mq * 32 + col) * PS + s * KS + h * KL]);
+                    const vec b = *reinterpret_cast<const vec*>(&sKt[(nd * 32 + col) * PS + s * KS + h * KL]);
+                    acc = E::mfma(a, b, acc);
+                }
+#pragma unroll
+                for (int a = 0; a < 16; ++a) {
+                    const int i = q0 + mq * 32 + acc_row(a, h);
+                    if (i < L) {
+                        float* dst = p.dq_acc + (static_cast<int64_t>(n) * p.tq + it.q_start + i) * D + nd * 32 + col;
+                        unsafeAtomicAdd(dst, acc[a]);
+                    }
                 }
             }
         }
-
-        // dS to LDS as [query][key] so dQ can contract over all 128 keys
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                sdS[(mt * 32 + acc_row(a, h)) * PS + 32 * w + col] = cvt<T>(accP[mt][a]);
-            }
-        }
-        __syncthreads();
-
-        // dQ_acc[tile] += dS K  (unscaled; the convert pass applies scale)
-        for (int tt = w; tt < MT * NT; tt += 4) {
-            const int mq = tt / NT;
-            const int nd = tt - mq * NT;
-            f32x16 acc = zero16();
-#pragma unroll
-            for (int s = 0; s < BKV / KS; ++s) {
-                const vec a = *reinterpret_cast<const vec*>(&sdS[(mq * 32 + col) * PS + s * KS + h * KL]);
-                const vec b = *reinterpret_cast<const vec*>(&sKt[(nd * 32 + col) * PS + s * KS + h * KL]);
-                acc = E::mfma(a, b, acc);
-            }
-#pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                const int i = q0 + mq * 32 + acc_row(a, h);
-                if (i < L) {
-                    float* dst = p.dq_acc + (static_cast<int64_t>(n) * p.tq + it.q_start + i) * D + nd * 32 + col;
-                    unsafeAtomicAdd(dst, acc[a]);
-                }
-            }
-        }
-    }
+    }  // query heads of the group
 
     // epilogue: dK = scale * sum dS^T Q, dV = sum Pd^T dY for this wave's 32 keys
-    T* gdk = static_cast<T*>(p.dk) + static_cast<int64_t>(it.kv_start) * p.dk_st + n * p.dk_sh;
-    T* gdv = static_cast<T*>(p.dv) + static_cast<int64_t>(it.kv_start) * p.dv_st + n * p.dv_sh;
+    T* gdk = static_cast<T*>(p.dk) + static_cast<int64_t>(it.kv_start) * p.dk_st + hk * p.dk_sh;
+    T* gdv = static_cast<T*>(p.dv) + static_cast<int64_t>(it.kv_start) * p.dv_st + hk * p.dv_sh;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -506,6 +508,7 @@ hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs
     d.drop_mask = a.drop_mask;
     d.tq = a.tq;
     d.heads = a.heads;
+    d.group = a.group;
     d.mode = a.mode;
     d.pre = a.pre;
     d.nxt = a.nxt;
@@ -513,8 +516,8 @@ hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs
     d.inv_keep = a.inv_keep;
     d.scale = a.scale;
 #define FA_MAIN(T, D)                                                          \
-    return dropout ? main_t<T, D, true>(d, n_items, a.heads, stream)           \
-                   : main_t<T, D, false>(d, n_items, a.heads, stream)
+    return dropout ? main_t<T, D, true>(d, n_items, a.heads / a.group, stream)           \
+                   : main_t<T, D, false>(d, n_items, a.heads / a.group, stream)
     if (dtype != FA_F32) return hipErrorInvalidValue;  // 16-bit inputs run launch_bwd16
     if (head_dim == 128) FA_MAIN(float, 128);
     FA_MAIN(float, 64);

@@ -7,8 +7,9 @@ HIP library can both consume its output without sharing any computation.
 
 Recipe (seed = workload number unless given):
   1. lengths, drawn first from numpy.random.default_rng(seed);
-  2. Q, K, V, each standard_normal((T, N, D)) in fp64;
-  3. dY = standard_normal((T, N, D)) * dy_scale;
+  2. Q, K, V, each standard_normal((T, N, D)) in fp64 (K and V with the
+     key/value head count and V with its own head dim when those differ);
+  3. dY = standard_normal((T, N, Dv)) * dy_scale;
   4. with keep_prob < 1: for each sequence b, for each head n, a
      [Lq_b, Lkv_b] block of random() < keep_prob, concatenated in that order
      and packed least-significant-bit first into uint8;
@@ -46,6 +47,16 @@ class Workload:
     seed: int = 0
     kv_lengths: Optional[tuple] = None   # only for edge cases with Lq != Lkv
     length_draw: Optional[tuple] = None  # how the lengths were drawn (first draw of the seed)
+    kv_heads: Optional[int] = None       # key/value heads (grouped heads); None = heads
+    head_dim_v: Optional[int] = None     # V head dim; None = head_dim
+
+    @property
+    def n_kv(self) -> int:
+        return self.heads if self.kv_heads is None else self.kv_heads
+
+    @property
+    def dv(self) -> int:
+        return self.head_dim if self.head_dim_v is None else self.head_dim_v
 
     @property
     def scale(self) -> float:
@@ -155,13 +166,11 @@ def make(wl: Workload, seed: Optional[int] = None) -> Inputs:
     t = wl.tokens
     cu_q, cu_kv = wl.cu_q(), wl.cu_kv()
     tk = int(cu_kv[-1])
-    shape_q = (t, wl.heads, wl.head_dim)
-    shape_k = (tk, wl.heads, wl.head_dim)
     dt = wl.torch_dtype
-    q = _normal(rng, shape_q, dt)
-    k = _normal(rng, shape_k, dt)
-    v = _normal(rng, shape_k, dt)
-    dy = _normal(rng, shape_q, dt, wl.dy_scale)
+    q = _normal(rng, (t, wl.heads, wl.head_dim), dt)
+    k = _normal(rng, (tk, wl.n_kv, wl.head_dim), dt)
+    v = _normal(rng, (tk, wl.n_kv, wl.dv), dt)
+    dy = _normal(rng, (t, wl.heads, wl.dv), dt, wl.dy_scale)
     drop = None
     if wl.keep_prob < 1.0:
         lq = np.diff(cu_q).tolist()
