@@ -86,11 +86,14 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BAND = 2 };
 /*
  * fa_varlen_bwd -- dQ, dK, dV of varlen attention.
  *
- * q, dy, y          [Tq, N, D] inputs (y is the forward output attentionIn).
- * k, v              [Tkv, Nkv, D] inputs.  Nkv divides N (grouped heads,
- *                   constraints section of the page): query head n reads
- *                   key/value head n / (N / Nkv), and dk, dv of a shared
- *                   head hold the sum over the query heads that read it.
+ * q                 [Tq, N, Dk] input.
+ * dy, y             [Tq, N, Dv] inputs (y is the forward output attentionIn).
+ * k, v              [Tkv, Nkv, Dk] and [Tkv, Nkv, Dv] inputs.  Nkv divides N
+ *                   (grouped heads, constraints section of the page): query
+ *                   head n reads key/value head n / (N / Nkv), and dk, dv of
+ *                   a shared head hold the sum over the query heads that read
+ *                   it.  Dv <= Dk (parameter table: V's head dim may be the
+ *                   smaller one).
  * softmax_max/sum   [N, Tq, 8] contiguous fp32 device arrays: the forward's
  *                   row max and row sum of exp, replicated over the last
  *                   axis (element 0 is read).  Rows with no admitted key are
@@ -109,9 +112,9 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BAND = 2 };
  * dq, dk, dv        outputs, same dtype and shapes as q, k, v.
  * stream            hipStream_t (NULL = the null stream).
  *
- * Supported: all tensors one dtype (FA_F32, FA_F16 or FA_BF16); D in {64,128};
- * v head_dim == q head_dim.  Other values the page allows (Dv < Dk, other D)
- * return FA_ERR_UNSUPPORTED.
+ * Supported: all tensors one dtype (FA_F32, FA_F16 or FA_BF16); head dims
+ * (Dk, Dv) in {(128, 128), (128, 64), (64, 64)}.  Other head dims the page
+ * allows return FA_ERR_UNSUPPORTED.
  * Tq == 0 returns FA_OK with nothing launched.
  *
  * Calls on different streams share one library workspace per device and

@@ -115,8 +115,12 @@ def test_unsupported_variants():
     # head dims outside {64, 128}
     args = {n: _t(10, dim=96) for n in ("q", "k", "v", "dy", "y", "dq", "dk", "dv")}
     assert _call(**args)[0] == B.FA_ERR_UNSUPPORTED
-    # v head dim smaller than k's
-    assert _call(v=_t(10, dim=32), dv=_t(10, dim=32))[0] == B.FA_ERR_UNSUPPORTED
+    # v head dim smaller than k's, in a pair no kernel is built for: (64, 32)
+    assert _call(v=_t(10, dim=32), dv=_t(10, dim=32), dy=_t(10, dim=32), y=_t(10, dim=32))[0] == B.FA_ERR_UNSUPPORTED
+    # (128, 32) likewise
+    args = {n: _t(10, dim=128) for n in ("q", "k", "dq", "dk")}
+    args.update({n: _t(10, dim=32) for n in ("v", "dv", "dy", "y")})
+    assert _call(**args)[0] == B.FA_ERR_UNSUPPORTED
     # misaligned base address
     assert _call(q=_t(10, data=FAKE + 2))[0] == B.FA_ERR_UNSUPPORTED
 
@@ -134,6 +138,25 @@ def test_grouped_heads_validation():
     args = {n: _t(0, heads=4, data=0) for n in ("q", "dy", "y", "dq")}
     args.update({n: _t(0, heads=2, data=0) for n in ("k", "v", "dk", "dv")})
     st, msg = _call(head_num=4, cu_q=(0, 0), cu_kv=(0, 0), **args)
+    assert st == B.FA_OK, msg
+
+
+def test_narrow_v_validation():
+    # dy and y take v's head dim; dv must match v
+    args = {n: _t(10, dim=128) for n in ("q", "k", "dq", "dk")}
+    args.update({n: _t(10, dim=64) for n in ("v", "dv", "y")})
+    assert _call(dy=_t(10, dim=128), **args)[0] == B.FA_ERR_INVALID
+    args = {n: _t(10, dim=128) for n in ("q", "k", "dq", "dk", "dv")}
+    args.update({n: _t(10, dim=64) for n in ("v", "dy", "y")})
+    assert _call(**args)[0] == B.FA_ERR_INVALID
+    # v wider than k is outside the page's constraints
+    args = {n: _t(10, dim=64) for n in ("q", "k", "dq", "dk")}
+    args.update({n: _t(10, dim=128) for n in ("v", "dv", "dy", "y")})
+    assert _call(**args)[0] == B.FA_ERR_INVALID
+    # (128, 64) with no query tokens: validated, then no device work
+    args = {n: _t(0, dim=128, data=0) for n in ("q", "k", "dq", "dk")}
+    args.update({n: _t(0, dim=64, data=0) for n in ("v", "dv", "dy", "y")})
+    st, msg = _call(cu_q=(0, 0), cu_kv=(0, 0), **args)
     assert st == B.FA_OK, msg
 
 
@@ -207,6 +230,15 @@ def test_forward_invalid_arguments(kwargs, status):
     st, msg = _fwd(**kwargs)
     assert st == status, msg
     assert msg
+
+
+def test_forward_narrow_v():
+    # y takes v's head dim
+    q, k = _t(10, dim=128), _t(10, dim=128)
+    assert _fwd(q=q, k=k, v=_t(10, dim=64), y=_t(10, dim=128))[0] == B.FA_ERR_INVALID
+    assert _fwd(q=q, k=k, v=_t(10, dim=32), y=_t(10, dim=32))[0] == B.FA_ERR_UNSUPPORTED
+    st, msg = _fwd(q=_t(0, dim=128), k=k, v=_t(10, dim=64), y=_t(0, dim=64), cu_q=(0, 0), smax=None, ssum=None)
+    assert st == B.FA_OK, msg
 
 
 def test_forward_empty_input_is_ok():

@@ -254,9 +254,9 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         set_error("head dims must satisfy qD == kD >= vD");
         return FA_ERR_INVALID;
     }
-    if (dy->tokens != q->tokens || dy->heads != q->heads || dy->head_dim != q->head_dim ||
-        y->tokens != q->tokens || y->heads != q->heads || y->head_dim != q->head_dim) {
-        set_error("dy and y must have the shape of q");
+    if (dy->tokens != q->tokens || dy->heads != q->heads || dy->head_dim != v->head_dim ||
+        y->tokens != q->tokens || y->heads != q->heads || y->head_dim != v->head_dim) {
+        set_error("dy and y must have q's tokens and heads and v's head_dim");
         return FA_ERR_INVALID;
     }
     if (dq->tokens != q->tokens || dq->heads != q->heads || dq->head_dim != q->head_dim ||
@@ -287,12 +287,8 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         return FA_ERR_INVALID;
     }
     // ---- allowed by the page, not built ----
-    if (v->head_dim != k->head_dim) {
-        set_error("v head_dim < k head_dim is not supported");
-        return FA_ERR_UNSUPPORTED;
-    }
-    if (q->head_dim != 64 && q->head_dim != 128) {
-        set_error("head_dim must be 64 or 128");
+    if (!fa::head_dims_supported(q->head_dim, v->head_dim)) {
+        set_error("head dims (q/k, v) must be (128, 128), (128, 64) or (64, 64)");
         return FA_ERR_UNSUPPORTED;
     }
     for (int i = 0; i < 8; ++i) {
@@ -305,6 +301,7 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     const int64_t tq = q->tokens;
     const int64_t heads = q->heads;
     const int d = static_cast<int>(q->head_dim);
+    const int dv_dim = static_cast<int>(v->head_dim);
     if (tq == 0) return FA_OK;  // empty input: nothing to compute
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -391,7 +388,7 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     fa::TensorArg tdy{dy->data, dy->stride_t, dy->stride_h};
     fa::TensorArg ty{y->data, y->stride_t, y->stride_h};
     e = timed(0, s, [&] {
-        return fa::launch_preprocess(dtype, d, tdy, ty, softmax_max, softmax_sum, ws.rowstat,
+        return fa::launch_preprocess(dtype, dv_dim, d, tdy, ty, softmax_max, softmax_sum, ws.rowstat,
                                      wide ? ws.dq_acc : nullptr, tq, heads, s);
     });
     if (e != hipSuccess) return runtime_error("preprocess launch", e);
@@ -442,9 +439,9 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         a.exp_scale = exp_scale;
         a.inv_keep = inv_keep;
         a.scale = static_cast<float>(scale);
-        e = timed(1, s, [&] { return fa::launch_dkdv16(dtype, d, keep_prob < 1.0, a, ws.n_items, s); });
+        e = timed(1, s, [&] { return fa::launch_dkdv16(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_items, s); });
         if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
-        e = timed(3, s, [&] { return fa::launch_dq16(dtype, d, keep_prob < 1.0, a, ws.n_q_items, s); });
+        e = timed(3, s, [&] { return fa::launch_dq16(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_q_items, s); });
         if (e != hipSuccess) return runtime_error("dQ kernel launch", e);
         return FA_OK;
     }
@@ -474,7 +471,7 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         a.exp_scale = exp_scale;
         a.inv_keep = inv_keep;
         a.scale = static_cast<float>(scale);
-        e = timed(1, s, [&] { return fa::launch_main(dtype, d, keep_prob < 1.0, a, ws.n_items, s); });
+        e = timed(1, s, [&] { return fa::launch_main(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_items, s); });
         if (e != hipSuccess) return runtime_error("main kernel launch", e);
     }
 
@@ -570,12 +567,8 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         set_error("cu_seqlens must end at the token counts of q and k");
         return FA_ERR_INVALID;
     }
-    if (v->head_dim != k->head_dim) {
-        set_error("v head_dim < k head_dim is not supported");
-        return FA_ERR_UNSUPPORTED;
-    }
-    if (q->head_dim != 64 && q->head_dim != 128) {
-        set_error("head_dim must be 64 or 128");
+    if (!fa::head_dims_supported(q->head_dim, v->head_dim)) {
+        set_error("head dims (q/k, v) must be (128, 128), (128, 64) or (64, 64)");
         return FA_ERR_UNSUPPORTED;
     }
     for (int i = 0; i < 4; ++i) {
@@ -604,6 +597,7 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     const int64_t tq = q->tokens;
     const int64_t heads = q->heads;
     const int d = static_cast<int>(q->head_dim);
+    const int dv_dim = static_cast<int>(v->head_dim);
     if (tq == 0) return FA_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -687,8 +681,8 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     a.exp_scale = static_cast<float>(scale * 1.4426950408889634);
     a.inv_keep = static_cast<float>(1.0 / keep_prob);
     e = timed(4, s, [&] {
-        return wide ? fa::launch_fwd32(d, keep_prob < 1.0, a, ws.n_fwd_items, s)
-                    : fa::launch_fwd16(dtype, d, keep_prob < 1.0, a, ws.n_fwd_items, s);
+        return wide ? fa::launch_fwd32(d, dv_dim, keep_prob < 1.0, a, ws.n_fwd_items, s)
+                    : fa::launch_fwd16(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_fwd_items, s);
     });
     if (e != hipSuccess) return runtime_error("forward kernel launch", e);
     return FA_OK;

@@ -55,27 +55,50 @@ namespace fa {
 //   tile (buffer b) only.  (buffer indices mod 3)
 enum StepKind { kStepA = 0, kStepB = 1, kStepFirst = 2, kStepLast = 3 };
 
-template <typename T, int D, bool DROP>
+// Order of two MFMA chains of NA and NB instructions over the slots of a step: slot j runs
+// chain A (j even) or chain B (j odd) while both last, then the rest of the longer one.
+// index(j) is the position of slot j's instruction within its chain.
+template <int NA, int NB>
+struct Interleave {
+    static constexpr int M = NA < NB ? NA : NB;
+    static constexpr bool is_a(int j) { return j < 2 * M ? j % 2 == 0 : NA > NB; }
+    static constexpr int index(int j) { return j < 2 * M ? j / 2 : M + (j - 2 * M); }
+};
+
+// Slots of the softmax-gradient work of element a (16 per step) among the NOPS slots: P at
+// p_slot(a), dS at d_slot(a) (the same slot when NOPS == 16, P first).
+constexpr int p_slot(int a, int nops) { return a * nops / 16; }
+constexpr int d_slot(int a, int nops) { return (a * nops + nops / 2) / 16; }
+
+template <typename T, int DK, int DV, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     using vec = typename Op16<T>::vec;
     constexpr int NW = 4;
     constexpr int BQ = FA16_DKDV_TILE_Q;  // query tile rows (64)
     constexpr int BKV = FA16_DKDV_BLOCK;  // keys per workgroup
-    constexpr int NT = D / 32;            // 32-column tiles of dK / dV
-    constexpr int NX = D / 8;             // MFMAs per step for S and dP (as many for dV and dK)
+    constexpr int NTK = DK / 32;          // 32-column tiles of dK
+    constexpr int NTV = DV / 32;          // ... of dV
+    constexpr int SK = DK / 16;           // MFMAs per step for S (as many for dK)
+    constexpr int SV = DV / 16;           // ... for dP (as many for dV)
+    constexpr int NX = SK + SV;           // X MFMAs per step (as many Y MFMAs)
     constexpr int NOPS = 2 * NX;          // slots per step: X and Y MFMAs alternate
-    constexpr int EPS = NOPS / 16;        // slots per softmax element (16 elements per step)
     constexpr int LA = 4;                 // LDS reads run LA slots ahead of their MFMA
     constexpr int NB = 3;                 // query tile buffers
-    constexpr int TILE = BQ * D;
-    constexpr int TI = TILE / 8 / 64;     // DMA instructions per query tile and tensor
-    constexpr int TW = TI / NW;           // ... per wave
-    static_assert(BQ == 64 && BKV == 32 * NW && TI % NW == 0 && NOPS >= 16 && LA % 2 == 0 && LA < NOPS,
-                  "tile shape");
+    constexpr int TILEQ = BQ * DK;
+    constexpr int TILED = BQ * DV;
+    constexpr int TWQ = TILEQ / 8 / 64 / NW;  // DMA instructions per wave and Q tile
+    constexpr int TWD = TILED / 8 / 64 / NW;  // ... and dY tile
+    using XS = Interleave<SK, SV>;        // X slots: S (chain A) and dP (chain B)
+    using YS = Interleave<SV, SK>;        // Y slots: dV (chain A) and dK (chain B)
+    static_assert(BQ == 64 && BKV == 32 * NW && (TILED / 8 / 64) % NW == 0 && NOPS >= 16 && LA % 2 == 0 &&
+                  LA < NOPS && DV <= DK, "tile shape");
 
-    // buffer b: Q tile at sBuf[b][0], dY tile at sBuf[b][1]
-    __shared__ __attribute__((aligned(16))) T sBuf[NB][2][TILE];
+    // buffer b: Q tile at sBuf[b], dY tile at sBuf[b] + TILEQ (one array, so that the reads of
+    // both tiles share one base address and differ by an immediate offset)
+    __shared__ __attribute__((aligned(16))) T sBuf[NB][TILEQ + TILED];
     __shared__ __attribute__((aligned(16))) float2 sSt[NB][BQ];
+    auto qtile = [&](int b) -> T* { return sBuf[b]; };
+    auto dtile = [&](int b) -> T* { return sBuf[b] + TILEQ; };
 
     const fa_work_item_t it = p.items_kv[blockIdx.x];
     const int hk = blockIdx.y;  // key/value head; query heads hk * group .. hk * group + group - 1 read it
@@ -91,45 +114,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     const int tb = it.tile_begin;
     const int te = it.tile_end;
 
-    f32x16 accK[NT];
-    f32x16 accV[NT];
+    f32x16 accK[NTK];
+    f32x16 accV[NTV];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        accK[i] = zero16();
-        accV[i] = zero16();
-    }
+    for (int i = 0; i < NTK; ++i) accK[i] = zero16();
+#pragma unroll
+    for (int i = 0; i < NTV; ++i) accV[i] = zero16();
 
     if (tb < te) {
-        LdsOffsets<D> lo_;
-        lo_.init(lane);
+        LdsOffsets<DK> loQ;
+        loQ.init(lane);
+        LdsOffsets<DV> loD_;
+        if constexpr (DK != DV) loD_.init(lane);
+        const LdsOffsets<DV>& loD = offsets_for(loQ, loD_);
 
         // the query head being walked (set per head below) and its tensors
         int n = hk * p.group;
         const T* gq = nullptr;
         const T* gdy = nullptr;
         const float2* gstat = nullptr;
-        int qoff[TW];
-        int dyoff[TW];
-        // wave w copies 1 KiB chunks w*TW .. w*TW + TW - 1 of each tile (one run)
+        int qoff[TWQ];
+        int dyoff[TWD];
+        // wave w copies 1 KiB chunks w*TWQ .. w*TWQ + TWQ - 1 of each Q tile (one run), and
+        // likewise TWD chunks of each dY tile
 #pragma unroll
-        for (int u = 0; u < TW; ++u) {
-            qoff[u] = dma_offset<D>(w * TW + u, lane, p.q_st) - 1024 * u;
-            dyoff[u] = dma_offset<D>(w * TW + u, lane, p.dy_st) - 1024 * u;
-        }
+        for (int u = 0; u < TWQ; ++u) qoff[u] = dma_offset<DK>(w * TWQ + u, lane, p.q_st) - 1024 * u;
+#pragma unroll
+        for (int u = 0; u < TWD; ++u) dyoff[u] = dma_offset<DV>(w * TWD + u, lane, p.dy_st) - 1024 * u;
 
         // this lane's K and V rows: B operands of S = Q K^T and dP = dY V^T
-        vec kreg[D / 16];
-        vec vreg[D / 16];
+        vec kreg[SK];
+        vec vreg[SV];
         {
             const bool ok = jw < K;
             const int64_t row = it.kv_start + (ok ? jw : 0);
             const vec* kr = reinterpret_cast<const vec*>(static_cast<const T*>(p.k) + row * p.k_st + hk * p.k_sh);
             const vec* vr = reinterpret_cast<const vec*>(static_cast<const T*>(p.v) + row * p.v_st + hk * p.v_sh);
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
+            for (int s = 0; s < SV; ++s) {
                 kreg[s] = ok ? kr[2 * s + h] : vec{};
                 vreg[s] = ok ? vr[2 * s + h] : vec{};
             }
+#pragma unroll
+            for (int s = SV; s < SK; ++s) kreg[s] = ok ? kr[2 * s + h] : vec{};
         }
 
         // Query rows this lane's key admits, [lo_row, hi_row]; the element of step rows q0s..
@@ -160,9 +187,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             const int q0 = t * BQ;
             const i32x4 rq = buffer_desc(gq + static_cast<int64_t>(q0) * p.q_st, tile_bytes(L - q0, BQ, p.q_st));
             const i32x4 rd = buffer_desc(gdy + static_cast<int64_t>(q0) * p.dy_st, tile_bytes(L - q0, BQ, p.dy_st));
-            const uint32_t mq = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sBuf[b][0] + w * TW * 512)));
-            const uint32_t md = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sBuf[b][1] + w * TW * 512)));
-            dma_pair<TW>(__builtin_amdgcn_readfirstlane(mq), rq, qoff, __builtin_amdgcn_readfirstlane(md), rd, dyoff);
+            const uint32_t mq = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(qtile(b) + w * TWQ * 512)));
+            const uint32_t md = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(dtile(b) + w * TWD * 512)));
+            dma_pair<TWQ, TWD>(__builtin_amdgcn_readfirstlane(mq), rq, qoff, __builtin_amdgcn_readfirstlane(md), rd,
+                               dyoff);
             if (w == NW - 1 && lane < BQ / 2) {
                 const i32x4 rs = buffer_desc(gstat + q0, q0 < L ? static_cast<uint32_t>(min(L - q0, BQ) * 8) : 0u);
                 dma16_async(sSt[b], rs, lane * 16);
@@ -182,19 +210,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             if (kind == kStepFirst) return {0, 0, 0, 0, 0, 0};
             return {b, 0, b, 0, b, 1};  // last
         };
-        // operand of slot k of a step: k even -> X (row read of Q or dY), k odd -> Y
-        // (transposing read of dY or Q)
+        // operand of slot k of a step: k even -> X (row read of Q for S, of dY for dP), k odd ->
+        // Y (transposing read of dY for dV, of Q for dK)
         auto read_op = [&](const Where& wh, auto kc) -> vec {
             constexpr int k = decltype(kc)::value;
             constexpr int j = k / 2;
             if constexpr (k % 2 == 0) {
-                const T* base = sBuf[wh.xb][j % 2] + 32 * wh.xm * D;
-                return lds_row<vec>(base, lo_.row[j / 2]);
+                constexpr int s = XS::index(j);
+                if constexpr (XS::is_a(j)) {
+                    return lds_row<vec>(qtile(wh.xb) + 32 * wh.xm * DK, loQ.row[s]);
+                } else {
+                    return lds_row<vec>(dtile(wh.xb) + 32 * wh.xm * DV, loD.row[s]);
+                }
             } else {
-                constexpr int kk = j / (2 * NT);
-                constexpr int nt = (j / 2) % NT;
-                const T* base = sBuf[wh.yb][1 - j % 2] + (32 * wh.ym + 16 * kk) * D;
-                return lds_tr<vec>(base, lo_.tr[nt][0], lo_.tr[nt][1]);
+                constexpr int i = YS::index(j);
+                if constexpr (YS::is_a(j)) {
+                    constexpr int kk = i / NTV;
+                    constexpr int nt = i % NTV;
+                    return lds_tr<vec>(dtile(wh.yb) + (32 * wh.ym + 16 * kk) * DV, loD.tr[nt][0], loD.tr[nt][1]);
+                } else {
+                    constexpr int kk = i / NTK;
+                    constexpr int nt = i % NTK;
+                    return lds_tr<vec>(qtile(wh.yb) + (32 * wh.ym + 16 * kk) * DK, loQ.tr[nt][0], loQ.tr[nt][1]);
+                }
             }
         };
         // statistics {delta, beta} of rows 32*sm + 8g + 4h + 0..3
@@ -263,10 +301,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 // ---- the MFMA of slot k
                 if constexpr (k % 2 == 0) {
                     if constexpr (HX) {
-                        constexpr int s = j / 2;
+                        constexpr int s = XS::index(j);
                         vec a = opr[k];
                         pin(a);
-                        if constexpr (j % 2 == 0) {
+                        if constexpr (XS::is_a(j)) {
                             sN = Op16<T>::mfma(a, kreg[s], s == 0 ? zero16() : sN);
                             pin(sN);
                         } else {
@@ -276,20 +314,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     }
                 } else {
                     if constexpr (HY) {
-                        constexpr int kk = j / (2 * NT);
-                        constexpr int nt = (j / 2) % NT;
-                        if constexpr (j % 2 == 0) {
-                            MfmaAccV<T>::run(accV[nt], pkY[kk], opr[k]);
+                        constexpr int i = YS::index(j);
+                        if constexpr (YS::is_a(j)) {
+                            MfmaAccV<T>::run(accV[i % NTV], pkY[i / NTV], opr[k]);
                         } else {
-                            MfmaAccV<T>::run(accK[nt], dsY[kk], opr[k]);
+                            MfmaAccV<T>::run(accK[i % NTK], dsY[i / NTK], opr[k]);
                         }
                     }
                 }
-                // ---- softmax gradient of element a = k / EPS: P in part one, dS in part two
-                if constexpr (HS) {
-                    constexpr int a = k / EPS;
+                // ---- softmax gradient of the elements whose parts fall in slot k: P in part
+                // one, dS in part two
+                if constexpr (HS) static_for<0, 16>([&](auto ac) {
+                    constexpr int a = decltype(ac)::value;
                     constexpr int cc = 8 * (a / 4) + (a % 4);
-                    if constexpr (k % EPS == 0) {
+                    if constexpr (p_slot(a, NOPS) == k) {
                         float x = sC[a];
                         pin(x);
                         const float bt = stC[a / 4][(a % 4) / 2][2 * (a % 2) + 1];
@@ -302,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                         }
                         pin(pv[a]);
                     }
-                    if constexpr (k % EPS == EPS - 1) {
+                    if constexpr (d_slot(a, NOPS) == k) {
                         float y = pC[a];
                         pin(y);
                         const float dl = stC[a / 4][(a % 4) / 2][2 * (a % 2)];
@@ -322,7 +360,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                             pin(dsw[a / 8][(a % 8) / 2]);
                         }
                     }
-                }
+                });
                 // ---- tile barrier: tile t + 1 has landed and every wave is done with the buffer
                 // of tile t - 1, which then receives tile t + 2
                 if constexpr (KIND == kStepA && k == NOPS - LA) {
@@ -334,7 +372,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 constexpr int kr = k + LA;
                 if constexpr (kr < NOPS) {
                     if constexpr ((kr % 2 == 0 && HX) || (kr % 2 == 1 && HY)) opr[kr] = read_op(wh, IC<kr>{});
-                    if constexpr (HS && kr % (4 * EPS) == 0) read_stats(wh, kr / (4 * EPS), stC[kr / (4 * EPS)]);
+                    // statistics of elements 4g .. 4g + 3, LA slots before the first of them (group 0
+                    // is read during the step before)
+                    static_for<1, 4>([&](auto gc) {
+                        constexpr int g = decltype(gc)::value;
+                        if constexpr (HS && kr == p_slot(4 * g, NOPS)) read_stats(wh, g, stC[g]);
+                    });
                 } else if constexpr (KIND != kStepLast) {
                     nopr[kr - NOPS] = read_op(nw, IC<kr - NOPS>{});
                     if constexpr (kr == NOPS && (NKIND == kStepA || NKIND == kStepB)) read_stats(nw, 0, stN);
@@ -417,7 +460,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             // the step before the first, whose packed P / dS are zero)
             issue(tb, 0);
             if (tb + 1 < te) issue(tb + 1, 1);
-            for (int i = threadIdx.x; i < 2 * TILE / 8; i += 64 * NW) reinterpret_cast<vec*>(sBuf[2][0])[i] = vec{};
+            for (int i = threadIdx.x; i < (TILEQ + TILED) / 8; i += 64 * NW) reinterpret_cast<vec*>(sBuf[2])[i] = vec{};
             wait_dma();
             __syncthreads();
             {
@@ -452,20 +495,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     // the accumulators were last written by MFMAs the compiler does not see: wait them out
     // before any other instruction reads them
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(accK[nt]), "+a"(accV[nt]));
+    for (int nt = 0; nt < NTK; ++nt) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(accK[nt]));
+#pragma unroll
+    for (int nt = 0; nt < NTV; ++nt) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(accV[nt]));
 
     // epilogue: dK = scale * sum dS^T Q, dV = sum Pd^T dY; the lane holds column nt*32 + col
     // of key rows 8g + 4h + r
     T* gdk = static_cast<T*>(p.dk) + static_cast<int64_t>(it.kv_start) * p.dk_st + hk * p.dk_sh;
     T* gdv = static_cast<T*>(p.dv) + static_cast<int64_t>(it.kv_start) * p.dv_st + hk * p.dv_sh;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NTK; ++nt) {
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
             const int j = j0 + 32 * w + acc_row(a, h);
             if (j < K) {
                 gdk[static_cast<int64_t>(j) * p.dk_st + nt * 32 + col] = static_cast<T>(accK[nt][a] * p.scale);
-                gdv[static_cast<int64_t>(j) * p.dv_st + nt * 32 + col] = static_cast<T>(accV[nt][a]);
+                if (nt < NTV) gdv[static_cast<int64_t>(j) * p.dv_st + nt * 32 + col] = static_cast<T>(accV[nt][a]);
             }
         }
     }
@@ -481,19 +526,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 //   dS^T = Ps (dP Z/kp - D)      (each lane holds one query: its D and beta are scalars)
 //   dQ^T += K^T dS^T             (A = transposing reads of K, B = dS^T straight from registers)
 
-template <typename T, int D, bool DROP>
+template <typename T, int DK, int DV, bool DROP>
 __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     using vec = typename Op16<T>::vec;
     constexpr int NW = 8;
     constexpr int BQ = FA16_DQ_BLOCK;    // queries per workgroup
     constexpr int BK = FA16_DQ_TILE_K;   // key tile rows (64): two steps of 32
-    constexpr int ND = D / 32;           // 32-row head-dim tiles of dQ^T
-    constexpr int TI = BK * D / 8 / 64;  // DMA instructions per key tile and tensor
-    constexpr int TW = TI / NW;          // ... per wave
-    static_assert(BQ == 32 * NW && BK == 64 && TI % NW == 0, "tile shape");
+    constexpr int ND = DK / 32;                 // 32-row head-dim tiles of dQ^T
+    constexpr int SK = DK / 16;                 // MFMAs per step for S^T
+    constexpr int SV = DV / 16;                 // ... for dP^T
+    constexpr int TWK = BK * DK / 8 / 64 / NW;  // DMA instructions per wave and key tile
+    constexpr int TWV = BK * DV / 8 / 64 / NW;  // ... and value tile
+    static_assert(BQ == 32 * NW && BK == 64 && (BK * DV / 8 / 64) % NW == 0 && DV <= DK, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
-    __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
+    __shared__ __attribute__((aligned(16))) T sK[2][BK * DK];
+    __shared__ __attribute__((aligned(16))) T sV[2][BK * DV];
 
     const fa_work_item_t it = p.items_q[blockIdx.x];
     const int n = blockIdx.y;
@@ -507,32 +554,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     const int i0 = it.block * BQ + 32 * w;  // first query of this wave
     const int qi = i0 + col;                // this lane's query
 
-    LdsOffsets<D> lo_;
-    lo_.init(lane);
+    LdsOffsets<DK> loK;
+    loK.init(lane);
+    LdsOffsets<DV> loV_;
+    if constexpr (DK != DV) loV_.init(lane);
+    const LdsOffsets<DV>& loV = offsets_for(loK, loV_);
 
     const int hk = n / p.group;  // the key/value head this query head reads
     const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh;
     const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + hk * p.v_sh;
-    // wave w copies 1 KiB chunks w*TW .. w*TW + TW - 1 of each key tile (one run)
-    int koff[TW];
-    int voff[TW];
+    // wave w copies 1 KiB chunks w*TWK .. w*TWK + TWK - 1 of each key tile (one run), and
+    // likewise TWV chunks of each value tile
+    int koff[TWK];
+    int voff[TWV];
 #pragma unroll
-    for (int u = 0; u < TW; ++u) {
-        koff[u] = dma_offset<D>(w * TW + u, lane, p.k_st) - 1024 * u;
-        voff[u] = dma_offset<D>(w * TW + u, lane, p.v_st) - 1024 * u;
-    }
+    for (int u = 0; u < TWK; ++u) koff[u] = dma_offset<DK>(w * TWK + u, lane, p.k_st) - 1024 * u;
+#pragma unroll
+    for (int u = 0; u < TWV; ++u) voff[u] = dma_offset<DV>(w * TWV + u, lane, p.v_st) - 1024 * u;
     auto issue = [&](int kt, int b) {
         const int k0 = kt * BK;
         const i32x4 rk = buffer_desc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st));
         const i32x4 rv = buffer_desc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st));
-        const uint32_t mk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TW * 512)));
-        const uint32_t mv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TW * 512)));
-        dma_pair<TW>(__builtin_amdgcn_readfirstlane(mk), rk, koff, __builtin_amdgcn_readfirstlane(mv), rv, voff);
+        const uint32_t mk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * 512)));
+        const uint32_t mv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * 512)));
+        dma_pair<TWK, TWV>(__builtin_amdgcn_readfirstlane(mk), rk, koff, __builtin_amdgcn_readfirstlane(mv), rv, voff);
     };
 
     // this lane's Q and dY rows (B operands of S^T = K Q^T and dP^T = V dY^T) and statistics
-    vec qreg[D / 16];
-    vec dyreg[D / 16];
+    vec qreg[SK];
+    vec dyreg[SV];
     float delta = 0.f;
     float beta = 0.f;
     {
@@ -541,10 +591,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         const vec* qr = reinterpret_cast<const vec*>(static_cast<const T*>(p.q) + row * p.q_st + n * p.q_sh);
         const vec* dr = reinterpret_cast<const vec*>(static_cast<const T*>(p.dy) + row * p.dy_st + n * p.dy_sh);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
+        for (int s = 0; s < SK; ++s) {
             qreg[s] = ok ? qr[2 * s + h] : vec{};
+            asm volatile("" : "+a"(qreg[s]));
+        }
+#pragma unroll
+        for (int s = 0; s < SV; ++s) {
             dyreg[s] = ok ? dr[2 * s + h] : vec{};
-            asm volatile("" : "+a"(qreg[s]), "+a"(dyreg[s]));
+            asm volatile("" : "+a"(dyreg[s]));
         }
         if (ok) {
             const float2 st = p.rowstat[static_cast<int64_t>(n) * p.tq + it.q_start + qi];
@@ -593,12 +647,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         f32x16 accS = zero16();
         f32x16 accP = zero16();
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const vec ak = lds_row<vec>(cK, lo_.row[s]);
-            const vec av = lds_row<vec>(cV, lo_.row[s]);
+        for (int s = 0; s < SV; ++s) {
+            const vec ak = lds_row<vec>(cK, loK.row[s]);
+            const vec av = lds_row<vec>(cV, loV.row[s]);
             accS = Op16<T>::mfma(ak, qreg[s], accS);
             accP = Op16<T>::mfma(av, dyreg[s], accP);
         }
+#pragma unroll
+        for (int s = SV; s < SK; ++s) accS = Op16<T>::mfma(lds_row<vec>(cK, loK.row[s]), qreg[s], accS);
         // dS^T = Ps (dP Z/kp - D); element (key k0s + 4h + cc(a), query qi)
         const bool full = wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
         uint32_t dsw[2][4];
@@ -641,7 +697,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             const vec bs = __builtin_bit_cast(vec, make_uint4(dsw[kk][0], dsw[kk][1], dsw[kk][2], dsw[kk][3]));
 #pragma unroll
             for (int nd = 0; nd < ND; ++nd) {
-                const vec ak = lds_tr<vec>(cK + 16 * kk * D, lo_.tr[nd][0], lo_.tr[nd][1]);
+                const vec ak = lds_tr<vec>(cK + 16 * kk * DK, loK.tr[nd][0], loK.tr[nd][1]);
                 accQ[nd] = Op16<T>::mfma(ak, bs, accQ[nd]);
             }
         }
@@ -654,7 +710,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         __syncthreads();  // tile kt is in buffer b; every wave is done with buffer b ^ 1
         if (kt + 1 < it.tile_end) issue(kt + 1, b ^ 1);
         kstep(sK[b], sV[b], kt * BK);
-        kstep(sK[b] + 32 * D, sV[b] + 32 * D, kt * BK + 32);
+        kstep(sK[b] + 32 * DK, sV[b] + 32 * DV, kt * BK + 32);
         b ^= 1;
     }
 
@@ -676,38 +732,43 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 
 // ------------------------------------------------------------------------------------------------
 
-template <typename T, int D, bool DROP>
+template <typename T, int DK, int DV, bool DROP>
 static hipError_t launch_dkdv_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
-    bwd_dkdv16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads / a.group)), dim3(256), 0,
-                                    stream>>>(a);
+    bwd_dkdv16_kernel<T, DK, DV, DROP>
+        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads / a.group)), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool DROP>
+template <typename T, int DK, int DV, bool DROP>
 static hipError_t launch_dq_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
-    bwd_dq16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0,
-                                  stream>>>(a);
+    bwd_dq16_kernel<T, DK, DV, DROP>
+        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-#define FA_DISPATCH16(FN)                                                                        \
-    if (n_items <= 0) return hipSuccess;                                                         \
-    if (dtype == FA_BF16) {                                                                      \
-        if (head_dim == 128)                                                                     \
-            return dropout ? FN<__bf16, 128, true>(a, n_items, stream) : FN<__bf16, 128, false>(a, n_items, stream); \
-        return dropout ? FN<__bf16, 64, true>(a, n_items, stream) : FN<__bf16, 64, false>(a, n_items, stream);       \
-    }                                                                                            \
-    if (head_dim == 128)                                                                         \
-        return dropout ? FN<_Float16, 128, true>(a, n_items, stream) : FN<_Float16, 128, false>(a, n_items, stream); \
-    return dropout ? FN<_Float16, 64, true>(a, n_items, stream) : FN<_Float16, 64, false>(a, n_items, stream)
+// dtype x head dims (Q/K, V) in {(128, 128), (128, 64), (64, 64)} x dropout
+#define FA_DISPATCH16(FN)                                                                             \
+    if (n_items <= 0) return hipSuccess;                                                              \
+    auto pick = [&](auto tag) -> hipError_t {                                                         \
+        using T = typename decltype(tag)::type;                                                       \
+        if (head_dim_k == 128 && head_dim_v == 128)                                                   \
+            return dropout ? FN<T, 128, 128, true>(a, n_items, stream) : FN<T, 128, 128, false>(a, n_items, stream); \
+        if (head_dim_k == 128 && head_dim_v == 64)                                                    \
+            return dropout ? FN<T, 128, 64, true>(a, n_items, stream) : FN<T, 128, 64, false>(a, n_items, stream);   \
+        if (head_dim_k == 64 && head_dim_v == 64)                                                     \
+            return dropout ? FN<T, 64, 64, true>(a, n_items, stream) : FN<T, 64, 64, false>(a, n_items, stream);     \
+        return hipErrorInvalidValue;                                                                  \
+    };                                                                                                \
+    if (dtype == FA_BF16) return pick(TypeTag<__bf16>{});                                  \
+    return pick(TypeTag<_Float16>{})
 
-hipError_t launch_dkdv16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
-                         hipStream_t stream) {
+hipError_t launch_dkdv16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const Bwd16Args& a,
+                         int64_t n_items, hipStream_t stream) {
     FA_DISPATCH16(launch_dkdv_t);
 }
 
-hipError_t launch_dq16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
-                       hipStream_t stream) {
+hipError_t launch_dq16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const Bwd16Args& a,
+                       int64_t n_items, hipStream_t stream) {
     FA_DISPATCH16(launch_dq_t);
 }
 

@@ -113,14 +113,55 @@ __device__ __forceinline__ void dma16_async(T* lds, const i32x4& desc, int voff)
         : "memory");
 }
 
-// Copy of two 16-byte-per-lane runs of TW KiB each (Q and dY of a tile): LDS destination
-// m0x + 1 KiB * u + 16 * lane for instruction u, global source desc + voff[u] + 1 KiB * u (the
-// instruction offset moves both addresses).  M0 is restored afterwards.
+// One 16-byte-per-lane run of TW KiB: LDS destination m0 + 1 KiB * u + 16 * lane for
+// instruction u, global source desc + v[u] + 1 KiB * u.  M0 is restored afterwards.
 template <int TW>
+__device__ __forceinline__ void dma_run(uint32_t m0, const i32x4& d, const int* v) {
+    uint32_t saved;
+    if constexpr (TW == 4) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
+            "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
+            "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "s"(d)
+            : "memory");
+    } else if constexpr (TW == 2) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(v[0]), "v"(v[1]), "s"(d)
+            : "memory");
+    } else {
+        static_assert(TW == 1, "runs of 1, 2 or 4 KiB");
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(v[0]), "s"(d)
+            : "memory");
+    }
+}
+
+// Copy of two 16-byte-per-lane runs, TW KiB of tensor a (e.g. Q of a tile) and TB KiB of tensor
+// b (dY): LDS destination m0x + 1 KiB * u + 16 * lane for instruction u, global source
+// desc + voff[u] + 1 KiB * u (the instruction offset moves both addresses).  With equal runs one
+// M0 save / restore covers both.
+template <int TW, int TB = TW>
 __device__ __forceinline__ void dma_pair(uint32_t m0a, const i32x4& da, const int* va, uint32_t m0b,
                                          const i32x4& db, const int* vb) {
     uint32_t saved;
-    if constexpr (TW == 4) {
+    if constexpr (TW != TB) {
+        dma_run<TW>(m0a, da, va);
+        dma_run<TB>(m0b, db, vb);
+    } else if constexpr (TW == 4) {
         asm volatile(
             "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
             "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
@@ -205,9 +246,15 @@ struct Tag {
     static constexpr bool value = V;
 };
 
+template <typename T>
+struct TypeTag {
+    using type = T;
+};
 
 
-// Per-lane LDS offsets (elements) of the swizzled reads.  Rows of the reads below are
+
+// Per-lane LDS offsets (elements) of the swizzled reads.  Kernels whose two tile kinds have
+// the same row length share one set (see offsets_for).  Rows of the reads below are
 // R + lane%32 (row reads) or R + 4h + (lane%16)/4 (+8) (transposing reads) with R a
 // multiple of 16, so the swizzle term depends on the lane only and R*D can be added as a
 // compile-time constant.
@@ -235,6 +282,17 @@ struct LdsOffsets {
         }
     }
 };
+
+// The offsets of tiles with rows of DB elements: `a` itself when DA == DB (one register set),
+// else `b`, which the caller has initialised.
+template <int DA, int DB>
+__device__ __forceinline__ const LdsOffsets<DB>& offsets_for(const LdsOffsets<DA>& a, const LdsOffsets<DB>& b) {
+    if constexpr (DA == DB) {
+        return a;
+    } else {
+        return b;
+    }
+}
 
 template <typename vec, typename T>
 __device__ __forceinline__ vec lds_row(const T* base, int off) {

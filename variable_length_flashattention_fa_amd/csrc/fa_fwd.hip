@@ -25,20 +25,20 @@ namespace fa {
 // O^T is rescaled only when a query's max grows past its reference mref by more than 8 (in
 // log2 units: P stays below 256), decided per wave, so most steps skip the rescale.
 
-template <typename T, int D, bool DROP>
+template <typename T, int DK, int DV, bool DROP>
 __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     using vec = typename Op16<T>::vec;
     constexpr int NW = 8;
     constexpr int BQ = FA16_DQ_BLOCK;
     constexpr int BK = FA16_DQ_TILE_K;
-    constexpr int ND = D / 32;
-    constexpr int NS = D / 16;
-    constexpr int TI = BK * D / 8 / 64;
-    constexpr int TW = TI / NW;
-    static_assert(BQ == 32 * NW && BK == 64 && TI % NW == 0, "tile shape");
+    constexpr int ND = DV / 32;              // 32-row head-dim tiles of O^T
+    constexpr int NS = DK / 16;              // MFMAs per step for S^T
+    constexpr int TWK = BK * DK / 8 / 64 / NW;  // DMA instructions per wave and key tile
+    constexpr int TWV = BK * DV / 8 / 64 / NW;  // ... and value tile
+    static_assert(BQ == 32 * NW && BK == 64 && (BK * DV / 8 / 64) % NW == 0 && DV <= DK, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
-    __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
+    __shared__ __attribute__((aligned(16))) T sK[2][BK * DK];
+    __shared__ __attribute__((aligned(16))) T sV[2][BK * DV];
 
     const fa_work_item_t it = p.items[blockIdx.x];
     const int n = blockIdx.y;
@@ -52,26 +52,28 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     const int i0 = it.block * BQ + 32 * w;
     const int qi = i0 + col;
 
-    LdsOffsets<D> lo_;
-    lo_.init(lane);
+    LdsOffsets<DK> loK;
+    loK.init(lane);
+    LdsOffsets<DV> loV_;
+    if constexpr (DK != DV) loV_.init(lane);
+    const LdsOffsets<DV>& loV = offsets_for(loK, loV_);
 
     const int hk = n / p.group;  // the key/value head this query head reads
     const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh;
     const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + hk * p.v_sh;
-    int koff[TW];
-    int voff[TW];
+    int koff[TWK];
+    int voff[TWV];
 #pragma unroll
-    for (int u = 0; u < TW; ++u) {
-        koff[u] = dma_offset<D>(w * TW + u, lane, p.k_st) - 1024 * u;
-        voff[u] = dma_offset<D>(w * TW + u, lane, p.v_st) - 1024 * u;
-    }
+    for (int u = 0; u < TWK; ++u) koff[u] = dma_offset<DK>(w * TWK + u, lane, p.k_st) - 1024 * u;
+#pragma unroll
+    for (int u = 0; u < TWV; ++u) voff[u] = dma_offset<DV>(w * TWV + u, lane, p.v_st) - 1024 * u;
     auto issue = [&](int kt, int b) {
         const int k0 = kt * BK;
         const i32x4 rk = buffer_desc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st));
         const i32x4 rv = buffer_desc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st));
-        const uint32_t mk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TW * 512)));
-        const uint32_t mv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TW * 512)));
-        dma_pair<TW>(__builtin_amdgcn_readfirstlane(mk), rk, koff, __builtin_amdgcn_readfirstlane(mv), rv, voff);
+        const uint32_t mk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * 512)));
+        const uint32_t mv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * 512)));
+        dma_pair<TWK, TWV>(__builtin_amdgcn_readfirstlane(mk), rk, koff, __builtin_amdgcn_readfirstlane(mv), rv, voff);
     };
 
     // this lane's Q row
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         f32x16 accS = zero16();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const vec ak = lds_row<vec>(cK, lo_.row[s]);
+            const vec ak = lds_row<vec>(cK, loK.row[s]);
             accS = Op16<T>::mfma(ak, qreg[s], accS);
         }
         const bool full = wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
             const vec bp = __builtin_bit_cast(vec, make_uint4(pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]));
 #pragma unroll
             for (int nd = 0; nd < ND; ++nd) {
-                const vec av = lds_tr<vec>(cV + 16 * kk * D, lo_.tr[nd][0], lo_.tr[nd][1]);
+                const vec av = lds_tr<vec>(cV + 16 * kk * DV, loV.tr[nd][0], loV.tr[nd][1]);
                 accO[nd] = Op16<T>::mfma(av, bp, accO[nd]);
             }
         }
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         __syncthreads();
         if (kt + 1 < it.tile_end) issue(kt + 1, b ^ 1);
         kstep(sK[b], sV[b], kt * BK);
-        kstep(sK[b] + 32 * D, sV[b] + 32 * D, kt * BK + 32);
+        kstep(sK[b] + 32 * DK, sV[b] + 32 * DV, kt * BK + 32);
         b ^= 1;
     }
 
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
 // fp32: one thread per (query, head) with an online softmax over its admitted keys, the O row in
 // registers.  Made for small problems.
 
-template <int D, bool DROP>
+template <int DK, int DV, bool DROP>
 __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) {
     const fa_work_item_t it = p.items[blockIdx.x];
     const int n = blockIdx.y;
@@ -289,13 +291,12 @@ __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) 
     const int hk = n / p.group;  // the key/value head this query head reads
     const float* kb = static_cast<const float*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh;
     const float* vb = static_cast<const float*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + hk * p.v_sh;
-    float qr[D];
-    float o[D];
+    float qr[DK];
+    float o[DV];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        qr[d] = q[d];
-        o[d] = 0.f;
-    }
+    for (int d = 0; d < DK; ++d) qr[d] = q[d];
+#pragma unroll
+    for (int d = 0; d < DV; ++d) o[d] = 0.f;
     const int64_t bit0 = it.drop_base + (static_cast<int64_t>(n) * L + qi) * K;
     float m = -INFINITY;
     float l = 0.f;
@@ -303,13 +304,13 @@ __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) 
         const float* kr = kb + static_cast<int64_t>(j) * p.k_st;
         float s = 0.f;
 #pragma unroll
-        for (int d = 0; d < D; ++d) s = fmaf(qr[d], kr[d], s);
+        for (int d = 0; d < DK; ++d) s = fmaf(qr[d], kr[d], s);
         s *= p.scale;
         if (s > m) {
             const float alpha = m == -INFINITY ? 0.f : expf(m - s);
             l *= alpha;
 #pragma unroll
-            for (int d = 0; d < D; ++d) o[d] *= alpha;
+            for (int d = 0; d < DV; ++d) o[d] *= alpha;
             m = s;
         }
         const float pj = expf(s - m);
@@ -322,12 +323,12 @@ __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) 
         const float c = pj * z;
         const float* vr = vb + static_cast<int64_t>(j) * p.v_st;
 #pragma unroll
-        for (int d = 0; d < D; ++d) o[d] = fmaf(c, vr[d], o[d]);
+        for (int d = 0; d < DV; ++d) o[d] = fmaf(c, vr[d], o[d]);
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
     float* y = static_cast<float*>(p.y) + static_cast<int64_t>(it.q_start + qi) * p.y_st + n * p.y_sh;
 #pragma unroll
-    for (int d = 0; d < D; ++d) y[d] = o[d] * inv;
+    for (int d = 0; d < DV; ++d) y[d] = o[d] * inv;
     const int64_t srow = (static_cast<int64_t>(n) * p.tq + it.q_start + qi) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -338,39 +339,46 @@ __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) 
 
 // ------------------------------------------------------------------------------------------------
 
-template <typename T, int D, bool DROP>
+template <typename T, int DK, int DV, bool DROP>
 static hipError_t launch_fwd16_t(const FwdArgs& a, int64_t n, hipStream_t stream) {
-    fwd16_kernel<T, D, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
+    fwd16_kernel<T, DK, DV, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_fwd16(int32_t dtype, int head_dim, bool dropout, const FwdArgs& a, int64_t n_items,
-                        hipStream_t stream) {
-    if (n_items <= 0) return hipSuccess;
-    if (dtype == FA_BF16) {
-        if (head_dim == 128)
-            return dropout ? launch_fwd16_t<__bf16, 128, true>(a, n_items, stream)
-                           : launch_fwd16_t<__bf16, 128, false>(a, n_items, stream);
-        return dropout ? launch_fwd16_t<__bf16, 64, true>(a, n_items, stream)
-                       : launch_fwd16_t<__bf16, 64, false>(a, n_items, stream);
-    }
-    if (head_dim == 128)
-        return dropout ? launch_fwd16_t<_Float16, 128, true>(a, n_items, stream)
-                       : launch_fwd16_t<_Float16, 128, false>(a, n_items, stream);
-    return dropout ? launch_fwd16_t<_Float16, 64, true>(a, n_items, stream)
-                   : launch_fwd16_t<_Float16, 64, false>(a, n_items, stream);
+template <typename T, int DK, int DV>
+static hipError_t fwd16_drop(bool dropout, const FwdArgs& a, int64_t n, hipStream_t stream) {
+    return dropout ? launch_fwd16_t<T, DK, DV, true>(a, n, stream) : launch_fwd16_t<T, DK, DV, false>(a, n, stream);
 }
 
-hipError_t launch_fwd32(int head_dim, bool dropout, const FwdArgs& a, int64_t n_items, hipStream_t stream) {
+template <typename T>
+static hipError_t fwd16_dims(int dk, int dv, bool dropout, const FwdArgs& a, int64_t n, hipStream_t stream) {
+    if (dk == 128 && dv == 128) return fwd16_drop<T, 128, 128>(dropout, a, n, stream);
+    if (dk == 128 && dv == 64) return fwd16_drop<T, 128, 64>(dropout, a, n, stream);
+    if (dk == 64 && dv == 64) return fwd16_drop<T, 64, 64>(dropout, a, n, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const FwdArgs& a,
+                        int64_t n_items, hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    if (dtype == FA_BF16) return fwd16_dims<__bf16>(head_dim_k, head_dim_v, dropout, a, n_items, stream);
+    return fwd16_dims<_Float16>(head_dim_k, head_dim_v, dropout, a, n_items, stream);
+}
+
+template <int DK, int DV>
+static void fwd32_launch(bool dropout, const FwdArgs& a, dim3 grid, hipStream_t stream) {
+    if (dropout) fwd32_kernel<DK, DV, true><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
+    else fwd32_kernel<DK, DV, false><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
+}
+
+hipError_t launch_fwd32(int head_dim_k, int head_dim_v, bool dropout, const FwdArgs& a, int64_t n_items,
+                        hipStream_t stream) {
     if (n_items <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(n_items), static_cast<unsigned>(a.heads));
-    if (head_dim == 128) {
-        if (dropout) fwd32_kernel<128, true><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
-        else fwd32_kernel<128, false><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
-    } else {
-        if (dropout) fwd32_kernel<64, true><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
-        else fwd32_kernel<64, false><<<grid, dim3(FA32_FWD_BLOCK), 0, stream>>>(a);
-    }
+    if (head_dim_k == 128 && head_dim_v == 128) fwd32_launch<128, 128>(dropout, a, grid, stream);
+    else if (head_dim_k == 128 && head_dim_v == 64) fwd32_launch<128, 64>(dropout, a, grid, stream);
+    else if (head_dim_k == 64 && head_dim_v == 64) fwd32_launch<64, 64>(dropout, a, grid, stream);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

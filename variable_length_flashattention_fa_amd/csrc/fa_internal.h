@@ -28,6 +28,11 @@ inline int64_t clamp_window(int64_t x) {
 // Returns FA_OK or an error status (message set).
 int check_seqlens(const fa_seqlens_t* s, const char* name);
 
+// Head dims (Q and K, V) the kernels are built for: (128, 128), (128, 64) and (64, 64).
+inline bool head_dims_supported(int64_t dk, int64_t dv) {
+    return (dk == 128 && (dv == 128 || dv == 64)) || (dk == 64 && dv == 64);
+}
+
 // Key rows per workgroup of the fp32 kernel.
 constexpr int kBlockKv32 = 128;
 

@@ -15,10 +15,10 @@ struct TensorArg {
     int64_t stride_h;
 };
 
-// Row pass: delta[n, t] = sum_d dY * Y (fp32), beta[n, t] = max*log2(e) + log2(sum),
-// stored as float2 {delta, beta} in rowstat[n * tq + t]; also zeroes the head-major
-// dq_acc [N, tq, D] when dq_acc is not null.
-hipError_t launch_preprocess(int32_t dtype, int head_dim, TensorArg dy, TensorArg y,
+// Row pass: delta[n, t] = sum_d dY * Y (fp32, over V's head dim), beta[n, t] = max*log2(e) +
+// log2(sum), stored as float2 {delta, beta} in rowstat[n * tq + t]; also zeroes the head-major
+// dq_acc [N, tq, Dk] when dq_acc is not null.  Head dims (V, Q/K): (128, 128), (64, 128), (64, 64).
+hipError_t launch_preprocess(int32_t dtype, int head_dim_v, int head_dim_k, TensorArg dy, TensorArg y,
                              const float* softmax_max, const float* softmax_sum, float2* rowstat,
                              float* dq_acc, int64_t tq, int64_t heads, hipStream_t stream);
 
@@ -43,9 +43,10 @@ struct MainArgs {
     float scale;      // folded into dK
 };
 
-// KV-block-major backward over n_items work items x key/value heads.
-hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs& a, int64_t n_items,
-                       hipStream_t stream);
+// KV-block-major backward over n_items work items x key/value heads (fp32 only).  Head dims
+// (Q/K, V): (128, 128), (128, 64) or (64, 64).
+hipError_t launch_main(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const MainArgs& a,
+                       int64_t n_items, hipStream_t stream);
 
 // dq[t, n, :] = scale * dq_acc[n, t, :] converted to the output dtype.
 hipError_t launch_convert(int32_t dtype, int head_dim, const float* dq_acc, void* dq, int64_t dq_st,
@@ -77,12 +78,13 @@ struct Bwd16Args {
 };
 
 // dK/dV kernel over n_items key-block items x key/value heads (each sums its group of query heads).
-hipError_t launch_dkdv16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
-                         hipStream_t stream);
+// Head dims (Q/K, V): (128, 128), (128, 64) or (64, 64).
+hipError_t launch_dkdv16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const Bwd16Args& a,
+                         int64_t n_items, hipStream_t stream);
 
-// dQ kernel over n_items query-block items x heads.
-hipError_t launch_dq16(int32_t dtype, int head_dim, bool dropout, const Bwd16Args& a, int64_t n_items,
-                       hipStream_t stream);
+// dQ kernel over n_items query-block items x query heads; the same head dims.
+hipError_t launch_dq16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const Bwd16Args& a,
+                       int64_t n_items, hipStream_t stream);
 
 // ---- forward ----------------------------------------------------------------------------------
 // Y = Dropout(Softmax(Mask(scale Q K^T))) V and the row statistics, over query-block items.
@@ -105,9 +107,11 @@ struct FwdArgs {
 constexpr int FA32_FWD_BLOCK = 64;  // queries per fp32 forward workgroup (one per thread)
 
 // bf16 / fp16 forward over n_items query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles).
-hipError_t launch_fwd16(int32_t dtype, int head_dim, bool dropout, const FwdArgs& a, int64_t n_items,
+// Head dims (Q/K, V): (128, 128), (128, 64) or (64, 64).
+hipError_t launch_fwd16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const FwdArgs& a,
+                        int64_t n_items, hipStream_t stream);
+// fp32 forward over n_items query-block items (FA32_FWD_BLOCK queries); the same head dims.
+hipError_t launch_fwd32(int head_dim_k, int head_dim_v, bool dropout, const FwdArgs& a, int64_t n_items,
                         hipStream_t stream);
-// fp32 forward over n_items query-block items (FA32_FWD_BLOCK queries).
-hipError_t launch_fwd32(int head_dim, bool dropout, const FwdArgs& a, int64_t n_items, hipStream_t stream);
 
 }  // namespace fa

@@ -91,7 +91,7 @@ __device__ __forceinline__ int acc_row(int a, int h) { return 8 * (a >> 2) + 4 *
 // preprocess: row delta, folded stats, dQ accumulator zeroing
 // ----------------------------------------------------------------------------
 
-template <typename T, int D>
+template <typename T, int D, int DQ>
 __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ dy, int64_t dy_st, int64_t dy_sh,
                                                          const T* __restrict__ y, int64_t y_st, int64_t y_sh,
                                                          const float* __restrict__ smax,
@@ -99,8 +99,10 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
                                                          float2* __restrict__ rowstat, float* __restrict__ dq_acc,
                                                          int64_t tq, int heads) {
     constexpr int VEC = 16 / sizeof(T);
-    constexpr int TPR = D / VEC;  // threads per (token, head) row
+    constexpr int TPR = D / VEC;    // threads per (token, head) row of dY and Y (D = V's head dim)
     constexpr int RPB = 256 / TPR;
+    constexpr int ZPT = DQ / TPR;   // dQ accumulator floats zeroed per thread (DQ = Q's head dim)
+    static_assert(ZPT % 4 == 0, "accumulator row split");
     const int sub = threadIdx.x % TPR;
     const int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
     const bool valid = r < tq * heads;
@@ -116,9 +118,9 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
         for (int e = 0; e < VEC; ++e) part += static_cast<float>(a.e[e]) * static_cast<float>(b.e[e]);
         if (dq_acc != nullptr) {
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4* acc = reinterpret_cast<f32x4*>(dq_acc + (static_cast<int64_t>(n) * tq + t) * D + sub * VEC);
+            f32x4* acc = reinterpret_cast<f32x4*>(dq_acc + (static_cast<int64_t>(n) * tq + t) * DQ + sub * ZPT);
 #pragma unroll
-            for (int e = 0; e < VEC / 4; ++e) acc[e] = z;
+            for (int e = 0; e < ZPT / 4; ++e) acc[e] = z;
         }
     }
 #pragma unroll
@@ -178,7 +180,7 @@ struct DevArgs {
     float exp_scale, inv_keep, scale;
 };
 
-template <typename T, int D, bool DROP>
+template <typename T, int DK, int DV, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     using E = Elem<T>;
     using vec = typename E::vec;
@@ -187,20 +189,23 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     constexpr int BQ = sizeof(T) == 4 ? 32 : 64;    // query tile rows (fp32 lists use 32)
     constexpr int BKV = 128;                        // key block rows (4 waves x 32)
     constexpr int MT = BQ / 32;                     // 32-row query sub-tiles
-    constexpr int NT = D / 32;                      // 32-column head-dim sub-tiles
+    constexpr int NTK = DK / 32;                    // 32-column sub-tiles of dK and dQ
+    constexpr int NTV = DV / 32;                    // ... of dV
     constexpr int PADE = 16 / sizeof(T);            // 16-byte row padding
-    constexpr int PQ = D + PADE;                    // pitch of row-major Q / dY tiles
+    constexpr int PQ = DK + PADE;                   // pitch of row-major Q tiles
+    constexpr int PD = DV + PADE;                   // pitch of row-major dY tiles
     constexpr int PT = BQ + PADE;                   // pitch of transposed Q / dY tiles
     constexpr int PS = BKV + PADE;                  // pitch of dS and K^T
     constexpr int VEC = 16 / sizeof(T);
-    constexpr int VPR = D / VEC;
+    constexpr int VPRQ = DK / VEC;
+    constexpr int VPRD = DV / VEC;
 
     __shared__ __attribute__((aligned(16))) T sQ[BQ * PQ];
-    __shared__ __attribute__((aligned(16))) T sdY[BQ * PQ];
-    __shared__ __attribute__((aligned(16))) T sQt[D * PT];
-    __shared__ __attribute__((aligned(16))) T sdYt[D * PT];
+    __shared__ __attribute__((aligned(16))) T sdY[BQ * PD];
+    __shared__ __attribute__((aligned(16))) T sQt[DK * PT];
+    __shared__ __attribute__((aligned(16))) T sdYt[DV * PT];
     __shared__ __attribute__((aligned(16))) T sdS[BQ * PS];
-    __shared__ __attribute__((aligned(16))) T sKt[D * PS];
+    __shared__ __attribute__((aligned(16))) T sKt[DK * PS];
     __shared__ float2 sStat[BQ];
 
     const fa_work_item_t it = p.items[blockIdx.x];
@@ -217,23 +222,25 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     const int jw = j0 + 32 * w + col;  // this lane's key (sequence coordinates) in S / P
 
     // K and V rows of this lane as B operands of S = Q K^T and dP = dY V^T
-    vec kreg[D / KS];
-    vec vreg[D / KS];
+    vec kreg[DK / KS];
+    vec vreg[DV / KS];
     {
         const bool ok = jw < K;
         const T* kr = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start + (ok ? jw : 0)) * p.k_st + hk * p.k_sh;
         const T* vr = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start + (ok ? jw : 0)) * p.v_st + hk * p.v_sh;
 #pragma unroll
-        for (int s = 0; s < D / KS; ++s) {
+        for (int s = 0; s < DK / KS; ++s) {
 #pragma unroll
-            for (int e = 0; e < KL; ++e) {
-                vset(kreg[s], e, ok ? kr[s * KS + h * KL + e] : static_cast<T>(0.f));
-                vset(vreg[s], e, ok ? vr[s * KS + h * KL + e] : static_cast<T>(0.f));
-            }
+            for (int e = 0; e < KL; ++e) vset(kreg[s], e, ok ? kr[s * KS + h * KL + e] : static_cast<T>(0.f));
+        }
+#pragma unroll
+        for (int s = 0; s < DV / KS; ++s) {
+#pragma unroll
+            for (int e = 0; e < KL; ++e) vset(vreg[s], e, ok ? vr[s * KS + h * KL + e] : static_cast<T>(0.f));
         }
         // K^T in LDS for the dQ = dS K contraction (over keys)
 #pragma unroll
-        for (int s = 0; s < D / KS; ++s) {
+        for (int s = 0; s < DK / KS; ++s) {
 #pragma unroll
             for (int e = 0; e < KL; ++e) {
                 T x;
@@ -243,13 +250,12 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
         }
     }
 
-    f32x16 accK[NT];
-    f32x16 accV[NT];
+    f32x16 accK[NTK];
+    f32x16 accV[NTV];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        accK[i] = zero16();
-        accV[i] = zero16();
-    }
+    for (int i = 0; i < NTK; ++i) accK[i] = zero16();
+#pragma unroll
+    for (int i = 0; i < NTV; ++i) accV[i] = zero16();
 
     for (int r = 0; r < p.group; ++r) {
         const int n = hk * p.group + r;  // query head
@@ -260,28 +266,35 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
         for (int t = it.tile_begin; t < it.tile_end; ++t) {
             const int q0 = t * BQ;
             __syncthreads();  // previous tile's LDS reads are done
-            for (int idx = tid; idx < BQ * VPR; idx += 256) {
-                const int r = idx / VPR;
-                const int cv = idx - r * VPR;
+            for (int idx = tid; idx < BQ * VPRQ; idx += 256) {
+                const int r = idx / VPRQ;
+                const int cv = idx - r * VPRQ;
                 const int qi = q0 + r;
-                Chunk<T> xq, xd;
+                Chunk<T> xq;
                 if (qi < L) {
                     xq = *reinterpret_cast<const Chunk<T>*>(gq + static_cast<int64_t>(qi) * p.q_st + cv * VEC);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) xq.e[e] = static_cast<T>(0.f);
+                }
+                *reinterpret_cast<Chunk<T>*>(&sQ[r * PQ + cv * VEC]) = xq;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) sQt[(cv * VEC + e) * PT + r] = xq.e[e];
+            }
+            for (int idx = tid; idx < BQ * VPRD; idx += 256) {
+                const int r = idx / VPRD;
+                const int cv = idx - r * VPRD;
+                const int qi = q0 + r;
+                Chunk<T> xd;
+                if (qi < L) {
                     xd = *reinterpret_cast<const Chunk<T>*>(gdy + static_cast<int64_t>(qi) * p.dy_st + cv * VEC);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        xq.e[e] = static_cast<T>(0.f);
-                        xd.e[e] = static_cast<T>(0.f);
-                    }
+                    for (int e = 0; e < VEC; ++e) xd.e[e] = static_cast<T>(0.f);
                 }
-                *reinterpret_cast<Chunk<T>*>(&sQ[r * PQ + cv * VEC]) = xq;
-                *reinterpret_cast<Chunk<T>*>(&sdY[r * PQ + cv * VEC]) = xd;
+                *reinterpret_cast<Chunk<T>*>(&sdY[r * PD + cv * VEC]) = xd;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    sQt[(cv * VEC + e) * PT + r] = xq.e[e];
-                    sdYt[(cv * VEC + e) * PT + r] = xd.e[e];
-                }
+                for (int e = 0; e < VEC; ++e) sdYt[(cv * VEC + e) * PT + r] = xd.e[e];
             }
             if (tid < BQ) {
                 const int qi = q0 + tid;
@@ -297,10 +310,13 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
                 accS[mt] = zero16();
                 accP[mt] = zero16();
 #pragma unroll
-                for (int s = 0; s < D / KS; ++s) {
+                for (int s = 0; s < DK / KS; ++s) {
                     const vec aq = *reinterpret_cast<const vec*>(&sQ[(mt * 32 + col) * PQ + s * KS + h * KL]);
-                    const vec ad = *reinterpret_cast<const vec*>(&sdY[(mt * 32 + col) * PQ + s * KS + h * KL]);
                     accS[mt] = E::mfma(aq, kreg[s], accS[mt]);
+                }
+#pragma unroll
+                for (int s = 0; s < DV / KS; ++s) {
+                    const vec ad = *reinterpret_cast<const vec*>(&sdY[(mt * 32 + col) * PD + s * KS + h * KL]);
                     accP[mt] = E::mfma(ad, vreg[s], accP[mt]);
                 }
             }
@@ -361,15 +377,19 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
                         vset(as, e, cvt<T>(accP[mt][kk * KL + e]));
                     }
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        vec bd, bq;
+                    for (int nt = 0; nt < NTV; ++nt) {
+                        vec bd;
 #pragma unroll
-                        for (int e = 0; e < KL; ++e) {
-                            const int qr = mt * 32 + acc_row(kk * KL + e, h);
-                            vset(bd, e, sdYt[(nt * 32 + col) * PT + qr]);
-                            vset(bq, e, sQt[(nt * 32 + col) * PT + qr]);
-                        }
+                        for (int e = 0; e < KL; ++e)
+                            vset(bd, e, sdYt[(nt * 32 + col) * PT + mt * 32 + acc_row(kk * KL + e, h)]);
                         accV[nt] = E::mfma(ap, bd, accV[nt]);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < NTK; ++nt) {
+                        vec bq;
+#pragma unroll
+                        for (int e = 0; e < KL; ++e)
+                            vset(bq, e, sQt[(nt * 32 + col) * PT + mt * 32 + acc_row(kk * KL + e, h)]);
                         accK[nt] = E::mfma(as, bq, accK[nt]);
                     }
                 }
@@ -386,9 +406,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
             __syncthreads();
 
             // dQ_acc[tile] += dS K  (unscaled; the convert pass applies scale)
-            for (int tt = w; tt < MT * NT; tt += 4) {
-                const int mq = tt / NT;
-                const int nd = tt - mq * NT;
+            for (int tt = w; tt < MT * NTK; tt += 4) {
+                const int mq = tt / NTK;
+                const int nd = tt - mq * NTK;
                 f32x16 acc = zero16();
 #pragma unroll
                 for (int s = 0; s < BKV / KS; ++s) {
@@ -400,7 +420,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
                 for (int a = 0; a < 16; ++a) {
                     const int i = q0 + mq * 32 + acc_row(a, h);
                     if (i < L) {
-                        float* dst = p.dq_acc + (static_cast<int64_t>(n) * p.tq + it.q_start + i) * D + nd * 32 + col;
+                        float* dst = p.dq_acc + (static_cast<int64_t>(n) * p.tq + it.q_start + i) * DK + nd * 32 + col;
                         unsafeAtomicAdd(dst, acc[a]);
                     }
                 }
@@ -412,13 +432,13 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     T* gdk = static_cast<T*>(p.dk) + static_cast<int64_t>(it.kv_start) * p.dk_st + hk * p.dk_sh;
     T* gdv = static_cast<T*>(p.dv) + static_cast<int64_t>(it.kv_start) * p.dv_st + hk * p.dv_sh;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NTK; ++nt) {
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
             const int j = j0 + 32 * w + acc_row(a, h);
             if (j < K) {
                 gdk[static_cast<int64_t>(j) * p.dk_st + nt * 32 + col] = cvt<T>(accK[nt][a] * p.scale);
-                gdv[static_cast<int64_t>(j) * p.dv_st + nt * 32 + col] = cvt<T>(accV[nt][a]);
+                if (nt < NTV) gdv[static_cast<int64_t>(j) * p.dv_st + nt * 32 + col] = cvt<T>(accV[nt][a]);
             }
         }
     }
@@ -428,28 +448,36 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
 // launchers
 // ----------------------------------------------------------------------------
 
-template <typename T, int D>
+template <typename T, int D, int DQ>
 static hipError_t preprocess_t(TensorArg dy, TensorArg y, const float* smax, const float* ssum, float2* rowstat,
                                float* dq_acc, int64_t tq, int64_t heads, hipStream_t stream) {
     constexpr int TPR = D / (16 / sizeof(T));
     constexpr int RPB = 256 / TPR;
     const int64_t rows = tq * heads;
     const int64_t blocks = (rows + RPB - 1) / RPB;
-    preprocess_kernel<T, D><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+    preprocess_kernel<T, D, DQ><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
         static_cast<const T*>(dy.data), dy.stride_t, dy.stride_h, static_cast<const T*>(y.data), y.stride_t,
         y.stride_h, smax, ssum, rowstat, dq_acc, tq, static_cast<int>(heads));
     return hipGetLastError();
 }
 
-hipError_t launch_preprocess(int32_t dtype, int head_dim, TensorArg dy, TensorArg y, const float* smax,
-                             const float* ssum, float2* rowstat, float* dq_acc, int64_t tq, int64_t heads,
-                             hipStream_t stream) {
-#define FA_PRE(T, D) return preprocess_t<T, D>(dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream)
-    if (dtype == FA_BF16) { if (head_dim == 128) FA_PRE(__bf16, 128); FA_PRE(__bf16, 64); }
-    if (dtype == FA_F16) { if (head_dim == 128) FA_PRE(_Float16, 128); FA_PRE(_Float16, 64); }
-    if (head_dim == 128) FA_PRE(float, 128);
-    FA_PRE(float, 64);
-#undef FA_PRE
+template <typename T>
+static hipError_t preprocess_dims(int dv, int dk, TensorArg dy, TensorArg y, const float* smax, const float* ssum,
+                                  float2* rowstat, float* dq_acc, int64_t tq, int64_t heads, hipStream_t stream) {
+    if (dv == 128 && dk == 128) return preprocess_t<T, 128, 128>(dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
+    if (dv == 64 && dk == 128) return preprocess_t<T, 64, 128>(dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
+    if (dv == 64 && dk == 64) return preprocess_t<T, 64, 64>(dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_preprocess(int32_t dtype, int head_dim_v, int head_dim_k, TensorArg dy, TensorArg y,
+                             const float* smax, const float* ssum, float2* rowstat, float* dq_acc, int64_t tq,
+                             int64_t heads, hipStream_t stream) {
+    if (dtype == FA_BF16)
+        return preprocess_dims<__bf16>(head_dim_v, head_dim_k, dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
+    if (dtype == FA_F16)
+        return preprocess_dims<_Float16>(head_dim_v, head_dim_k, dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
+    return preprocess_dims<float>(head_dim_v, head_dim_k, dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
 }
 
 template <typename T, int D>
@@ -474,15 +502,15 @@ hipError_t launch_convert(int32_t dtype, int head_dim, const float* dq_acc, void
 #undef FA_CVT
 }
 
-template <typename T, int D, bool DROP>
+template <typename T, int DK, int DV, bool DROP>
 static hipError_t main_t(const DevArgs& d, int64_t n_items, int heads, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(n_items), static_cast<unsigned>(heads));
-    bwd_main_kernel<T, D, DROP><<<grid, dim3(256), 0, stream>>>(d);
+    bwd_main_kernel<T, DK, DV, DROP><<<grid, dim3(256), 0, stream>>>(d);
     return hipGetLastError();
 }
 
-hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs& a, int64_t n_items,
-                       hipStream_t stream) {
+hipError_t launch_main(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const MainArgs& a,
+                       int64_t n_items, hipStream_t stream) {
     DevArgs d;
     d.q = a.q.data;
     d.k = a.k.data;
@@ -515,12 +543,14 @@ hipError_t launch_main(int32_t dtype, int head_dim, bool dropout, const MainArgs
     d.exp_scale = a.exp_scale;
     d.inv_keep = a.inv_keep;
     d.scale = a.scale;
-#define FA_MAIN(T, D)                                                          \
-    return dropout ? main_t<T, D, true>(d, n_items, a.heads / a.group, stream)           \
-                   : main_t<T, D, false>(d, n_items, a.heads / a.group, stream)
-    if (dtype != FA_F32) return hipErrorInvalidValue;  // 16-bit inputs run launch_bwd16
-    if (head_dim == 128) FA_MAIN(float, 128);
-    FA_MAIN(float, 64);
+#define FA_MAIN(DK, DV)                                                                   \
+    return dropout ? main_t<float, DK, DV, true>(d, n_items, a.heads / a.group, stream)     \
+                   : main_t<float, DK, DV, false>(d, n_items, a.heads / a.group, stream)
+    if (dtype != FA_F32) return hipErrorInvalidValue;  // 16-bit inputs run launch_dkdv16 / launch_dq16
+    if (head_dim_k == 128 && head_dim_v == 128) FA_MAIN(128, 128);
+    if (head_dim_k == 128 && head_dim_v == 64) FA_MAIN(128, 64);
+    if (head_dim_k == 64 && head_dim_v == 64) FA_MAIN(64, 64);
+    return hipErrorInvalidValue;
 #undef FA_MAIN
 }
 
