@@ -2,7 +2,7 @@
 """Benchmark of the varlen attention backward on one MI355X.
 
 One step = one fa_varlen_bwd call over the whole workload (row preprocess,
-main backward kernel, dQ convert) with every input already resident in HBM.
+dK/dV and dQ kernels) with every input already resident in HBM.
 Default workload: bf16, 4 sequences x 16384 tokens, 16 heads, D = 128,
 bottom-right causal mask, keep_prob 1.
 
@@ -278,10 +278,9 @@ def main(argv=None):
     esz = q.element_size()
     pair_flops = 2.0 * wl.heads * wl.head_dim * pairs  # one contraction over all admitted pairs
     if q.dtype == torch.float32:
-        # one kernel runs all five contractions; dQ goes through an fp32 accumulator
-        mfma = {"bwd_main": ("bwd_main_kernel", 5 * pair_flops)}
-        hbm = {"preprocess": tq * heads * (2 * d * esz + 2 * 4 + 8 + 4 * d),  # + zeroed dQ accumulator
-               "convert_dq": tq * heads * (4 * d + d * esz)}
+        # dK/dV kernel: S, dP, dV, dK on fp32 MFMA; dQ kernel: S, dP (recomputed) and dQ on the VALU
+        mfma = {"bwd_main": ("bwd_main_kernel", 4 * pair_flops), "bwd_dq": ("bwd_dq32_kernel", 3 * pair_flops)}
+        hbm = {"preprocess": tq * heads * (2 * d * esz + 2 * 4 + 8)}
     else:
         # dK/dV kernel: S, dP, dV, dK; dQ kernel: S, dP (recomputed) and dQ
         mfma = {"bwd_main": ("bwd_dkdv16_kernel", 4 * pair_flops), "bwd_dq": ("bwd_dq16_kernel", 3 * pair_flops)}

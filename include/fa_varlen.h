@@ -182,9 +182,8 @@ int64_t fa_varlen_worklist(const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t*
 /*
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
  * fa_varlen_bwd / fa_varlen_fwd call records a pair of HIP events around each
- * of its kernels on the call's stream: index 0 the row preprocess, 1 the main
- * backward kernel (dK/dV for bf16 / fp16; the whole backward for fp32), 2 the
- * dQ convert (fp32 only), 3 the dQ kernel (bf16 / fp16 only), 4 the forward.
+ * of its kernels on the call's stream: index 0 the row preprocess, 1 the dK/dV
+ * kernel, 2 (unused), 3 the dQ kernel, 4 the forward.
  */
 void fa_profile_enable(int on);
 

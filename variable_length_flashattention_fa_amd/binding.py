@@ -51,7 +51,7 @@ _lib = None
 
 EXPORTS = ("fa_varlen_bwd", "fa_varlen_fwd", "fa_last_error", "fa_release", "fa_varlen_worklist",
            "fa_profile_enable", "fa_profile_read", "fa_mfma_peak")
-KERNEL_NAMES = ("preprocess", "bwd_main", "convert_dq", "bwd_dq", "fwd")
+KERNEL_NAMES = ("preprocess", "bwd_main", "unused", "bwd_dq", "fwd")
 
 
 def load(path: Optional[str] = None):

@@ -66,8 +66,6 @@ bool aligned16(const fa_tensor_t* t) {
 }
 
 struct Workspace {
-    float* dq_acc = nullptr;
-    size_t dq_acc_bytes = 0;
     float2* rowstat = nullptr;
     size_t rowstat_bytes = 0;
     fa_work_item_t* items = nullptr;
@@ -87,7 +85,7 @@ std::mutex g_mutex;
 std::unordered_map<int, Workspace> g_ws;
 
 // ---- optional per-kernel event timing ----
-constexpr int kKernels = 5;  // 0 preprocess, 1 main / dK-dV, 2 convert, 3 dQ, 4 forward
+constexpr int kKernels = 5;  // 0 preprocess, 1 dK/dV, 2 (unused), 3 dQ, 4 forward
 struct EventPair {
     int kernel;
     hipEvent_t start;
@@ -153,7 +151,6 @@ extern "C" void fa_release(void) {
     for (auto& kv : g_ws) {
         (void)hipSetDevice(kv.first);
         (void)hipDeviceSynchronize();
-        if (kv.second.dq_acc) (void)hipFree(kv.second.dq_acc);
         if (kv.second.rowstat) (void)hipFree(kv.second.rowstat);
         if (kv.second.items) (void)hipFree(kv.second.items);
         if (kv.second.fwd_items) (void)hipFree(kv.second.fwd_items);
@@ -306,7 +303,7 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t dtype = q->dtype;
-    const bool wide = dtype == FA_F32;  // fp32 runs the single-kernel path with a dQ accumulator
+    const bool wide = dtype == FA_F32;  // fp32 runs its own dK/dV and dQ kernels
     const int64_t pre = atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0;
     const int64_t nxt = atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0;
 
@@ -332,6 +329,8 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         if (wide) {
             fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
                                FA_ITEMS_KEY_BLOCKS, fa::kBlockKv32, fa::kTileQ32, list);
+            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
+                               FA_ITEMS_QUERY_BLOCKS, fa::FA32_FWD_BLOCK, fa::FA32_FWD_BLOCK, qlist);
         } else {
             fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
                                FA_ITEMS_KEY_BLOCKS, fa::FA16_DKDV_BLOCK, fa::FA16_DKDV_TILE_Q, list);
@@ -377,19 +376,12 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         int g = grow(&ptr, &ws.rowstat_bytes, static_cast<size_t>(tq * heads) * sizeof(float2), "row statistics");
         ws.rowstat = static_cast<float2*>(ptr);
         if (g != FA_OK) return g;
-        if (wide) {
-            ptr = ws.dq_acc;
-            g = grow(&ptr, &ws.dq_acc_bytes, static_cast<size_t>(tq * heads * d) * sizeof(float), "dq accumulator");
-            ws.dq_acc = static_cast<float*>(ptr);
-            if (g != FA_OK) return g;
-        }
     }
 
     fa::TensorArg tdy{dy->data, dy->stride_t, dy->stride_h};
     fa::TensorArg ty{y->data, y->stride_t, y->stride_h};
     e = timed(0, s, [&] {
-        return fa::launch_preprocess(dtype, dv_dim, d, tdy, ty, softmax_max, softmax_sum, ws.rowstat,
-                                     wide ? ws.dq_acc : nullptr, tq, heads, s);
+        return fa::launch_preprocess(dtype, dv_dim, tdy, ty, softmax_max, softmax_sum, ws.rowstat, tq, heads, s);
     });
     if (e != hipSuccess) return runtime_error("preprocess launch", e);
 
@@ -446,40 +438,37 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         return FA_OK;
     }
 
-    if (ws.n_items > 0) {
-        fa::MainArgs a;
-        a.q = {q->data, q->stride_t, q->stride_h};
-        a.k = {k->data, k->stride_t, k->stride_h};
-        a.v = {v->data, v->stride_t, v->stride_h};
-        a.dy = tdy;
-        a.dk = dk->data;
-        a.dk_st = dk->stride_t;
-        a.dk_sh = dk->stride_h;
-        a.dv = dv->data;
-        a.dv_st = dv->stride_t;
-        a.dv_sh = dv->stride_h;
-        a.rowstat = ws.rowstat;
-        a.dq_acc = ws.dq_acc;
-        a.items = ws.items;
-        a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
-        a.tq = static_cast<int32_t>(tq);
-        a.heads = static_cast<int32_t>(heads);
-        a.group = static_cast<int32_t>(heads / k->heads);
-        a.mode = atten_mode;
-        a.pre = static_cast<int32_t>(pre);
-        a.nxt = static_cast<int32_t>(nxt);
-        a.exp_scale = exp_scale;
-        a.inv_keep = inv_keep;
-        a.scale = static_cast<float>(scale);
-        e = timed(1, s, [&] { return fa::launch_main(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_items, s); });
-        if (e != hipSuccess) return runtime_error("main kernel launch", e);
-    }
-
-    e = timed(2, s, [&] {
-        return fa::launch_convert(dtype, d, ws.dq_acc, dq->data, dq->stride_t, dq->stride_h, tq, heads,
-                                  static_cast<float>(scale), s);
-    });
-    if (e != hipSuccess) return runtime_error("convert launch", e);
+    fa::MainArgs a;
+    a.q = {q->data, q->stride_t, q->stride_h};
+    a.k = {k->data, k->stride_t, k->stride_h};
+    a.v = {v->data, v->stride_t, v->stride_h};
+    a.dy = tdy;
+    a.dq = dq->data;
+    a.dq_st = dq->stride_t;
+    a.dq_sh = dq->stride_h;
+    a.dk = dk->data;
+    a.dk_st = dk->stride_t;
+    a.dk_sh = dk->stride_h;
+    a.dv = dv->data;
+    a.dv_st = dv->stride_t;
+    a.dv_sh = dv->stride_h;
+    a.rowstat = ws.rowstat;
+    a.items = ws.items;
+    a.items_q = ws.items + ws.n_items;
+    a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
+    a.tq = static_cast<int32_t>(tq);
+    a.heads = static_cast<int32_t>(heads);
+    a.group = static_cast<int32_t>(heads / k->heads);
+    a.mode = atten_mode;
+    a.pre = static_cast<int32_t>(pre);
+    a.nxt = static_cast<int32_t>(nxt);
+    a.exp_scale = exp_scale;
+    a.inv_keep = inv_keep;
+    a.scale = static_cast<float>(scale);
+    e = timed(1, s, [&] { return fa::launch_main(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_items, s); });
+    if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
+    e = timed(3, s, [&] { return fa::launch_dq32(d, dv_dim, keep_prob < 1.0, a, ws.n_q_items, s); });
+    if (e != hipSuccess) return runtime_error("dQ kernel launch", e);
     return FA_OK;
 }
 

@@ -16,21 +16,22 @@ struct TensorArg {
 };
 
 // Row pass: delta[n, t] = sum_d dY * Y (fp32, over V's head dim), beta[n, t] = max*log2(e) +
-// log2(sum), stored as float2 {delta, beta} in rowstat[n * tq + t]; also zeroes the head-major
-// dq_acc [N, tq, Dk] when dq_acc is not null.  Head dims (V, Q/K): (128, 128), (64, 128), (64, 64).
-hipError_t launch_preprocess(int32_t dtype, int head_dim_v, int head_dim_k, TensorArg dy, TensorArg y,
+// log2(sum), stored as float2 {delta, beta} in rowstat[n * tq + t].
+hipError_t launch_preprocess(int32_t dtype, int head_dim_v, TensorArg dy, TensorArg y,
                              const float* softmax_max, const float* softmax_sum, float2* rowstat,
-                             float* dq_acc, int64_t tq, int64_t heads, hipStream_t stream);
+                             int64_t tq, int64_t heads, hipStream_t stream);
 
 struct MainArgs {
     TensorArg q, k, v, dy;
+    void* dq;
+    int64_t dq_st, dq_sh;
     void* dk;
     int64_t dk_st, dk_sh;
     void* dv;
     int64_t dv_st, dv_sh;
     const float2* rowstat;
-    float* dq_acc;
-    const fa_work_item_t* items;
+    const fa_work_item_t* items;    // key-block items (kBlockKv32 keys, kTileQ32 query tiles)
+    const fa_work_item_t* items_q;  // query-block items (FA32_FWD_BLOCK queries)
     const uint8_t* drop_mask;
     int32_t tq;
     int32_t heads;   // query heads
@@ -40,17 +41,19 @@ struct MainArgs {
     int32_t nxt;
     float exp_scale;  // scale * log2(e)
     float inv_keep;   // 1 / keep_prob
-    float scale;      // folded into dK
+    float scale;      // folded into dK and dQ
 };
 
-// KV-block-major backward over n_items work items x key/value heads (fp32 only).  Head dims
-// (Q/K, V): (128, 128), (128, 64) or (64, 64).
+constexpr int FA32_FWD_BLOCK = 64;  // queries per fp32 forward / dQ workgroup (one per thread)
+
+// fp32 dK/dV kernel over n_items key-block items x key/value heads.  Head dims (Q/K, V):
+// (128, 128), (128, 64) or (64, 64).
 hipError_t launch_main(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const MainArgs& a,
                        int64_t n_items, hipStream_t stream);
 
-// dq[t, n, :] = scale * dq_acc[n, t, :] converted to the output dtype.
-hipError_t launch_convert(int32_t dtype, int head_dim, const float* dq_acc, void* dq, int64_t dq_st,
-                          int64_t dq_sh, int64_t tq, int64_t heads, float scale, hipStream_t stream);
+// fp32 dQ kernel over n_items query-block items x query heads; the same head dims.
+hipError_t launch_dq32(int head_dim_k, int head_dim_v, bool dropout, const MainArgs& a, int64_t n_items,
+                       hipStream_t stream);
 
 // ---- 16-bit path: dK/dV and dQ kernels without atomics ----
 constexpr int FA16_DKDV_BLOCK = 128;  // keys per dK/dV workgroup
@@ -103,8 +106,6 @@ struct FwdArgs {
     int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float scale, exp_scale, inv_keep;
 };
-
-constexpr int FA32_FWD_BLOCK = 64;  // queries per fp32 forward workgroup (one per thread)
 
 // bf16 / fp16 forward over n_items query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles).
 // Head dims (Q/K, V): (128, 128), (128, 64) or (64, 64).

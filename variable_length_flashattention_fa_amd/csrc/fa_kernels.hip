@@ -1,4 +1,5 @@
-// gfx950 (CDNA4) kernels of the varlen attention backward.
+// gfx950 (CDNA4) kernels of the varlen attention backward: the row preprocess (all dtypes) and
+// the fp32 path.
 //
 // The backward follows the formulas section of the "FlashAttention梯度V2" page
 // (dV = P^T dY, dQ = scale dS K, dK = scale dS^T Q) with the softmax Jacobian
@@ -6,11 +7,13 @@
 // Ps rebuilt from the forward's row max / row sum (the page's softmaxMax and
 // softmaxSum inputs).
 //
-// Work split: one workgroup (4 wave64s) per (key block of 128 rows, head).  The
-// workgroup keeps its K and V rows and its dK / dV accumulators in registers
-// and walks the query tiles that can see the block.  All five contractions run
-// on 32x32 MFMA (bf16 / fp16 with fp32 accumulation; fp32 MFMA for fp32), with
-// dQ accumulated in fp32 with atomics and converted by a separate pass.
+// fp32 work split, deterministic (no atomics):
+//   dK/dV: one workgroup (4 wave64s) per (key block of 128 rows, key/value head).  It keeps
+//          its K and V rows and dK / dV accumulators in registers and walks the query tiles
+//          that can see the block, for every query head of the group; S, dP, dV and dK run
+//          on the fp32 32x32x2 MFMA.
+//   dQ:    two lanes per (query, head) walk the keys the query admits and recompute S and dP
+//          for them (the fp32 path serves small problems; each dQ row has one owner).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -88,21 +91,18 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ int acc_row(int a, int h) { return 8 * (a >> 2) + 4 * h + (a & 3); }
 
 // ----------------------------------------------------------------------------
-// preprocess: row delta, folded stats, dQ accumulator zeroing
+// preprocess: row delta and folded stats
 // ----------------------------------------------------------------------------
 
-template <typename T, int D, int DQ>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ dy, int64_t dy_st, int64_t dy_sh,
                                                          const T* __restrict__ y, int64_t y_st, int64_t y_sh,
                                                          const float* __restrict__ smax,
                                                          const float* __restrict__ ssum,
-                                                         float2* __restrict__ rowstat, float* __restrict__ dq_acc,
-                                                         int64_t tq, int heads) {
+                                                         float2* __restrict__ rowstat, int64_t tq, int heads) {
     constexpr int VEC = 16 / sizeof(T);
     constexpr int TPR = D / VEC;    // threads per (token, head) row of dY and Y (D = V's head dim)
     constexpr int RPB = 256 / TPR;
-    constexpr int ZPT = DQ / TPR;   // dQ accumulator floats zeroed per thread (DQ = Q's head dim)
-    static_assert(ZPT % 4 == 0, "accumulator row split");
     const int sub = threadIdx.x % TPR;
     const int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
     const bool valid = r < tq * heads;
@@ -116,12 +116,6 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
         const Chunk<T> b = *reinterpret_cast<const Chunk<T>*>(y + t * y_st + n * y_sh + sub * VEC);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) part += static_cast<float>(a.e[e]) * static_cast<float>(b.e[e]);
-        if (dq_acc != nullptr) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4* acc = reinterpret_cast<f32x4*>(dq_acc + (static_cast<int64_t>(n) * tq + t) * DQ + sub * ZPT);
-#pragma unroll
-            for (int e = 0; e < ZPT / 4; ++e) acc[e] = z;
-        }
     }
 #pragma unroll
     for (int m = TPR / 2; m > 0; m >>= 1) part += __shfl_xor(part, m, TPR);
@@ -134,32 +128,6 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
 }
 
 // ----------------------------------------------------------------------------
-// convert: dq = scale * dq_acc
-// ----------------------------------------------------------------------------
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ acc, T* __restrict__ dq, int64_t st,
-                                                      int64_t sh, int64_t tq, int heads, float scale) {
-    constexpr int VEC = 16 / sizeof(T);
-    constexpr int TPR = D / VEC;
-    constexpr int RPB = 256 / TPR;
-    const int sub = threadIdx.x % TPR;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
-    if (r >= tq * heads) return;
-    const int64_t t = r / heads;
-    const int n = static_cast<int>(r - t * heads);
-    const f32x4* src = reinterpret_cast<const f32x4*>(acc + (static_cast<int64_t>(n) * tq + t) * D + sub * VEC);
-    Chunk<T> out;
-#pragma unroll
-    for (int e = 0; e < VEC / 4; ++e) {
-        const f32x4 x = src[e];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out.e[4 * e + i] = cvt<T>(x[i] * scale);
-    }
-    *reinterpret_cast<Chunk<T>*>(dq + t * st + n * sh + sub * VEC) = out;
-}
-
-// ----------------------------------------------------------------------------
 // main kernel
 // ----------------------------------------------------------------------------
 
@@ -169,12 +137,13 @@ struct DevArgs {
     const void* v;
     const void* dy;
     int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, dy_st, dy_sh;
+    void* dq;
     void* dk;
     void* dv;
-    int64_t dk_st, dk_sh, dv_st, dv_sh;
+    int64_t dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh;
     const float2* rowstat;
-    float* dq_acc;
-    const fa_work_item_t* items;
+    const fa_work_item_t* items;    // key-block items (dK / dV)
+    const fa_work_item_t* items_q;  // query-block items (dQ)
     const uint8_t* drop_mask;
     int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float exp_scale, inv_keep, scale;
@@ -195,7 +164,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     constexpr int PQ = DK + PADE;                   // pitch of row-major Q tiles
     constexpr int PD = DV + PADE;                   // pitch of row-major dY tiles
     constexpr int PT = BQ + PADE;                   // pitch of transposed Q / dY tiles
-    constexpr int PS = BKV + PADE;                  // pitch of dS and K^T
     constexpr int VEC = 16 / sizeof(T);
     constexpr int VPRQ = DK / VEC;
     constexpr int VPRD = DV / VEC;
@@ -204,8 +172,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     __shared__ __attribute__((aligned(16))) T sdY[BQ * PD];
     __shared__ __attribute__((aligned(16))) T sQt[DK * PT];
     __shared__ __attribute__((aligned(16))) T sdYt[DV * PT];
-    __shared__ __attribute__((aligned(16))) T sdS[BQ * PS];
-    __shared__ __attribute__((aligned(16))) T sKt[DK * PS];
     __shared__ float2 sStat[BQ];
 
     const fa_work_item_t it = p.items[blockIdx.x];
@@ -237,16 +203,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
         for (int s = 0; s < DV / KS; ++s) {
 #pragma unroll
             for (int e = 0; e < KL; ++e) vset(vreg[s], e, ok ? vr[s * KS + h * KL + e] : static_cast<T>(0.f));
-        }
-        // K^T in LDS for the dQ = dS K contraction (over keys)
-#pragma unroll
-        for (int s = 0; s < DK / KS; ++s) {
-#pragma unroll
-            for (int e = 0; e < KL; ++e) {
-                T x;
-                if constexpr (KL == 1) x = kreg[s]; else x = kreg[s][e];
-                sKt[(s * KS + h * KL + e) * PS + 32 * w + col] = x;
-            }
         }
     }
 
@@ -394,37 +350,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
                     }
                 }
             }
-
-            // dS to LDS as [query][key] so dQ can contract over all 128 keys
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    sdS[(mt * 32 + acc_row(a, h)) * PS + 32 * w + col] = cvt<T>(accP[mt][a]);
-                }
-            }
-            __syncthreads();
-
-            // dQ_acc[tile] += dS K  (unscaled; the convert pass applies scale)
-            for (int tt = w; tt < MT * NTK; tt += 4) {
-                const int mq = tt / NTK;
-                const int nd = tt - mq * NTK;
-                f32x16 acc = zero16();
-#pragma unroll
-                for (int s = 0; s < BKV / KS; ++s) {
-                    const vec a = *reinterpret_cast<const vec*>(&sdS[(mq * 32 + col) * PS + s * KS + h * KL]);
-                    const vec b = *reinterpret_cast<const vec*>(&sKt[(nd * 32 + col) * PS + s * KS + h * KL]);
-                    acc = E::mfma(a, b, acc);
-                }
-#pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    const int i = q0 + mq * 32 + acc_row(a, h);
-                    if (i < L) {
-                        float* dst = p.dq_acc + (static_cast<int64_t>(n) * p.tq + it.q_start + i) * DK + nd * 32 + col;
-                        unsafeAtomicAdd(dst, acc[a]);
-                    }
-                }
-            }
         }
     }  // query heads of the group
 
@@ -444,62 +369,99 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
     }
 }
 
+// dQ for fp32: two lanes per (query qi, query head n), each holding half of the head dims.
+// dQ_i = scale * sum_j dS_ij K_j over the keys j that query i admits, with
+// dS_ij = Ps_ij (dP_ij Z_ij / kp - D_i), Ps_ij = exp2(S_ij * scale * log2 e - beta_i) and
+// dP_ij = dY_i . V_j, summed in key order.
+template <int DK, int DV, bool DROP>
+__global__ __launch_bounds__(2 * FA32_FWD_BLOCK) void bwd_dq32_kernel(const DevArgs p) {
+    constexpr int HK = DK / 2;  // this lane's share of Q / K / dQ columns
+    constexpr int HV = DV / 2;  // ... of dY / V columns
+    const fa_work_item_t it = p.items_q[blockIdx.x];
+    const int n = blockIdx.y;
+    const int L = it.len_q;
+    const int K = it.len_kv;
+    const int half = static_cast<int>(threadIdx.x & 1);
+    const int qi = it.block * FA32_FWD_BLOCK + static_cast<int>(threadIdx.x >> 1);
+    if (qi >= L) return;  // both lanes of a query leave together
+    const int off = K - L;
+    int klo = 0;
+    int khi = K - 1;
+    if (p.mode == FA_MASK_CAUSAL) {
+        khi = min(khi, qi + off);
+    } else if (p.mode == FA_MASK_BAND) {
+        klo = max(klo, qi + off - p.pre);
+        khi = min(khi, qi + off + p.nxt);
+    }
+    const int64_t row = it.q_start + qi;
+    const float* q = static_cast<const float*>(p.q) + row * p.q_st + n * p.q_sh + half * HK;
+    const float* dy = static_cast<const float*>(p.dy) + row * p.dy_st + n * p.dy_sh + half * HV;
+    const int hk = n / p.group;  // the key/value head this query head reads
+    const float* kb = static_cast<const float*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh + half * HK;
+    const float* vb = static_cast<const float*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + hk * p.v_sh + half * HV;
+    float qr[HK];
+    float dyr[HV];
+    float acc[HK];
+#pragma unroll
+    for (int d = 0; d < HK; ++d) {
+        qr[d] = q[d];
+        acc[d] = 0.f;
+    }
+#pragma unroll
+    for (int d = 0; d < HV; ++d) dyr[d] = dy[d];
+    const float2 st = p.rowstat[static_cast<int64_t>(n) * p.tq + row];  // {D_i, beta_i}
+    const int64_t bit0 = it.drop_base + (static_cast<int64_t>(n) * L + qi) * K;
+    for (int j = klo; j <= khi; ++j) {
+        const float* kr = kb + static_cast<int64_t>(j) * p.k_st;
+        const float* vr = vb + static_cast<int64_t>(j) * p.v_st;
+        float sc = 0.f;
+#pragma unroll
+        for (int d = 0; d < HK; ++d) sc = fmaf(qr[d], kr[d], sc);
+        float dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < HV; ++d) dp = fmaf(dyr[d], vr[d], dp);
+        sc += __shfl_xor(sc, 1);  // the two halves of each dot product
+        dp += __shfl_xor(dp, 1);
+        const float pv = __builtin_amdgcn_exp2f(sc * p.exp_scale - st.y);
+        float zk = 1.f;
+        if constexpr (DROP) {
+            const int64_t bit = bit0 + j;
+            zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
+        }
+        const float ds = pv * (dp * zk - st.x);
+#pragma unroll
+        for (int d = 0; d < HK; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
+    }
+    float* dq = static_cast<float*>(p.dq) + row * p.dq_st + n * p.dq_sh + half * HK;
+#pragma unroll
+    for (int d = 0; d < HK; ++d) dq[d] = acc[d] * p.scale;
+}
+
 // ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
 
-template <typename T, int D, int DQ>
-static hipError_t preprocess_t(TensorArg dy, TensorArg y, const float* smax, const float* ssum, float2* rowstat,
-                               float* dq_acc, int64_t tq, int64_t heads, hipStream_t stream) {
-    constexpr int TPR = D / (16 / sizeof(T));
-    constexpr int RPB = 256 / TPR;
-    const int64_t rows = tq * heads;
-    const int64_t blocks = (rows + RPB - 1) / RPB;
-    preprocess_kernel<T, D, DQ><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
-        static_cast<const T*>(dy.data), dy.stride_t, dy.stride_h, static_cast<const T*>(y.data), y.stride_t,
-        y.stride_h, smax, ssum, rowstat, dq_acc, tq, static_cast<int>(heads));
-    return hipGetLastError();
-}
-
-template <typename T>
-static hipError_t preprocess_dims(int dv, int dk, TensorArg dy, TensorArg y, const float* smax, const float* ssum,
-                                  float2* rowstat, float* dq_acc, int64_t tq, int64_t heads, hipStream_t stream) {
-    if (dv == 128 && dk == 128) return preprocess_t<T, 128, 128>(dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
-    if (dv == 64 && dk == 128) return preprocess_t<T, 64, 128>(dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
-    if (dv == 64 && dk == 64) return preprocess_t<T, 64, 64>(dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_preprocess(int32_t dtype, int head_dim_v, int head_dim_k, TensorArg dy, TensorArg y,
-                             const float* smax, const float* ssum, float2* rowstat, float* dq_acc, int64_t tq,
-                             int64_t heads, hipStream_t stream) {
-    if (dtype == FA_BF16)
-        return preprocess_dims<__bf16>(head_dim_v, head_dim_k, dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
-    if (dtype == FA_F16)
-        return preprocess_dims<_Float16>(head_dim_v, head_dim_k, dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
-    return preprocess_dims<float>(head_dim_v, head_dim_k, dy, y, smax, ssum, rowstat, dq_acc, tq, heads, stream);
-}
-
 template <typename T, int D>
-static hipError_t convert_t(const float* acc, void* dq, int64_t st, int64_t sh, int64_t tq, int64_t heads,
-                            float scale, hipStream_t stream) {
+static hipError_t preprocess_t(TensorArg dy, TensorArg y, const float* smax, const float* ssum, float2* rowstat,
+                               int64_t tq, int64_t heads, hipStream_t stream) {
     constexpr int TPR = D / (16 / sizeof(T));
     constexpr int RPB = 256 / TPR;
     const int64_t rows = tq * heads;
     const int64_t blocks = (rows + RPB - 1) / RPB;
-    convert_kernel<T, D><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
-        acc, static_cast<T*>(dq), st, sh, tq, static_cast<int>(heads), scale);
+    preprocess_kernel<T, D><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+        static_cast<const T*>(dy.data), dy.stride_t, dy.stride_h, static_cast<const T*>(y.data), y.stride_t,
+        y.stride_h, smax, ssum, rowstat, tq, static_cast<int>(heads));
     return hipGetLastError();
 }
 
-hipError_t launch_convert(int32_t dtype, int head_dim, const float* dq_acc, void* dq, int64_t dq_st, int64_t dq_sh,
-                          int64_t tq, int64_t heads, float scale, hipStream_t stream) {
-#define FA_CVT(T, D) return convert_t<T, D>(dq_acc, dq, dq_st, dq_sh, tq, heads, scale, stream)
-    if (dtype == FA_BF16) { if (head_dim == 128) FA_CVT(__bf16, 128); FA_CVT(__bf16, 64); }
-    if (dtype == FA_F16) { if (head_dim == 128) FA_CVT(_Float16, 128); FA_CVT(_Float16, 64); }
-    if (head_dim == 128) FA_CVT(float, 128);
-    FA_CVT(float, 64);
-#undef FA_CVT
+hipError_t launch_preprocess(int32_t dtype, int head_dim_v, TensorArg dy, TensorArg y, const float* smax,
+                             const float* ssum, float2* rowstat, int64_t tq, int64_t heads, hipStream_t stream) {
+#define FA_PRE(T, D) return preprocess_t<T, D>(dy, y, smax, ssum, rowstat, tq, heads, stream)
+    if (dtype == FA_BF16) { if (head_dim_v == 128) FA_PRE(__bf16, 128); FA_PRE(__bf16, 64); }
+    if (dtype == FA_F16) { if (head_dim_v == 128) FA_PRE(_Float16, 128); FA_PRE(_Float16, 64); }
+    if (head_dim_v == 128) FA_PRE(float, 128);
+    FA_PRE(float, 64);
+#undef FA_PRE
 }
 
 template <typename T, int DK, int DV, bool DROP>
@@ -509,8 +471,14 @@ static hipError_t main_t(const DevArgs& d, int64_t n_items, int heads, hipStream
     return hipGetLastError();
 }
 
-hipError_t launch_main(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const MainArgs& a,
-                       int64_t n_items, hipStream_t stream) {
+template <int DK, int DV, bool DROP>
+static hipError_t dq32_t(const DevArgs& d, int64_t n_items, int heads, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(n_items), static_cast<unsigned>(heads));
+    bwd_dq32_kernel<DK, DV, DROP><<<grid, dim3(2 * FA32_FWD_BLOCK), 0, stream>>>(d);
+    return hipGetLastError();
+}
+
+static DevArgs dev_args(const MainArgs& a) {
     DevArgs d;
     d.q = a.q.data;
     d.k = a.k.data;
@@ -524,15 +492,18 @@ hipError_t launch_main(int32_t dtype, int head_dim_k, int head_dim_v, bool dropo
     d.v_sh = a.v.stride_h;
     d.dy_st = a.dy.stride_t;
     d.dy_sh = a.dy.stride_h;
+    d.dq = a.dq;
     d.dk = a.dk;
     d.dv = a.dv;
+    d.dq_st = a.dq_st;
+    d.dq_sh = a.dq_sh;
     d.dk_st = a.dk_st;
     d.dk_sh = a.dk_sh;
     d.dv_st = a.dv_st;
     d.dv_sh = a.dv_sh;
     d.rowstat = a.rowstat;
-    d.dq_acc = a.dq_acc;
     d.items = a.items;
+    d.items_q = a.items_q;
     d.drop_mask = a.drop_mask;
     d.tq = a.tq;
     d.heads = a.heads;
@@ -543,6 +514,26 @@ hipError_t launch_main(int32_t dtype, int head_dim_k, int head_dim_v, bool dropo
     d.exp_scale = a.exp_scale;
     d.inv_keep = a.inv_keep;
     d.scale = a.scale;
+    return d;
+}
+
+hipError_t launch_dq32(int head_dim_k, int head_dim_v, bool dropout, const MainArgs& a, int64_t n_items,
+                       hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    const DevArgs d = dev_args(a);
+#define FA_DQ32(DK, DV) \
+    return dropout ? dq32_t<DK, DV, true>(d, n_items, a.heads, stream) : dq32_t<DK, DV, false>(d, n_items, a.heads, stream)
+    if (head_dim_k == 128 && head_dim_v == 128) FA_DQ32(128, 128);
+    if (head_dim_k == 128 && head_dim_v == 64) FA_DQ32(128, 64);
+    if (head_dim_k == 64 && head_dim_v == 64) FA_DQ32(64, 64);
+    return hipErrorInvalidValue;
+#undef FA_DQ32
+}
+
+hipError_t launch_main(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const MainArgs& a,
+                       int64_t n_items, hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    const DevArgs d = dev_args(a);
 #define FA_MAIN(DK, DV)                                                                   \
     return dropout ? main_t<float, DK, DV, true>(d, n_items, a.heads / a.group, stream)     \
                    : main_t<float, DK, DV, false>(d, n_items, a.heads / a.group, stream)
