@@ -41,6 +41,12 @@ Readings of points the page leaves open (each one is listed in the design doc):
       is indexed by the query head.
   R16 Dv < Dk (参数说明: V may have a smaller head dim than Q and K): Y, dY
       and dV have V's head dim, dQ and dK have Q's; nothing else changes.
+  R17 explicit atten_mask (参数说明: attenMaskOptional, 1 = the position takes
+      no part, shapes [B,N,Sq,Skv], [B,1,Sq,Skv], [1,1,Sq,Skv] or [Sq,Skv]):
+      element (b, n, i, j) with sequence-relative i, j and the query head n,
+      size-1 axes broadcast; a pair is admitted when the mode's window admits
+      it and its mask element is 0 (the window and the mask intersect; with
+      no window the mask alone decides).
 
 Every function below computes the plain definition (one library matmul per
 contraction, no blocking beyond splitting query rows into chunks, which only
@@ -87,6 +93,19 @@ def admit_mask(lq: int, lkv: int, mode: int, pre: int = 0, nxt: int = 0,
     raise ValueError(f"unknown mask mode {mode}")
 
 
+def explicit_mask_block(atten_mask, b: int, n: int, lq: int, lkv: int):
+    """Excluded positions (bool [lq, lkv]) of sequence b, query head n, from an explicit mask
+    (R17), or None without one."""
+    if atten_mask is None:
+        return None
+    m = np.asarray(atten_mask)
+    if m.ndim == 4:
+        m = m[b if m.shape[0] > 1 else 0, n if m.shape[1] > 1 else 0]
+    elif m.ndim != 2:
+        raise ValueError("atten_mask must be [B|1, N|1, Sq, Skv] or [Sq, Skv]")
+    return m[:lq, :lkv] != 0
+
+
 def seq_lengths(cu: Sequence[int]) -> np.ndarray:
     cu = np.asarray(cu, dtype=np.int64)
     return cu[1:] - cu[:-1]
@@ -130,7 +149,7 @@ def kv_head(n: int, head_num: int, kv_heads: int) -> int:
 
 def forward_unit(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                  mode: int, pre: int, nxt: int, keep_prob: float,
-                 drop_mask: Optional[np.ndarray], bit0: int):
+                 drop_mask: Optional[np.ndarray], bit0: int, xmask=None):
     """Forward of one (sequence, head): returns Y [Lq, D], m [Lq], l [Lq] in fp64.
 
     S = scale * Q K^T; m_i = max over admitted j; l_i = sum_j exp(S_ij - m_i);
@@ -147,15 +166,23 @@ def forward_unit(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     for c0 in range(0, lq, _ROW_CHUNK):
         rows = np.arange(c0, min(lq, c0 + _ROW_CHUNK))
         y[rows], m[rows], l[rows] = _forward_rows(q[rows], k, v, lq, rows, scale, mode, pre, nxt,
-                                                  keep_prob, drop_mask, bit0)
+                                                  keep_prob, drop_mask, bit0, xmask)
     return y, m, l
 
 
-def _forward_rows(qr, k, v, lq: int, rows, scale, mode, pre, nxt, keep_prob, drop_mask, bit0):
+def _admitted(lq, lkv, mode, pre, nxt, rows, xmask):
+    """Admitted pairs of the given rows: the mode's window without the explicitly masked ones."""
+    a = admit_mask(lq, lkv, mode, pre, nxt, rows)
+    if xmask is not None:
+        a = a & ~xmask[np.asarray(rows, dtype=np.int64)]
+    return a
+
+
+def _forward_rows(qr, k, v, lq: int, rows, scale, mode, pre, nxt, keep_prob, drop_mask, bit0, xmask=None):
     """Y, m, l of the given query rows (sequence-relative), with qr their Q rows (fp64)."""
     lkv = k.shape[0]
     s = scale * (qr @ k.T)
-    a = admit_mask(lq, lkv, mode, pre, nxt, rows)
+    a = _admitted(lq, lkv, mode, pre, nxt, rows, xmask)
     has = a.any(axis=1)
     sm = np.where(a, s, -np.inf)
     mc = sm.max(axis=1, initial=-np.inf)
@@ -168,7 +195,8 @@ def _forward_rows(qr, k, v, lq: int, rows, scale, mode, pre, nxt, keep_prob, dro
 
 
 def forward_rows(q, k, v, cu_q, cu_kv, b: int, n: int, rows, *, mode: int = MASK_NONE, pre: int = 0,
-                 nxt: int = 0, keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int):
+                 nxt: int = 0, keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int,
+                 atten_mask=None):
     """Forward of selected query rows (sequence-relative) of one (b, n): Y [len(rows), D], m, l.
 
     The same definition as forward_unit restricted to those rows (each row needs only its own
@@ -182,11 +210,12 @@ def forward_rows(q, k, v, cu_q, cu_kv, b: int, n: int, rows, *, mode: int = MASK
     qr = np.asarray(q[q0:q1, n], dtype=np.float64)[rows]
     ks = np.asarray(k[k0:k1, hk], dtype=np.float64)
     vs = np.asarray(v[k0:k1, hk], dtype=np.float64)
-    return _forward_rows(qr, ks, vs, q1 - q0, rows, scale, mode, pre, nxt, keep_prob, drop_mask, bit0)
+    xm = explicit_mask_block(atten_mask, b, n, q1 - q0, k1 - k0)
+    return _forward_rows(qr, ks, vs, q1 - q0, rows, scale, mode, pre, nxt, keep_prob, drop_mask, bit0, xm)
 
 
 def forward(q, k, v, cu_q, cu_kv, *, mode: int = MASK_NONE, pre: int = 0, nxt: int = 0,
-            keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int):
+            keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int, atten_mask=None):
     """Varlen forward over TND tensors; returns Y [T, N, Dv], m [N, T], l [N, T] (fp64).
 
     q is [Tq, N, Dk]; k and v are [Tkv, Nkv, Dk] and [Tkv, Nkv, Dv] with N a multiple of Nkv (R15).
@@ -205,7 +234,8 @@ def forward(q, k, v, cu_q, cu_kv, *, mode: int = MASK_NONE, pre: int = 0, nxt: i
             bit0 = int(bases[b]) + n * (q1 - q0) * (k1 - k0)
             hk = kv_head(n, head_num, k.shape[1])
             yb, mb, lb = forward_unit(q[q0:q1, n], k[k0:k1, hk], v[k0:k1, hk], scale,
-                                      mode, pre, nxt, keep_prob, drop_mask, bit0)
+                                      mode, pre, nxt, keep_prob, drop_mask, bit0,
+                                      explicit_mask_block(atten_mask, b, n, q1 - q0, k1 - k0))
             y[q0:q1, n] = yb
             m[n, q0:q1] = mb
             l[n, q0:q1] = lb
@@ -232,7 +262,7 @@ def _probs(s, a, m, l):
 
 
 def backward_unit(q, k, v, dy, y, m, l, scale: float, mode: int, pre: int, nxt: int,
-                  keep_prob: float, drop_mask, bit0: int, want_ds: bool = False):
+                  keep_prob: float, drop_mask, bit0: int, want_ds: bool = False, xmask=None):
     """Backward of one (sequence, head) in fp64.
 
     Inputs are the [L, D] slices of Q, dY, Y and the [Lkv, D] slices of K, V,
@@ -264,7 +294,7 @@ def backward_unit(q, k, v, dy, y, m, l, scale: float, mode: int, pre: int, nxt: 
     for c0 in range(0, lq, _ROW_CHUNK):
         rows = np.arange(c0, min(lq, c0 + _ROW_CHUNK))
         s = scale * (q[rows] @ k.T)
-        a = admit_mask(lq, lkv, mode, pre, nxt, rows)
+        a = _admitted(lq, lkv, mode, pre, nxt, rows, xmask)
         ps = _probs(s, a, m[rows], l[rows])
         if keep_prob < 1.0:
             zk = dropout_keep(drop_mask, bit0, rows, lkv) / keep_prob
@@ -289,14 +319,16 @@ def _stat0(stat):
     return stat[..., 0] if stat.ndim == 3 else stat
 
 
-def _unit_args(b, n, q, k, v, dy, y, mstat, lstat, cu_q, cu_kv, bases):
-    """Slices of query head n of sequence b, with the key/value head it reads (R15)."""
+def _unit_args(b, n, q, k, v, dy, y, mstat, lstat, cu_q, cu_kv, bases, atten_mask=None):
+    """Slices of query head n of sequence b, with the key/value head it reads (R15) and the
+    unit's explicitly masked positions (R17, or None)."""
     q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
     k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
     bit0 = int(bases[b]) + n * (q1 - q0) * (k1 - k0)
     hk = kv_head(n, q.shape[1], k.shape[1])
     return (q[q0:q1, n], k[k0:k1, hk], v[k0:k1, hk], dy[q0:q1, n], y[q0:q1, n],
-            mstat[n, q0:q1], lstat[n, q0:q1], bit0)
+            mstat[n, q0:q1], lstat[n, q0:q1], bit0,
+            explicit_mask_block(atten_mask, b, n, q1 - q0, k1 - k0))
 
 
 _POOL_STATE = {}
@@ -310,16 +342,16 @@ def _pool_init(state):
 def _pool_unit(job):
     b, n = job
     st = _POOL_STATE
-    qs, ks, vs, dys, ys, ms, ls, bit0 = _unit_args(
+    qs, ks, vs, dys, ys, ms, ls, bit0, xm = _unit_args(
         b, n, st["q"], st["k"], st["v"], st["dy"], st["y"], st["m"], st["l"],
-        st["cu_q"], st["cu_kv"], st["bases"])
+        st["cu_q"], st["cu_kv"], st["bases"], st["atten_mask"])
     return (b, n) + backward_unit(qs, ks, vs, dys, ys, ms, ls, st["scale"], st["mode"],
-                                  st["pre"], st["nxt"], st["keep_prob"], st["drop_mask"], bit0)
+                                  st["pre"], st["nxt"], st["keep_prob"], st["drop_mask"], bit0, xmask=xm)
 
 
 def backward(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, *, mode: int = MASK_NONE,
              pre: int = 0, nxt: int = 0, keep_prob: float = 1.0, drop_mask=None,
-             scale: float, head_num: int, workers: int = 1, units=None):
+             scale: float, head_num: int, workers: int = 1, units=None, atten_mask=None):
     """Varlen backward over TND tensors; returns dQ [Tq, N, Dk], dK [Tkv, Nkv, Dk], dV [Tkv, Nkv, Dv] in fp64.
 
     Rows or keys that no admitted pair touches stay exactly 0.  `units` may
@@ -348,16 +380,16 @@ def backward(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, *, mode: int
 
     if workers <= 1 or len(units) <= 1:
         for b, n in units:
-            qs, ks, vs, dys, ys, ms, ls, bit0 = _unit_args(b, n, q, k, v, dy, y, mstat, lstat,
-                                                           cu_q, cu_kv, bases)
+            qs, ks, vs, dys, ys, ms, ls, bit0, xm = _unit_args(b, n, q, k, v, dy, y, mstat, lstat,
+                                                               cu_q, cu_kv, bases, atten_mask)
             put(b, n, *backward_unit(qs, ks, vs, dys, ys, ms, ls, scale, mode, pre, nxt,
-                                     keep_prob, drop_mask, bit0))
+                                     keep_prob, drop_mask, bit0, xmask=xm))
         return dq, dk, dv
 
     import multiprocessing as mp
     state = dict(q=q, k=k, v=v, dy=dy, y=y, m=mstat, l=lstat, cu_q=cu_q, cu_kv=cu_kv,
                  bases=bases, scale=scale, mode=mode, pre=pre, nxt=nxt,
-                 keep_prob=keep_prob, drop_mask=drop_mask)
+                 keep_prob=keep_prob, drop_mask=drop_mask, atten_mask=atten_mask)
     ctx = mp.get_context("fork")
     # one BLAS thread per worker: the pool supplies the parallelism
     old = {key: os.environ.get(key) for key in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
@@ -382,7 +414,7 @@ def backward(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, *, mode: int
 
 def backward_dq_rows(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b: int, n: int,
                      rows, *, mode: int = MASK_NONE, pre: int = 0, nxt: int = 0,
-                     keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int):
+                     keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int, atten_mask=None):
     """dQ for selected query rows (sequence-relative) of one (b, n): [len(rows), D] fp64.
 
     The same definition as backward_unit restricted to those rows: each needs
@@ -390,8 +422,8 @@ def backward_dq_rows(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b: i
     """
     mstat, lstat = _stat0(softmax_max), _stat0(softmax_sum)
     bases = dropout_bit_bases(cu_q, cu_kv, head_num)
-    qs, ks, vs, dys, ys, ms, ls, bit0 = _unit_args(b, n, q, k, v, dy, y, mstat, lstat,
-                                                   np.asarray(cu_q), np.asarray(cu_kv), bases)
+    qs, ks, vs, dys, ys, ms, ls, bit0, xm = _unit_args(b, n, q, k, v, dy, y, mstat, lstat,
+                                                       np.asarray(cu_q), np.asarray(cu_kv), bases, atten_mask)
     rows = np.asarray(rows, dtype=np.int64)
     qs = np.asarray(qs, dtype=np.float64)[rows]
     ks = np.asarray(ks, dtype=np.float64)
@@ -402,7 +434,7 @@ def backward_dq_rows(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b: i
     ls = np.asarray(ls, dtype=np.float64)[rows]
     lq = int(cu_q[b + 1] - cu_q[b])
     s = scale * (qs @ ks.T)
-    a = admit_mask(lq, ks.shape[0], mode, pre, nxt, rows)
+    a = _admitted(lq, ks.shape[0], mode, pre, nxt, rows, xm)
     ps = _probs(s, a, ms, ls)
     zk = dropout_keep(drop_mask, bit0, rows, ks.shape[0]) / keep_prob if keep_prob < 1.0 else 1.0
     delta = np.sum(dys * ys, axis=1)
@@ -412,7 +444,7 @@ def backward_dq_rows(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b: i
 
 def backward_dkdv_cols(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b: int, n: int,
                        cols, *, mode: int = MASK_NONE, pre: int = 0, nxt: int = 0,
-                       keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int):
+                       keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int, atten_mask=None):
     """dK and dV for selected keys (sequence-relative) of key/value head n of sequence b.
 
     Returns two [len(cols), Dk] and [len(cols), Dv] fp64 arrays: the sums over the query heads
@@ -425,19 +457,19 @@ def backward_dkdv_cols(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b:
     dv = np.zeros((cols.size, v.shape[2]), dtype=np.float64)
     for nq in range(n * group, (n + 1) * group):
         a, c = _dkdv_cols_one_head(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b, nq, cols,
-                                   mode, pre, nxt, keep_prob, drop_mask, scale, head_num)
+                                   mode, pre, nxt, keep_prob, drop_mask, scale, head_num, atten_mask)
         dk += a
         dv += c
     return dk, dv
 
 
 def _dkdv_cols_one_head(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b, n, cols, mode, pre, nxt,
-                        keep_prob, drop_mask, scale, head_num):
+                        keep_prob, drop_mask, scale, head_num, atten_mask=None):
     """Contribution of query head n to dK and dV of the selected keys of its key/value head."""
     mstat, lstat = _stat0(softmax_max), _stat0(softmax_sum)
     bases = dropout_bit_bases(cu_q, cu_kv, head_num)
-    qs, ks, vs, dys, ys, ms, ls, bit0 = _unit_args(b, n, q, k, v, dy, y, mstat, lstat,
-                                                   np.asarray(cu_q), np.asarray(cu_kv), bases)
+    qs, ks, vs, dys, ys, ms, ls, bit0, xm = _unit_args(b, n, q, k, v, dy, y, mstat, lstat,
+                                                       np.asarray(cu_q), np.asarray(cu_kv), bases, atten_mask)
     lq, lkv = qs.shape[0], ks.shape[0]
     qs = np.asarray(qs, dtype=np.float64)
     kc = np.asarray(ks, dtype=np.float64)[cols]
@@ -450,7 +482,7 @@ def _dkdv_cols_one_head(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, b
         dyr = np.asarray(dys[rows], dtype=np.float64)
         yr = np.asarray(ys[rows], dtype=np.float64)
         s = scale * (qr @ kc.T)
-        a_full = admit_mask(lq, lkv, mode, pre, nxt, rows)
+        a_full = _admitted(lq, lkv, mode, pre, nxt, rows, xm)
         ps = _probs_cols(s, a_full[:, cols], np.asarray(ms[rows], dtype=np.float64),
                          np.asarray(ls[rows], dtype=np.float64), a_full.any(axis=1))
         if keep_prob < 1.0:

@@ -45,11 +45,20 @@ MODES = [
 ]
 
 
-def _full_backward(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, heads):
+def _full_backward(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, heads, atten_mask=None):
     y, m, l = O.forward(q, k, v, cu_q, cu_kv, mode=mode, pre=pre, nxt=nxt, keep_prob=kp,
-                        drop_mask=drop, scale=scale, head_num=heads)
+                        drop_mask=drop, scale=scale, head_num=heads, atten_mask=atten_mask)
     return O.backward(q, k, v, dy, y, m, l, cu_q, cu_kv, mode=mode, pre=pre, nxt=nxt,
-                      keep_prob=kp, drop_mask=drop, scale=scale, head_num=heads), (y, m, l)
+                      keep_prob=kp, drop_mask=drop, scale=scale, head_num=heads,
+                      atten_mask=atten_mask), (y, m, l)
+
+
+def _rand_mask(rng, shape, frac=0.3, empty_row=True):
+    """A random explicit mask (1 = excluded) with, optionally, one fully excluded row."""
+    m = (rng.random(shape) < frac).astype(np.uint8)
+    if empty_row:
+        m[..., 1, :] = 1
+    return m
 
 
 # --- P1: central finite differences of L = sum(dY o Y(Q, K, V)) ---------------------------
@@ -122,7 +131,7 @@ def test_p1_finite_differences_grouped_heads_and_narrow_v(mode, pre, nxt, heads,
 
 # --- P2/P4: torch fp64 autograd of a dense padded formulation -----------------------------
 
-def _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, heads):
+def _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scale, heads, atten_mask=None):
     """softmax(scale*QK^T + additive mask) V on [B, N, Smax, D] with padding masked out.
 
     The mask is built from torch.tril/triu diagonals (an independent construction of the
@@ -161,6 +170,13 @@ def _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, scal
             win = torch.tril(ones, diagonal=off + nxt) & torch.triu(ones, diagonal=off - pre)
         for n in range(heads):
             allow[b, n, :a, :c] = win
+            if atten_mask is not None:
+                # the page's mask: 1 excludes; size-1 batch / head axes broadcast
+                tm = torch.as_tensor(atten_mask)
+                if tm.dim() == 2:
+                    tm = tm[None, None]
+                blk = tm[b % tm.shape[0], n % tm.shape[1], :a, :c]
+                allow[b, n, :a, :c] &= blk == 0
             if allbits is not None:
                 blk = allbits[pos:pos + a * c].reshape(a, c)
                 zmul[b, n, :a, :c] = torch.from_numpy(blk.astype(np.float64)) / kp
@@ -216,6 +232,79 @@ def test_p2_torch_autograd_grouped_heads_and_narrow_v(mode, pre, nxt, heads, kv_
     for g, r in ((dq, rq), (dk, rk), (dv, rv)):
         assert g.shape == r.shape
         assert np.max(np.abs(g - r)) <= 1e-12 * max(1.0, np.max(np.abs(r)))
+
+
+@pytest.mark.parametrize("mode,pre,nxt", [(O.MASK_NONE, 0, 0), (O.MASK_CAUSAL, 0, 0), (O.MASK_BAND, 6, 2)])
+@pytest.mark.parametrize("shape_kind", ["bnqk", "b1qk", "qk"])
+@pytest.mark.parametrize("kp", [1.0, 0.8])
+def test_p2_torch_autograd_explicit_mask(mode, pre, nxt, shape_kind, kp):
+    # R17: the explicit mask intersects the window; rows it empties give zero gradients
+    rng = np.random.default_rng(90 + mode)
+    lq, lkv = (23, 9, 31), (17, 9, 40)
+    heads = 4
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, lq, lkv, heads=heads, dim=8, keep_prob=kp, kv_heads=2)
+    sq, sk = max(lq) + 3, max(lkv) + 2  # larger than every sequence: only the leading block is read
+    shape = {"bnqk": (3, heads, sq, sk), "b1qk": (3, 1, sq, sk), "qk": (sq, sk)}[shape_kind]
+    am = _rand_mask(rng, shape)
+    (dq, dk, dv), _ = _full_backward(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, 0.4, heads, am)
+    rq, rk, rv = _torch_padded_grads(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, kp, drop, 0.4, heads, am)
+    for g, r in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.max(np.abs(g - r)) <= 1e-12 * max(1.0, np.max(np.abs(r)))
+
+
+def test_p1_finite_differences_explicit_mask():
+    rng = np.random.default_rng(93)
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, (5, 4), (6, 7), heads=2, dim=4, keep_prob=0.7)
+    am = _rand_mask(rng, (2, 2, 5, 7), frac=0.4)
+    (dq, dk, dv), _ = _full_backward(q, k, v, dy, cu_q, cu_kv, O.MASK_BAND, 2, 1, 0.7, drop, 0.6, 2, am)
+
+    def loss(qq, kk, vv):
+        y, _, _ = O.forward(qq, kk, vv, cu_q, cu_kv, mode=O.MASK_BAND, pre=2, nxt=1, keep_prob=0.7,
+                            drop_mask=drop, scale=0.6, head_num=2, atten_mask=am)
+        return float(np.sum(dy * y))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args[name] = xp
+            fp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            fm = loss(args["q"], args["k"], args["v"])
+            fd[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(fd - g)) / max(np.max(np.abs(fd)), 1e-12) <= 1e-6, name
+
+
+def test_explicit_mask_reproduces_the_generated_windows():
+    # an explicit mask holding the causal (band) pattern with no window == the generated window
+    rng = np.random.default_rng(95)
+    lq, lkv = (30, 12), (26, 19)
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, lq, lkv, heads=2, dim=8, keep_prob=0.9)
+    for mode, pre, nxt in ((O.MASK_CAUSAL, 0, 0), (O.MASK_BAND, 5, 3)):
+        am = np.ones((2, 1, 30, 26), dtype=np.uint8)
+        for b in range(2):
+            am[b, 0, :lq[b], :lkv[b]] = ~O.admit_mask(lq[b], lkv[b], mode, pre, nxt)
+        ref, (y0, _, _) = _full_backward(q, k, v, dy, cu_q, cu_kv, mode, pre, nxt, 0.9, drop, 0.3, 2)
+        got, (y1, _, _) = _full_backward(q, k, v, dy, cu_q, cu_kv, O.MASK_NONE, 0, 0, 0.9, drop, 0.3, 2, am)
+        np.testing.assert_array_equal(y0, y1)
+        for a, c in zip(ref, got):
+            np.testing.assert_array_equal(a, c)
+
+
+def test_explicit_mask_broadcast_shapes_agree():
+    rng = np.random.default_rng(96)
+    q, k, v, dy, cu_q, cu_kv, _ = _rand_case(rng, (11, 7), (9, 13), heads=3, dim=8)
+    base = _rand_mask(rng, (12, 14))
+    outs = []
+    for am in (base, base[None, None], np.broadcast_to(base, (2, 3, 12, 14)).copy(),
+               np.broadcast_to(base, (2, 1, 12, 14)).copy()):
+        outs.append(_full_backward(q, k, v, dy, cu_q, cu_kv, O.MASK_CAUSAL, 0, 0, 1.0, None, 0.5, 3, am)[0])
+    for o in outs[1:]:
+        for a, c in zip(outs[0], o):
+            np.testing.assert_array_equal(a, c)
 
 
 def test_forward_matches_torch_logsumexp():
@@ -422,6 +511,30 @@ def test_sampled_outputs_equal_full_grouped_heads():
             r = O.backward_dq_rows(q, k, v, dy, y, m, l, cu_q, cu_kv, b, n, rows, **kw)
             np.testing.assert_allclose(r, dq[cu_q[b] + rows, n], rtol=0, atol=1e-13)
             yr, mr, lr = O.forward_rows(q, k, v, cu_q, cu_kv, b, n, rows, **kw)
+            np.testing.assert_array_equal(yr, yf[cu_q[b] + rows, n])
+        for hk in range(kv_heads):
+            gk, gv = O.backward_dkdv_cols(q, k, v, dy, y, m, l, cu_q, cu_kv, b, hk, cols, **kw)
+            np.testing.assert_allclose(gk, dk[cu_kv[b] + cols, hk], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(gv, dv[cu_kv[b] + cols, hk], rtol=0, atol=1e-13)
+
+
+def test_sampled_outputs_equal_full_explicit_mask():
+    rng = np.random.default_rng(47)
+    heads, kv_heads, kp = 4, 2, 0.85
+    lq, lkv = (21, 14), (17, 25)
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, lq, lkv, heads=heads, dim=8, keep_prob=kp, kv_heads=kv_heads)
+    am = _rand_mask(rng, (2, heads, 21, 25))
+    (dq, dk, dv), (y, m, l) = _full_backward(q, k, v, dy, cu_q, cu_kv, O.MASK_CAUSAL, 0, 0, kp, drop, 0.3, heads,
+                                             am)
+    kw = dict(mode=O.MASK_CAUSAL, keep_prob=kp, drop_mask=drop, scale=0.3, head_num=heads, atten_mask=am)
+    yf, _, _ = O.forward(q, k, v, cu_q, cu_kv, **kw)
+    for b in range(2):
+        rows = np.array([0, 1, 4, lq[b] - 1])
+        cols = np.array([0, 7, lkv[b] - 1])
+        for n in range(heads):
+            r = O.backward_dq_rows(q, k, v, dy, y, m, l, cu_q, cu_kv, b, n, rows, **kw)
+            np.testing.assert_allclose(r, dq[cu_q[b] + rows, n], rtol=0, atol=1e-13)
+            yr, _, _ = O.forward_rows(q, k, v, cu_q, cu_kv, b, n, rows, **kw)
             np.testing.assert_array_equal(yr, yf[cu_q[b] + rows, n])
         for hk in range(kv_heads):
             gk, gv = O.backward_dkdv_cols(q, k, v, dy, y, m, l, cu_q, cu_kv, b, hk, cols, **kw)
