@@ -64,6 +64,24 @@ typedef struct {
     int64_t        batch;
 } fa_seqlens_t;
 
+/* An explicit attention mask (the page's attenMaskOptional: parameter table, atten_mask in the
+ * formulas section): DEVICE uint8 (or bool) elements, nonzero = the pair takes no part.
+ * Element (b, n, i, j) -- sequence b, query head n, sequence-relative query i and key j -- is
+ * data[b * stride_b + n * stride_n + i * stride_q + j].  The page's shapes map to
+ *   [B, N, Sq, Skv]  stride_b = N*Sq*Skv, stride_n = Sq*Skv, stride_q = Skv
+ *   [B, 1, Sq, Skv]  stride_n = 0;   [1, 1, Sq, Skv] and [Sq, Skv]: stride_b = stride_n = 0.
+ * rows >= every Lq_b and cols >= every Lkv_b (Sq, Skv); stride_q >= cols; strides >= 0.  Only
+ * elements with i < Lq_b and j < Lkv_b are read.  A pair is admitted when the window of
+ * atten_mode admits it and its mask element is 0 (with FA_MASK_NONE the mask alone decides). */
+typedef struct {
+    const uint8_t* data;
+    int64_t        stride_b;
+    int64_t        stride_n;
+    int64_t        stride_q;
+    int64_t        rows;
+    int64_t        cols;
+} fa_mask_t;
+
 /* Status codes.  FA_ERR_NULLPTR and FA_ERR_INVALID mirror the page's
  * ACLNN_ERR_PARAM_NULLPTR (161001) and ACLNN_ERR_PARAM_INVALID (161002). */
 enum {
@@ -129,6 +147,24 @@ int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t*
                   double scale, int64_t head_num,
                   const fa_tensor_t* dq, const fa_tensor_t* dk, const fa_tensor_t* dv,
                   void* stream);
+
+/*
+ * fa_varlen_bwd_masked -- fa_varlen_bwd with an explicit attention mask (the page's
+ * attenMaskOptional, parameter table): every argument as for fa_varlen_bwd, plus atten_mask
+ * (a fa_mask_t, see above; NULL = none, which is exactly fa_varlen_bwd).
+ * Additional status codes: FA_ERR_NULLPTR when atten_mask->data is NULL; FA_ERR_INVALID when
+ * rows / cols do not cover every sequence, a stride is negative or stride_q < cols;
+ * FA_ERR_UNSUPPORTED when one (sequence, head) block spans 2^31 bytes or more.
+ */
+int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                         const fa_tensor_t* dy, const fa_tensor_t* y,
+                         const float* softmax_max, const float* softmax_sum,
+                         const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
+                         int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens,
+                         double keep_prob, const uint8_t* drop_mask, const fa_mask_t* atten_mask,
+                         double scale, int64_t head_num,
+                         const fa_tensor_t* dq, const fa_tensor_t* dk, const fa_tensor_t* dv,
+                         void* stream);
 
 /* Thread-local description of the last non-OK status (empty string if none). */
 const char* fa_last_error(void);
@@ -213,6 +249,16 @@ int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t*
                   int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens, double keep_prob,
                   const uint8_t* drop_mask, double scale, int64_t head_num, const fa_tensor_t* y,
                   float* softmax_max, float* softmax_sum, void* stream);
+
+/* fa_varlen_fwd with an explicit attention mask (NULL = none): the forward counterpart of
+ * fa_varlen_bwd_masked, with the same mask rules and status codes.  A row whose keys are all
+ * excluded gets max -inf, sum 0 and a zero Y row. */
+int fa_varlen_fwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                         const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
+                         int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens, double keep_prob,
+                         const uint8_t* drop_mask, const fa_mask_t* atten_mask, double scale,
+                         int64_t head_num, const fa_tensor_t* y, float* softmax_max, float* softmax_sum,
+                         void* stream);
 
 /* Measured matrix-core ceiling of the current device (a diagnostic, not part of the
  * operator): runs a kernel of independent bf16 32x32x16 MFMAs, one workgroup per compute

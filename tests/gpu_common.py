@@ -37,24 +37,24 @@ def assert_close(name, g, o, dtype):
     assert np.max(np.abs(g - o)) <= 5e-2 * mx, f"{name}: max abs error {np.max(np.abs(g - o)):.3e} vs {mx:.3e}"
 
 
-def oracle_forward(inp, mode, pre, nxt, kp, scale):
+def oracle_forward(inp, mode, pre, nxt, kp, scale, atten_mask=None):
     q, k, v = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v))
     y, m, l = O.forward(q, k, v, inp.cu_q, inp.cu_kv, mode=mode, pre=pre, nxt=nxt, keep_prob=kp,
-                        drop_mask=inp.drop_mask, scale=scale, head_num=inp.q.shape[1])
+                        drop_mask=inp.drop_mask, scale=scale, head_num=inp.q.shape[1], atten_mask=atten_mask)
     yt = torch.from_numpy(y).to(inp.q.dtype)
     smax, ssum = O.stats_to_page_layout(m, l)
     return yt, smax, ssum
 
 
-def oracle_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, workers=4):
+def oracle_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, workers=4, atten_mask=None):
     q, k, v, dy = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v, inp.dy))
     y = synth.as_float_array(yt)
     return O.backward(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, mode=mode, pre=pre, nxt=nxt,
                       keep_prob=kp, drop_mask=inp.drop_mask, scale=scale, head_num=inp.q.shape[1],
-                      workers=workers)
+                      workers=workers, atten_mask=atten_mask)
 
 
-def gpu_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, views=None):
+def gpu_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, views=None, atten_mask=None):
     dev = torch.device(DEV)
     q, k, v, dy, y = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.dy, yt))
     smax_d = torch.as_tensor(np.ascontiguousarray(smax)).to(dev)
@@ -68,25 +68,31 @@ def gpu_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, views=None):
     # poison the outputs: every element must be written by the library
     for t in (dq, dk, dv):
         t.fill_(float("nan"))
-    B.fa_varlen_bwd(q, k, v, dy, y, smax_d, ssum_d, inp.cu_q, inp.cu_kv, mode, pre, nxt, kp, drop, scale,
-                    q.shape[1], dq, dk, dv)
+    if atten_mask is None:
+        B.fa_varlen_bwd(q, k, v, dy, y, smax_d, ssum_d, inp.cu_q, inp.cu_kv, mode, pre, nxt, kp, drop, scale,
+                        q.shape[1], dq, dk, dv)
+    else:
+        am = torch.from_numpy(np.ascontiguousarray(atten_mask)).to(dev)
+        B.fa_varlen_bwd_masked(q, k, v, dy, y, smax_d, ssum_d, inp.cu_q, inp.cu_kv, mode, pre, nxt, kp, drop, am,
+                               scale, q.shape[1], dq, dk, dv)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 
-def run_small(inp, mode, pre=0, nxt=0, kp=1.0, scale=None, poison_empty=False, views=None):
+def run_small(inp, mode, pre=0, nxt=0, kp=1.0, scale=None, poison_empty=False, views=None, atten_mask=None):
     scale = scale if scale is not None else 1.0 / np.sqrt(inp.q.shape[2])
     log(f"case T={inp.q.shape[0]} N={inp.q.shape[1]} D={inp.q.shape[2]} {inp.q.dtype} mode={mode} "
-        f"pre={pre} nxt={nxt} kp={kp} lens={np.diff(inp.cu_q).tolist()[:12]}")
-    yt, smax, ssum = oracle_forward(inp, mode, pre, nxt, kp, scale)
+        f"pre={pre} nxt={nxt} kp={kp} lens={np.diff(inp.cu_q).tolist()[:12]} "
+        f"mask={None if atten_mask is None else atten_mask.shape}")
+    yt, smax, ssum = oracle_forward(inp, mode, pre, nxt, kp, scale, atten_mask=atten_mask)
     if poison_empty:
         empty = ~np.isfinite(smax[:, :, 0]) | (ssum[:, :, 0] == 0)
         assert empty.any()
         smax = smax.copy(); ssum = ssum.copy()
         smax[empty] = np.nan
         ssum[empty] = np.nan
-    ref = oracle_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale)
-    got = gpu_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, views=views)
+    ref = oracle_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, atten_mask=atten_mask)
+    got = gpu_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, views=views, atten_mask=atten_mask)
     for name, g, o in zip(("dq", "dk", "dv"), got, ref):
         assert_close(name, g.double().numpy(), o, inp.q.dtype)
     return got, ref, (yt, smax, ssum)

@@ -34,7 +34,8 @@ def _header_functions():
 def test_library_exports_every_header_function():
     lib = B.load()
     names = _header_functions()
-    assert {"fa_varlen_bwd", "fa_last_error", "fa_release", "fa_varlen_worklist"} <= names
+    assert {"fa_varlen_bwd", "fa_varlen_bwd_masked", "fa_varlen_fwd", "fa_varlen_fwd_masked", "fa_last_error",
+            "fa_release", "fa_varlen_worklist"} <= names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -158,6 +159,69 @@ def test_narrow_v_validation():
     args.update({n: _t(0, dim=64, data=0) for n in ("v", "dv", "dy", "y")})
     st, msg = _call(cu_q=(0, 0), cu_kv=(0, 0), **args)
     assert st == B.FA_OK, msg
+
+
+def _mcall(mask, **kw):
+    """fa_varlen_bwd_masked with the default valid arguments of _call and the given mask view."""
+    cu_q, cu_kv = kw.pop("cu_q", (0, 10)), kw.pop("cu_kv", (0, 10))
+    tq, tk = cu_q[-1], cu_kv[-1]
+    t = {n: kw.pop(n, _t(tq if n in ("q", "dy", "y", "dq") else tk)) for n in ("q", "k", "v", "dy", "y", "dq", "dk", "dv")}
+    aq = np.asarray(cu_q, dtype=np.int64)
+    ak = np.asarray(cu_kv, dtype=np.int64)
+    sq = B.FaSeqlens(aq.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), aq.size - 1)
+    sk = B.FaSeqlens(ak.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ak.size - 1)
+    lib = B.load()
+    r = ctypes.byref
+    st = lib.fa_varlen_bwd_masked(r(t["q"]), r(t["k"]), r(t["v"]), r(t["dy"]), r(t["y"]), ctypes.c_void_p(FAKE),
+                                  ctypes.c_void_p(FAKE), r(sq), r(sk), 0, 0, 0, 1.0, None,
+                                  None if mask is None else r(mask), 0.125, 2, r(t["dq"]), r(t["dk"]), r(t["dv"]),
+                                  None)
+    return st, lib.fa_last_error().decode()
+
+
+def _mask(data=FAKE, sb=0, sn=0, sq=16, rows=10, cols=10):
+    return B.FaMask(ctypes.c_void_p(data), sb, sn, sq, rows, cols)
+
+
+def test_explicit_mask_validation():
+    assert _mcall(_mask(data=0))[0] == B.FA_ERR_NULLPTR
+    assert _mcall(_mask(rows=9))[0] == B.FA_ERR_INVALID          # rows < Lq
+    assert _mcall(_mask(cols=9, sq=9))[0] == B.FA_ERR_INVALID    # cols < Lkv
+    assert _mcall(_mask(sq=8))[0] == B.FA_ERR_INVALID            # stride_q < cols
+    assert _mcall(_mask(sb=-1))[0] == B.FA_ERR_INVALID
+    assert _mcall(_mask(sq=1 << 28))[0] == B.FA_ERR_UNSUPPORTED  # a block spans >= 2^31 bytes
+    st, msg = _mcall(_mask(data=0), cu_q=(0, 0), cu_kv=(0, 0), **{n: _t(0, data=0) for n in
+                                                                    ("q", "k", "v", "dy", "y", "dq", "dk", "dv")})
+    assert st == B.FA_OK, msg
+
+
+def test_explicit_mask_forward_validation():
+    lib = B.load()
+    aq = np.asarray((0, 10), dtype=np.int64)
+    sq = B.FaSeqlens(aq.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1)
+    r = ctypes.byref
+    q, k, v, y = _t(10), _t(10), _t(10), _t(10)
+
+    def call(m):
+        return lib.fa_varlen_fwd_masked(r(q), r(k), r(v), r(sq), r(sq), 0, 0, 0, 1.0, None, r(m), 0.125, 2, r(y),
+                                        ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None)
+
+    assert call(_mask(data=0)) == B.FA_ERR_NULLPTR
+    assert call(_mask(rows=3)) == B.FA_ERR_INVALID
+    assert call(_mask(sq=1 << 28)) == B.FA_ERR_UNSUPPORTED
+
+
+def test_mask_desc_strides():
+    import torch
+    m = torch.zeros(3, 4, 20, 30, dtype=torch.uint8)
+    d = B.mask_desc(m)
+    assert (d.stride_b, d.stride_n, d.stride_q, d.rows, d.cols) == (2400, 600, 30, 20, 30)
+    d = B.mask_desc(m[:, :1])
+    assert (d.stride_b, d.stride_n) == (2400, 0)
+    d = B.mask_desc(torch.zeros(20, 30, dtype=torch.bool))
+    assert (d.stride_b, d.stride_n, d.stride_q) == (0, 0, 30)
+    with pytest.raises(ValueError):
+        B.mask_desc(torch.zeros(20, 30, dtype=torch.float32))
 
 
 def test_empty_query_returns_ok_without_device_work():

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def gpu_forward(inp, mode, pre, nxt, kp, scale, views=None):
+def gpu_forward(inp, mode, pre, nxt, kp, scale, views=None, atten_mask=None):
     dev = torch.device(DEV)
     q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
     drop = torch.from_numpy(inp.drop_mask).to(dev) if inp.drop_mask is not None else None
@@ -30,7 +30,12 @@ def gpu_forward(inp, mode, pre, nxt, kp, scale, views=None):
     ssum = torch.empty_like(smax)
     for t in (y, smax, ssum):
         t.fill_(float("nan"))  # every element must be written
-    B.fa_varlen_fwd(q, k, v, inp.cu_q, inp.cu_kv, mode, pre, nxt, kp, drop, scale, q.shape[1], y, smax, ssum)
+    if atten_mask is None:
+        B.fa_varlen_fwd(q, k, v, inp.cu_q, inp.cu_kv, mode, pre, nxt, kp, drop, scale, q.shape[1], y, smax, ssum)
+    else:
+        am = torch.from_numpy(np.ascontiguousarray(atten_mask)).to(dev)
+        B.fa_varlen_fwd_masked(q, k, v, inp.cu_q, inp.cu_kv, mode, pre, nxt, kp, drop, am, scale, q.shape[1], y,
+                               smax, ssum)
     torch.cuda.synchronize()
     return y.cpu(), smax.cpu().numpy(), ssum.cpu().numpy()
 
@@ -46,14 +51,14 @@ def check_stats(gm, gl, m, l, dtype):
     np.testing.assert_allclose(gl[~empty], l[~empty], rtol=1e-5 if dtype == torch.float32 else 1e-3, atol=0)
 
 
-def run_fwd(inp, mode, pre=0, nxt=0, kp=1.0, scale=None, views=None):
+def run_fwd(inp, mode, pre=0, nxt=0, kp=1.0, scale=None, views=None, atten_mask=None):
     scale = scale if scale is not None else 1.0 / np.sqrt(inp.q.shape[2])
     log(f"forward T={inp.q.shape[0]} N={inp.q.shape[1]} D={inp.q.shape[2]} {inp.q.dtype} mode={mode} "
         f"pre={pre} nxt={nxt} kp={kp} lens={np.diff(inp.cu_q).tolist()[:12]}")
     q, k, v = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v))
     y, m, l = O.forward(q, k, v, inp.cu_q, inp.cu_kv, mode=mode, pre=pre, nxt=nxt, keep_prob=kp,
-                        drop_mask=inp.drop_mask, scale=scale, head_num=inp.q.shape[1])
-    gy, gm, gl = gpu_forward(inp, mode, pre, nxt, kp, scale, views=views)
+                        drop_mask=inp.drop_mask, scale=scale, head_num=inp.q.shape[1], atten_mask=atten_mask)
+    gy, gm, gl = gpu_forward(inp, mode, pre, nxt, kp, scale, views=views, atten_mask=atten_mask)
     assert_close("y", gy.double().numpy(), y, inp.q.dtype)
     check_stats(gm, gl, m, l, inp.q.dtype)
     empty = ~np.isfinite(m)  # [N, T]

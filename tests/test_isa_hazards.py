@@ -72,13 +72,22 @@ def test_no_valu_to_asm_mfma_hazard(tmp_path):
     hipcc = os.environ.get("HIPCC") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc"))
     if not hipcc:
         pytest.skip("hipcc not available")
-    out = tmp_path / "bwd16.s"
-    cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
-           "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-mllvm", "-amdgpu-mfma-vgpr-form", "--cuda-device-only", "-S", "-o", str(out),
-           os.path.join(CSRC, "fa_bwd16.hip")]
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    assert r.returncode == 0, r.stdout[-2000:]
-    text = out.read_text()
-    assert "v_mfma_f32_32x32x16_bf16 a[" in text  # the asm MFMAs are there
-    assert _hazards(text) == []
+    # the asm MFMAs live in the dK/dV kernels: compile parts 1 (bf16) and 2 (fp16) side by side
+    import concurrent.futures as cf
+
+    def compile_part(part):
+        out = tmp_path / f"bwd16_p{part}.s"
+        cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+               "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form", f"-DFA_BWD16_PART={part}", "--cuda-device-only", "-S",
+               "-o", str(out), os.path.join(CSRC, "fa_bwd16.hip")]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        assert r.returncode == 0, r.stdout[-2000:]
+        return out.read_text()
+
+    with cf.ThreadPoolExecutor(max_workers=2) as ex:
+        texts = list(ex.map(compile_part, (1, 2)))
+    assert "v_mfma_f32_32x32x16_bf16 a[" in texts[0]  # the asm MFMAs are there
+    assert "v_mfma_f32_32x32x16_f16 a[" in texts[1]
+    for text in texts:
+        assert _hazards(text) == []

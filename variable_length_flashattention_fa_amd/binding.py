@@ -35,6 +35,11 @@ class FaSeqlens(ctypes.Structure):
     _fields_ = [("cu", ctypes.POINTER(ctypes.c_int64)), ("batch", ctypes.c_int64)]
 
 
+class FaMask(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+                ("stride_q", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
 class FaWorkItem(ctypes.Structure):
     _fields_ = [("q_start", ctypes.c_int32), ("kv_start", ctypes.c_int32), ("len_q", ctypes.c_int32),
                 ("len_kv", ctypes.c_int32), ("block", ctypes.c_int32), ("tile_begin", ctypes.c_int32),
@@ -49,8 +54,8 @@ class FaError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ("fa_varlen_bwd", "fa_varlen_fwd", "fa_last_error", "fa_release", "fa_varlen_worklist",
-           "fa_profile_enable", "fa_profile_read", "fa_mfma_peak")
+EXPORTS = ("fa_varlen_bwd", "fa_varlen_bwd_masked", "fa_varlen_fwd", "fa_varlen_fwd_masked", "fa_last_error",
+           "fa_release", "fa_varlen_worklist", "fa_profile_enable", "fa_profile_read", "fa_mfma_peak")
 KERNEL_NAMES = ("preprocess", "bwd_main", "unused", "bwd_dq", "fwd")
 
 
@@ -73,6 +78,15 @@ def load(path: Optional[str] = None):
                                   ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, T, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_varlen_fwd.restype = ctypes.c_int
+    M = ctypes.POINTER(FaMask)
+    lib.fa_varlen_bwd_masked.argtypes = [T, T, T, T, T, ctypes.c_void_p, ctypes.c_void_p, S, S, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, M,
+                                         ctypes.c_double, ctypes.c_int64, T, T, T, ctypes.c_void_p]
+    lib.fa_varlen_bwd_masked.restype = ctypes.c_int
+    lib.fa_varlen_fwd_masked.argtypes = [T, T, T, S, S, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_double, ctypes.c_void_p, M, ctypes.c_double, ctypes.c_int64, T,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_varlen_fwd_masked.restype = ctypes.c_int
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_release.argtypes = []
@@ -112,6 +126,26 @@ def tensor_desc(t: Optional[torch.Tensor]) -> Optional[FaTensor]:
         raise ValueError("the head-dim stride must be 1")
     return FaTensor(ctypes.c_void_p(t.data_ptr() if t.numel() else 0), _DTYPE_CODE[t.dtype], t.shape[0],
                     t.shape[1], t.shape[2], t.stride(0), t.stride(1))
+
+
+def mask_desc(m: Optional[torch.Tensor]) -> Optional[FaMask]:
+    """fa_mask_t view of an explicit mask tensor (uint8 / bool, nonzero = excluded) of shape
+    [B, N, Sq, Skv], [B, 1, Sq, Skv], [1, 1, Sq, Skv] or [Sq, Skv]; size-1 axes get stride 0."""
+    if m is None:
+        return None
+    if m.dtype not in (torch.uint8, torch.bool):
+        raise ValueError("atten_mask must be uint8 or bool")
+    if m.dim() == 2:
+        sb, sn, sq = 0, 0, m.stride(0)
+    elif m.dim() == 4:
+        sb = m.stride(0) if m.shape[0] > 1 else 0
+        sn = m.stride(1) if m.shape[1] > 1 else 0
+        sq = m.stride(2)
+    else:
+        raise ValueError("atten_mask must be 2-D [Sq, Skv] or 4-D [B|1, N|1, Sq, Skv]")
+    if m.numel() and m.stride(-1) != 1:
+        raise ValueError("the key stride of atten_mask must be 1")
+    return FaMask(ctypes.c_void_p(m.data_ptr() if m.numel() else 0), sb, sn, sq, m.shape[-2], m.shape[-1])
 
 
 def _seqlens(cu: Sequence[int]):
@@ -159,9 +193,47 @@ def fa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dy: torch.T
         raise FaError(status, last_error())
 
 
+def fa_varlen_bwd_masked(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+                         atten_mode: int, pre_tokens: int, next_tokens: int, keep_prob: float,
+                         drop_mask: Optional[torch.Tensor], atten_mask: Optional[torch.Tensor], scale: float,
+                         head_num: int, dq, dk, dv, stream=None) -> None:
+    """fa_varlen_bwd with an explicit mask tensor (see mask_desc); same conventions."""
+    lib = load()
+    tq, tk, tv, tdy, ty = (tensor_desc(x) for x in (q, k, v, dy, y))
+    tdq, tdk, tdv = (tensor_desc(x) for x in (dq, dk, dv))
+    tm = mask_desc(atten_mask)
+    sq, aq = _seqlens(cu_seqlens_q)
+    sk, ak = _seqlens(cu_seqlens_kv)
+    for st in (softmax_max, softmax_sum):
+        if st is not None and not st.is_contiguous():
+            raise ValueError("softmax statistics must be contiguous [N, T, 8] fp32")
+    stream = _stream(q, stream)
+
+    def ref(x):
+        return None if x is None else ctypes.byref(x)
+
+    status = lib.fa_varlen_bwd_masked(ref(tq), ref(tk), ref(tv), ref(tdy), ref(ty), _ptr(softmax_max),
+                                      _ptr(softmax_sum), ctypes.byref(sq), ctypes.byref(sk), int(atten_mode),
+                                      int(pre_tokens), int(next_tokens), float(keep_prob), _ptr(drop_mask), ref(tm),
+                                      float(scale), int(head_num), ref(tdq), ref(tdk), ref(tdv),
+                                      ctypes.c_void_p(int(stream)))
+    del aq, ak
+    if status != FA_OK:
+        raise FaError(status, last_error())
+
+
+def _stream(q, stream):
+    if stream is None:
+        return torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
+
+
 def varlen_bwd(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, *,
                atten_mode: int = FA_MASK_NONE, pre_tokens: int = 0, next_tokens: int = 0,
-               keep_prob: float = 1.0, drop_mask=None, scale: Optional[float] = None, head_num=None):
+               keep_prob: float = 1.0, drop_mask=None, scale: Optional[float] = None, head_num=None,
+               atten_mask=None):
     """Convenience wrapper: allocates dq, dk, dv like q, k, v and returns them."""
     if scale is None:
         scale = 1.0 / float(q.shape[2]) ** 0.5
@@ -170,8 +242,12 @@ def varlen_bwd(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlen
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    fa_varlen_bwd(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
-                  pre_tokens, next_tokens, keep_prob, drop_mask, scale, head_num, dq, dk, dv)
+    if atten_mask is None:
+        fa_varlen_bwd(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
+                      pre_tokens, next_tokens, keep_prob, drop_mask, scale, head_num, dq, dk, dv)
+    else:
+        fa_varlen_bwd_masked(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
+                             pre_tokens, next_tokens, keep_prob, drop_mask, atten_mask, scale, head_num, dq, dk, dv)
     return dq, dk, dv
 
 
@@ -208,9 +284,36 @@ def fa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
         raise FaError(status, last_error())
 
 
+def fa_varlen_fwd_masked(q, k, v, cu_seqlens_q, cu_seqlens_kv, atten_mode: int, pre_tokens: int,
+                         next_tokens: int, keep_prob: float, drop_mask: Optional[torch.Tensor],
+                         atten_mask: Optional[torch.Tensor], scale: float, head_num: int, y, softmax_max,
+                         softmax_sum, stream=None) -> None:
+    """fa_varlen_fwd with an explicit mask tensor (see mask_desc); same conventions."""
+    lib = load()
+    tq, tk, tv, ty = (tensor_desc(x) for x in (q, k, v, y))
+    tm = mask_desc(atten_mask)
+    sq, aq = _seqlens(cu_seqlens_q)
+    sk, ak = _seqlens(cu_seqlens_kv)
+    for st in (softmax_max, softmax_sum):
+        if st is not None and not st.is_contiguous():
+            raise ValueError("softmax statistics must be contiguous [N, T, 8] fp32")
+    stream = _stream(q, stream)
+
+    def ref(x):
+        return None if x is None else ctypes.byref(x)
+
+    status = lib.fa_varlen_fwd_masked(ref(tq), ref(tk), ref(tv), ctypes.byref(sq), ctypes.byref(sk),
+                                      int(atten_mode), int(pre_tokens), int(next_tokens), float(keep_prob),
+                                      _ptr(drop_mask), ref(tm), float(scale), int(head_num), ref(ty),
+                                      _ptr(softmax_max), _ptr(softmax_sum), ctypes.c_void_p(int(stream)))
+    del aq, ak
+    if status != FA_OK:
+        raise FaError(status, last_error())
+
+
 def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, atten_mode: int = FA_MASK_NONE, pre_tokens: int = 0,
                next_tokens: int = 0, keep_prob: float = 1.0, drop_mask=None, scale: Optional[float] = None,
-               head_num=None):
+               head_num=None, atten_mask=None):
     """Convenience wrapper: allocates y like q and the [N, T, 8] statistics; returns (y, max, sum)."""
     if scale is None:
         scale = 1.0 / float(q.shape[2]) ** 0.5
@@ -219,8 +322,12 @@ def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, atten_mode: int = FA_MAS
     y = torch.empty(q.shape[0], q.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
     smax = torch.empty(q.shape[1], q.shape[0], 8, dtype=torch.float32, device=q.device)
     ssum = torch.empty_like(smax)
-    fa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, atten_mode, pre_tokens, next_tokens, keep_prob, drop_mask,
-                  scale, head_num, y, smax, ssum)
+    if atten_mask is None:
+        fa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, atten_mode, pre_tokens, next_tokens, keep_prob,
+                      drop_mask, scale, head_num, y, smax, ssum)
+    else:
+        fa_varlen_fwd_masked(q, k, v, cu_seqlens_q, cu_seqlens_kv, atten_mode, pre_tokens, next_tokens, keep_prob,
+                             drop_mask, atten_mask, scale, head_num, y, smax, ssum)
     return y, smax, ssum
 
 

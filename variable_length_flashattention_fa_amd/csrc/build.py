@@ -18,10 +18,15 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libfa_varlen.so"
 
-HIP_SOURCES = ["fa_kernels.hip", "fa_bwd16.hip", "fa_fwd.hip", "fa_probe.hip", "fa_api.cpp"]
-# The 16-bit kernels feed MFMA results straight into VALU work (exp, dS): keep MFMA
-# destinations in VGPRs instead of accumulation registers that would need copying back.
-PER_SOURCE_FLAGS = {"fa_bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# (source, object name, extra flags).  The 16-bit kernels feed MFMA results straight into VALU
+# work (exp, dS): their MFMA destinations stay in VGPRs instead of accumulation registers that
+# would need copying back.  fa_bwd16.hip and fa_fwd.hip compile in parts (one per kernel and
+# dtype), in parallel.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+HIP_UNITS = [("fa_kernels.hip", "fa_kernels", []), ("fa_probe.hip", "fa_probe", []), ("fa_api.cpp", "fa_api", [])]
+HIP_UNITS += [("fa_bwd16.hip", f"fa_bwd16_p{i}", _VGPR_FORM + [f"-DFA_BWD16_PART={i}"]) for i in (1, 2, 3, 4)]
+HIP_UNITS += [("fa_fwd.hip", f"fa_fwd_p{i}", _VGPR_FORM + [f"-DFA_FWD_PART={i}"]) for i in (1, 2)]
+HIP_SOURCES = sorted({u[0] for u in HIP_UNITS})
 CXX_SOURCES = ["fa_worklist.cpp"]
 
 
@@ -52,10 +57,9 @@ def build(arch: str = "gfx950", verbose: bool = False) -> str:
                  "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
     jobs = []
     objs = []
-    for src in HIP_SOURCES:
-        obj = os.path.join(objdir, src + ".o")
+    for src, name, extra in HIP_UNITS:
+        obj = os.path.join(objdir, name + ".o")
         lang = [] if src.endswith(".hip") else ["-x", "hip"]
-        extra = PER_SOURCE_FLAGS.get(src, [])
         jobs.append([hipcc] + common + hip_flags + extra + lang + ["-c", os.path.join(HERE, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:

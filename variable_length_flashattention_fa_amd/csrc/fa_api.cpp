@@ -140,6 +140,32 @@ int grow(void** ptr, size_t* cap, size_t need, const char* what) {
     return FA_OK;
 }
 
+// Checks an explicit mask view against the sequence layout (see fa_mask_t in fa_varlen.h).
+int check_mask(const fa_mask_t* m, const fa_seqlens_t* cq, const fa_seqlens_t* ck) {
+    if (m->stride_b < 0 || m->stride_n < 0 || m->stride_q < 0 || m->rows < 0 || m->cols < 0) {
+        set_error("atten_mask: strides and sizes must be non-negative");
+        return FA_ERR_INVALID;
+    }
+    if (m->stride_q < m->cols) {
+        set_error("atten_mask: stride_q must be at least cols");
+        return FA_ERR_INVALID;
+    }
+    for (int64_t b = 0; b < cq->batch; ++b) {
+        const int64_t lq = cq->cu[b + 1] - cq->cu[b];
+        const int64_t lk = ck->cu[b + 1] - ck->cu[b];
+        if (lq > m->rows || lk > m->cols) {
+            set_error("atten_mask: rows / cols must cover every sequence (Sq >= Lq_b, Skv >= Lkv_b)");
+            return FA_ERR_INVALID;
+        }
+        // the kernels address one (sequence, head) block with 32-bit offsets
+        if (lq > 0 && lk > 0 && (lq - 1) * m->stride_q + lk >= (int64_t(1) << 31)) {
+            set_error("atten_mask: one (sequence, head) block must span less than 2^31 bytes");
+            return FA_ERR_UNSUPPORTED;
+        }
+    }
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" const char* fa_last_error(void) { return fa::last_error_cstr(); }
@@ -196,6 +222,19 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
                              int64_t next_tokens, double keep_prob, const uint8_t* drop_mask, double scale,
                              int64_t head_num, const fa_tensor_t* dq, const fa_tensor_t* dk,
                              const fa_tensor_t* dv, void* stream) {
+    return fa_varlen_bwd_masked(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
+                                pre_tokens, next_tokens, keep_prob, drop_mask, nullptr, scale, head_num, dq, dk,
+                                dv, stream);
+}
+
+extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                                    const fa_tensor_t* dy, const fa_tensor_t* y, const float* softmax_max,
+                                    const float* softmax_sum, const fa_seqlens_t* cu_seqlens_q,
+                                    const fa_seqlens_t* cu_seqlens_kv, int32_t atten_mode, int64_t pre_tokens,
+                                    int64_t next_tokens, double keep_prob, const uint8_t* drop_mask,
+                                    const fa_mask_t* atten_mask, double scale, int64_t head_num,
+                                    const fa_tensor_t* dq, const fa_tensor_t* dk, const fa_tensor_t* dv,
+                                    void* stream) {
     fa::clear_error();
     // ---- null pointers (page: ACLNN_ERR_PARAM_NULLPTR) ----
     const fa_tensor_t* all[8] = {q, k, v, dy, y, dq, dk, dv};
@@ -222,6 +261,10 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     }
     if (keep_prob < 1.0 && drop_mask == nullptr) {
         set_error("drop_mask is null while keep_prob < 1");
+        return FA_ERR_NULLPTR;
+    }
+    if (atten_mask != nullptr && atten_mask->data == nullptr && q->tokens != 0) {
+        set_error("atten_mask->data is null");
         return FA_ERR_NULLPTR;
     }
     // ---- values (page: ACLNN_ERR_PARAM_INVALID) ----
@@ -282,6 +325,10 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     if (cu_seqlens_q->cu[batch] != q->tokens || cu_seqlens_kv->cu[batch] != k->tokens) {
         set_error("cu_seqlens must end at the token counts of q and k");
         return FA_ERR_INVALID;
+    }
+    if (atten_mask != nullptr) {
+        st = check_mask(atten_mask, cu_seqlens_q, cu_seqlens_kv);
+        if (st != FA_OK) return st;
     }
     // ---- allowed by the page, not built ----
     if (!fa::head_dims_supported(q->head_dim, v->head_dim)) {
@@ -431,9 +478,11 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
         a.exp_scale = exp_scale;
         a.inv_keep = inv_keep;
         a.scale = static_cast<float>(scale);
-        e = timed(1, s, [&] { return fa::launch_dkdv16(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_items, s); });
+        fa::set_mask(a, atten_mask);
+        const bool xm = atten_mask != nullptr;
+        e = timed(1, s, [&] { return fa::launch_dkdv16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, ws.n_items, s); });
         if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
-        e = timed(3, s, [&] { return fa::launch_dq16(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_q_items, s); });
+        e = timed(3, s, [&] { return fa::launch_dq16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, ws.n_q_items, s); });
         if (e != hipSuccess) return runtime_error("dQ kernel launch", e);
         return FA_OK;
     }
@@ -465,6 +514,7 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     a.exp_scale = exp_scale;
     a.inv_keep = inv_keep;
     a.scale = static_cast<float>(scale);
+    fa::set_mask(a, atten_mask);
     e = timed(1, s, [&] { return fa::launch_main(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_items, s); });
     if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
     e = timed(3, s, [&] { return fa::launch_dq32(d, dv_dim, keep_prob < 1.0, a, ws.n_q_items, s); });
@@ -479,6 +529,16 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
                              int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens, double keep_prob,
                              const uint8_t* drop_mask, double scale, int64_t head_num, const fa_tensor_t* y,
                              float* softmax_max, float* softmax_sum, void* stream) {
+    return fa_varlen_fwd_masked(q, k, v, cu_seqlens_q, cu_seqlens_kv, atten_mode, pre_tokens, next_tokens,
+                                keep_prob, drop_mask, nullptr, scale, head_num, y, softmax_max, softmax_sum, stream);
+}
+
+extern "C" int fa_varlen_fwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                                    const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
+                                    int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens, double keep_prob,
+                                    const uint8_t* drop_mask, const fa_mask_t* atten_mask, double scale,
+                                    int64_t head_num, const fa_tensor_t* y, float* softmax_max,
+                                    float* softmax_sum, void* stream) {
     fa::clear_error();
     const fa_tensor_t* all[4] = {q, k, v, y};
     const char* names[4] = {"q", "k", "v", "y"};
@@ -503,6 +563,10 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     }
     if (keep_prob < 1.0 && drop_mask == nullptr) {
         set_error("drop_mask is null while keep_prob < 1");
+        return FA_ERR_NULLPTR;
+    }
+    if (atten_mask != nullptr && atten_mask->data == nullptr && q->tokens != 0) {
+        set_error("atten_mask->data is null");
         return FA_ERR_NULLPTR;
     }
     for (int i = 0; i < 4; ++i) {
@@ -555,6 +619,10 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     if (cu_seqlens_q->cu[batch] != q->tokens || cu_seqlens_kv->cu[batch] != k->tokens) {
         set_error("cu_seqlens must end at the token counts of q and k");
         return FA_ERR_INVALID;
+    }
+    if (atten_mask != nullptr) {
+        st = check_mask(atten_mask, cu_seqlens_q, cu_seqlens_kv);
+        if (st != FA_OK) return st;
     }
     if (!fa::head_dims_supported(q->head_dim, v->head_dim)) {
         set_error("head dims (q/k, v) must be (128, 128), (128, 64) or (64, 64)");
@@ -669,9 +737,11 @@ extern "C" int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
     a.scale = static_cast<float>(scale);
     a.exp_scale = static_cast<float>(scale * 1.4426950408889634);
     a.inv_keep = static_cast<float>(1.0 / keep_prob);
+    fa::set_mask(a, atten_mask);
     e = timed(4, s, [&] {
         return wide ? fa::launch_fwd32(d, dv_dim, keep_prob < 1.0, a, ws.n_fwd_items, s)
-                    : fa::launch_fwd16(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_fwd_items, s);
+                    : fa::launch_fwd16(dtype, d, dv_dim, keep_prob < 1.0, atten_mask != nullptr, a,
+                                       ws.n_fwd_items, s);
     });
     if (e != hipSuccess) return runtime_error("forward kernel launch", e);
     return FA_OK;

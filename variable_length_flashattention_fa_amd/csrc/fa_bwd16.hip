@@ -70,7 +70,7 @@ struct Interleave {
 constexpr int p_slot(int a, int nops) { return a * nops / 16; }
 constexpr int d_slot(int a, int nops) { return (a * nops + nops / 2) / 16; }
 
-template <typename T, int DK, int DV, bool DROP>
+template <typename T, int DK, int DV, bool DROP, bool XM>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     using vec = typename Op16<T>::vec;
     constexpr int NW = 4;
@@ -128,11 +128,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         if constexpr (DK != DV) loD_.init(lane);
         const LdsOffsets<DV>& loD = offsets_for(loQ, loD_);
 
-        // the query head being walked (set per head below) and its tensors
+        // the query head being walked (set per head below), its tensors and (XM) its block of the
+        // explicit mask
         int n = hk * p.group;
         const T* gq = nullptr;
         const T* gdy = nullptr;
         const float2* gstat = nullptr;
+        __amdgpu_buffer_rsrc_t mrs;
         int qoff[TWQ];
         int dyoff[TWD];
         // wave w copies 1 KiB chunks w*TWQ .. w*TWQ + TWQ - 1 of each Q tile (one run), and
@@ -251,13 +253,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         vec dsY[2];
         uint32_t dbC[16];      // dropout mask bytes and bit base of the softmax rows
         int dcC = 0;
+        uint32_t mkC[16];      // explicit mask bytes of the softmax rows (XM)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             pkY[i] = vec{};
             dsY[i] = vec{};
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dbC[i] = 0;
+        for (int i = 0; i < 16; ++i) {
+            dbC[i] = 0;
+            mkC[i] = 0;
+        }
 
         // One step (see the kinds above) of the tile in buffer b, tile index t; nkind / nb:
         // the step that follows (its first operands and statistics are read at the end).
@@ -282,6 +288,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             float dsv[16];
             uint32_t dbN[16];
             int dcN = 0;
+            uint32_t mkN[16];
+            // explicit mask bytes of the X rows: element a sits at mbN + cc(a) * am_sq of the block
+            uint32_t mbN = 0;
+            if constexpr (XM && HX) {
+                const int xt = t + (KIND == kStepB ? 1 : 0);
+                mbN = static_cast<uint32_t>(xt * BQ + 32 * wh.xm + 4 * h) * static_cast<uint32_t>(p.mask.am_sq) +
+                      static_cast<uint32_t>(jw);
+            }
             // dropout bits of the X rows: the bit of (row 4h + cc(a), key jw) sits at bit
             // dcN + cc(a) * K of the buffer that starts at the step's first mask byte
             __amdgpu_buffer_rsrc_t drs;
@@ -333,7 +347,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                         const float bt = stC[a / 4][(a % 4) / 2][2 * (a % 2) + 1];
                         const float e = __builtin_amdgcn_exp2f(x * p.exp_scale - bt);
                         if constexpr (MASKED) {
-                            const bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(rng);
+                            bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(rng);
+                            if constexpr (XM) adm = adm && mkC[a] == 0;
                             pv[a] = adm ? e : 0.f;
                         } else {
                             pv[a] = e;
@@ -388,6 +403,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     const int u = dcN + cc * K;
                     dbN[k] = __builtin_amdgcn_raw_buffer_load_b8(drs, u >> 3, 0, 0);
                 }
+                // ---- explicit mask byte of X element k (rows past the sequence read zero or are
+                // excluded by the row range anyway)
+                if constexpr (XM && HX && k < 16) {
+                    constexpr int cc = 8 * (k / 4) + (k % 4);
+                    mkN[k] = __builtin_amdgcn_raw_buffer_load_b8(
+                        mrs, mbN + static_cast<uint32_t>(cc) * static_cast<uint32_t>(p.mask.am_sq), 0, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
             // hand the pipeline over to the next step
@@ -398,6 +420,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) dbC[i] = dbN[i];
                     dcC = dcN;
+                }
+                if constexpr (XM) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) mkC[i] = mkN[i];
                 }
             }
             if constexpr (HS) {
@@ -441,12 +467,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             }
             f0 = min(max(lo, tb), te);
             f1 = min(max(hi, f0), te);
+            if (XM) {
+                f0 = te;  // an explicit mask can exclude pairs anywhere: every tile is masked
+                f1 = te;
+            }
         }
         for (int r = 0; r < p.group; ++r) {
             n = hk * p.group + r;
             gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
             gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
             gstat = p.rowstat + static_cast<int64_t>(n) * p.tq + it.q_start;
+            if constexpr (XM) {
+                const uint8_t* mb = p.mask.amask + it.seq * p.mask.am_sb + n * p.mask.am_sn;
+                mrs = raw_rsrc(mb, static_cast<uint32_t>((L - 1) * p.mask.am_sq + K));
+            }
             if (r > 0) {
                 // every wave is done with the previous head's tiles before they are overwritten
                 __syncthreads();
@@ -526,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 //   dS^T = Ps (dP Z/kp - D)      (each lane holds one query: its D and beta are scalars)
 //   dQ^T += K^T dS^T             (A = transposing reads of K, B = dS^T straight from registers)
 
-template <typename T, int DK, int DV, bool DROP>
+template <typename T, int DK, int DV, bool DROP, bool XM>
 __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     using vec = typename Op16<T>::vec;
     constexpr int NW = 8;
@@ -642,8 +676,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 #pragma unroll
     for (int i = 0; i < ND; ++i) accQ[i] = zero16();
 
+    // explicit mask block of this (sequence, head); this lane reads row qi
+    __amdgpu_buffer_rsrc_t mrs;
+    if constexpr (XM) {
+        const uint8_t* mb = p.mask.amask + it.seq * p.mask.am_sb + n * p.mask.am_sn;
+        mrs = raw_rsrc(mb, static_cast<uint32_t>((L - 1) * p.mask.am_sq + K));
+    }
+
     // one 32-key step (keys k0s .. k0s + 31, rows 32 kh of the tile in cK / cV)
     auto kstep = [&](const T* cK, const T* cV, int k0s) {
+        // explicit mask bytes of keys k0s + 4h + cc(a), issued before the products that hide them
+        uint32_t mk[16];
+        if constexpr (XM) {
+            const uint32_t mrow = static_cast<uint32_t>(qi) * static_cast<uint32_t>(p.mask.am_sq) +
+                                  static_cast<uint32_t>(k0s + 4 * h);
+#pragma unroll
+            for (int a = 0; a < 16; ++a)
+                mk[a] = __builtin_amdgcn_raw_buffer_load_b8(mrs, mrow + 8 * (a >> 2) + (a & 3), 0, 0);
+        }
         f32x16 accS = zero16();
         f32x16 accP = zero16();
 #pragma unroll
@@ -656,7 +706,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 #pragma unroll
         for (int s = SV; s < SK; ++s) accS = Op16<T>::mfma(lds_row<vec>(cK, loK.row[s]), qreg[s], accS);
         // dS^T = Ps (dP Z/kp - D); element (key k0s + 4h + cc(a), query qi)
-        const bool full = wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
+        const bool full = !XM && wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
         uint32_t dsw[2][4];
         auto softmax_grad = [&](auto masked_tag) {
             constexpr bool MASKED = decltype(masked_tag)::value;
@@ -669,7 +719,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
                     const int cc = 8 * ((a + e) >> 2) + ((a + e) & 3);
                     float pv = __builtin_amdgcn_exp2f(accS[a + e] * p.exp_scale - beta);
                     if constexpr (MASKED) {
-                        const bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(krng);
+                        bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(krng);
+                        if constexpr (XM) adm = adm && mk[a + e] == 0;
                         pv = adm ? pv : 0.f;
                     }
                     if constexpr (DROP) {
@@ -732,45 +783,74 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 
 // ------------------------------------------------------------------------------------------------
 
-template <typename T, int DK, int DV, bool DROP>
+template <typename T, int DK, int DV, bool DROP, bool XM>
 static hipError_t launch_dkdv_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
-    bwd_dkdv16_kernel<T, DK, DV, DROP>
+    bwd_dkdv16_kernel<T, DK, DV, DROP, XM>
         <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads / a.group)), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-template <typename T, int DK, int DV, bool DROP>
+template <typename T, int DK, int DV, bool DROP, bool XM>
 static hipError_t launch_dq_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
-    bwd_dq16_kernel<T, DK, DV, DROP>
+    bwd_dq16_kernel<T, DK, DV, DROP, XM>
         <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-// dtype x head dims (Q/K, V) in {(128, 128), (128, 64), (64, 64)} x dropout
-#define FA_DISPATCH16(FN)                                                                             \
-    if (n_items <= 0) return hipSuccess;                                                              \
-    auto pick = [&](auto tag) -> hipError_t {                                                         \
-        using T = typename decltype(tag)::type;                                                       \
-        if (head_dim_k == 128 && head_dim_v == 128)                                                   \
-            return dropout ? FN<T, 128, 128, true>(a, n_items, stream) : FN<T, 128, 128, false>(a, n_items, stream); \
-        if (head_dim_k == 128 && head_dim_v == 64)                                                    \
-            return dropout ? FN<T, 128, 64, true>(a, n_items, stream) : FN<T, 128, 64, false>(a, n_items, stream);   \
-        if (head_dim_k == 64 && head_dim_v == 64)                                                     \
-            return dropout ? FN<T, 64, 64, true>(a, n_items, stream) : FN<T, 64, 64, false>(a, n_items, stream);     \
-        return hipErrorInvalidValue;                                                                  \
+// head dims (Q/K, V) in {(128, 128), (128, 64), (64, 64)} x dropout x explicit mask, for one dtype
+#define FA_DISPATCH16(FN, T)                                                                          \
+    auto flags = [&](auto dk_c, auto dv_c) -> hipError_t {                                            \
+        constexpr int DK = decltype(dk_c)::value;                                                     \
+        constexpr int DV = decltype(dv_c)::value;                                                     \
+        if (dropout) return xmask ? FN<T, DK, DV, true, true>(a, n, s) : FN<T, DK, DV, true, false>(a, n, s); \
+        return xmask ? FN<T, DK, DV, false, true>(a, n, s) : FN<T, DK, DV, false, false>(a, n, s);    \
     };                                                                                                \
-    if (dtype == FA_BF16) return pick(TypeTag<__bf16>{});                                  \
-    return pick(TypeTag<_Float16>{})
+    if (dk == 128 && dv == 128) return flags(IC<128>{}, IC<128>{});                                    \
+    if (dk == 128 && dv == 64) return flags(IC<128>{}, IC<64>{});                                      \
+    if (dk == 64 && dv == 64) return flags(IC<64>{}, IC<64>{});                                        \
+    return hipErrorInvalidValue
 
-hipError_t launch_dkdv16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const Bwd16Args& a,
-                         int64_t n_items, hipStream_t stream) {
-    FA_DISPATCH16(launch_dkdv_t);
+// The kernels of each (kernel, dtype) pair are instantiated in a compile part of their own
+// (FA_BWD16_PART 1..4; without it, all of them), so that the build compiles them in parallel.
+hipError_t dkdv16_bf16(int dk, int dv, bool dropout, bool xmask, const Bwd16Args& a, int64_t n, hipStream_t s);
+hipError_t dkdv16_f16(int dk, int dv, bool dropout, bool xmask, const Bwd16Args& a, int64_t n, hipStream_t s);
+hipError_t dq16_bf16(int dk, int dv, bool dropout, bool xmask, const Bwd16Args& a, int64_t n, hipStream_t s);
+hipError_t dq16_f16(int dk, int dv, bool dropout, bool xmask, const Bwd16Args& a, int64_t n, hipStream_t s);
+
+#if !defined(FA_BWD16_PART) || FA_BWD16_PART == 1
+hipError_t dkdv16_bf16(int dk, int dv, bool dropout, bool xmask, const Bwd16Args& a, int64_t n, hipStream_t s) {
+    FA_DISPATCH16(launch_dkdv_t, __bf16);
 }
 
-hipError_t launch_dq16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const Bwd16Args& a,
-                       int64_t n_items, hipStream_t stream) {
-    FA_DISPATCH16(launch_dq_t);
+hipError_t launch_dkdv16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, bool xmask,
+                         const Bwd16Args& a, int64_t n_items, hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    return dtype == FA_BF16 ? dkdv16_bf16(head_dim_k, head_dim_v, dropout, xmask, a, n_items, stream)
+                            : dkdv16_f16(head_dim_k, head_dim_v, dropout, xmask, a, n_items, stream);
 }
+
+hipError_t launch_dq16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, bool xmask,
+                       const Bwd16Args& a, int64_t n_items, hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    return dtype == FA_BF16 ? dq16_bf16(head_dim_k, head_dim_v, dropout, xmask, a, n_items, stream)
+                            : dq16_f16(head_dim_k, head_dim_v, dropout, xmask, a, n_items, stream);
+}
+#endif
+#if !defined(FA_BWD16_PART) || FA_BWD16_PART == 2
+hipError_t dkdv16_f16(int dk, int dv, bool dropout, bool xmask, const Bwd16Args& a, int64_t n, hipStream_t s) {
+    FA_DISPATCH16(launch_dkdv_t, _Float16);
+}
+#endif
+#if !defined(FA_BWD16_PART) || FA_BWD16_PART == 3
+hipError_t dq16_bf16(int dk, int dv, bool dropout, bool xmask, const Bwd16Args& a, int64_t n, hipStream_t s) {
+    FA_DISPATCH16(launch_dq_t, __bf16);
+}
+#endif
+#if !defined(FA_BWD16_PART) || FA_BWD16_PART == 4
+hipError_t dq16_f16(int dk, int dv, bool dropout, bool xmask, const Bwd16Args& a, int64_t n, hipStream_t s) {
+    FA_DISPATCH16(launch_dq_t, _Float16);
+}
+#endif
 
 #undef FA_DISPATCH16
 

@@ -25,7 +25,7 @@ namespace fa {
 // O^T is rescaled only when a query's max grows past its reference mref by more than 8 (in
 // log2 units: P stays below 256), decided per wave, so most steps skip the rescale.
 
-template <typename T, int DK, int DV, bool DROP>
+template <typename T, int DK, int DV, bool DROP, bool XM>
 __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     using vec = typename Op16<T>::vec;
     constexpr int NW = 8;
@@ -133,6 +133,13 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         rbit = (rb & 7) + static_cast<int64_t>(qi < L ? qi : 0) * K;
     }
 
+    // explicit mask block of this (sequence, head); this lane reads row qi
+    __amdgpu_buffer_rsrc_t mrs;
+    if constexpr (XM) {
+        const uint8_t* mb = p.mask.amask + it.seq * p.mask.am_sb + n * p.mask.am_sn;
+        mrs = raw_rsrc(mb, static_cast<uint32_t>((L - 1) * p.mask.am_sq + K));
+    }
+
     f32x16 accO[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i) accO[i] = zero16();
@@ -141,13 +148,22 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     float lsum = 0.f;         // sum of P over this lane's keys (relative to mref)
 
     auto kstep = [&](const T* cK, const T* cV, int k0s) {
+        // explicit mask bytes of keys k0s + 4h + cc(a), issued before the product that hides them
+        uint32_t mk[16];
+        if constexpr (XM) {
+            const uint32_t mrow = static_cast<uint32_t>(qi) * static_cast<uint32_t>(p.mask.am_sq) +
+                                  static_cast<uint32_t>(k0s + 4 * h);
+#pragma unroll
+            for (int a = 0; a < 16; ++a)
+                mk[a] = __builtin_amdgcn_raw_buffer_load_b8(mrs, mrow + 8 * (a >> 2) + (a & 3), 0, 0);
+        }
         f32x16 accS = zero16();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const vec ak = lds_row<vec>(cK, loK.row[s]);
             accS = Op16<T>::mfma(ak, qreg[s], accS);
         }
-        const bool full = wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
+        const bool full = !XM && wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
         float x[16];
         auto scores = [&](auto masked_tag) {
             constexpr bool MASKED = decltype(masked_tag)::value;
@@ -157,7 +173,8 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
                 x[a] = accS[a] * p.exp_scale;
                 if constexpr (MASKED) {
                     const int cc = 8 * (a >> 2) + (a & 3);
-                    const bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(krng);
+                    bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(krng);
+                    if constexpr (XM) adm = adm && mk[a] == 0;
                     x[a] = adm ? x[a] : -INFINITY;
                 }
             }
@@ -298,9 +315,15 @@ __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) 
 #pragma unroll
     for (int d = 0; d < DV; ++d) o[d] = 0.f;
     const int64_t bit0 = it.drop_base + (static_cast<int64_t>(n) * L + qi) * K;
+    // this query's row of the explicit mask, if any
+    const uint8_t* mrow = p.mask.amask == nullptr
+                              ? nullptr
+                              : p.mask.amask + it.seq * p.mask.am_sb + n * p.mask.am_sn +
+                                    static_cast<int64_t>(qi) * p.mask.am_sq;
     float m = -INFINITY;
     float l = 0.f;
     for (int j = klo; j <= khi; ++j) {
+        if (mrow != nullptr && mrow[j] != 0) continue;
         const float* kr = kb + static_cast<int64_t>(j) * p.k_st;
         float s = 0.f;
 #pragma unroll
@@ -339,30 +362,52 @@ __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) 
 
 // ------------------------------------------------------------------------------------------------
 
-template <typename T, int DK, int DV, bool DROP>
+template <typename T, int DK, int DV, bool DROP, bool XM>
 static hipError_t launch_fwd16_t(const FwdArgs& a, int64_t n, hipStream_t stream) {
-    fwd16_kernel<T, DK, DV, DROP><<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
+    fwd16_kernel<T, DK, DV, DROP, XM>
+        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-template <typename T, int DK, int DV>
-static hipError_t fwd16_drop(bool dropout, const FwdArgs& a, int64_t n, hipStream_t stream) {
-    return dropout ? launch_fwd16_t<T, DK, DV, true>(a, n, stream) : launch_fwd16_t<T, DK, DV, false>(a, n, stream);
-}
-
+// dtype parts: each instantiated in a compile part of its own (FA_FWD_PART 1 = bf16, 2 = fp16 and
+// the fp32 kernels; without it, all), so that the build compiles them in parallel
 template <typename T>
-static hipError_t fwd16_dims(int dk, int dv, bool dropout, const FwdArgs& a, int64_t n, hipStream_t stream) {
-    if (dk == 128 && dv == 128) return fwd16_drop<T, 128, 128>(dropout, a, n, stream);
-    if (dk == 128 && dv == 64) return fwd16_drop<T, 128, 64>(dropout, a, n, stream);
-    if (dk == 64 && dv == 64) return fwd16_drop<T, 64, 64>(dropout, a, n, stream);
+static hipError_t fwd16_dims(int dk, int dv, bool dropout, bool xmask, const FwdArgs& a, int64_t n,
+                             hipStream_t stream) {
+    auto flags = [&](auto dk_c, auto dv_c) -> hipError_t {
+        constexpr int DK = decltype(dk_c)::value;
+        constexpr int DV = decltype(dv_c)::value;
+        if (dropout)
+            return xmask ? launch_fwd16_t<T, DK, DV, true, true>(a, n, stream)
+                         : launch_fwd16_t<T, DK, DV, true, false>(a, n, stream);
+        return xmask ? launch_fwd16_t<T, DK, DV, false, true>(a, n, stream)
+                     : launch_fwd16_t<T, DK, DV, false, false>(a, n, stream);
+    };
+    if (dk == 128 && dv == 128) return flags(IC<128>{}, IC<128>{});
+    if (dk == 128 && dv == 64) return flags(IC<128>{}, IC<64>{});
+    if (dk == 64 && dv == 64) return flags(IC<64>{}, IC<64>{});
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const FwdArgs& a,
+hipError_t fwd16_bf16(int dk, int dv, bool dropout, bool xmask, const FwdArgs& a, int64_t n, hipStream_t s);
+hipError_t fwd16_f16(int dk, int dv, bool dropout, bool xmask, const FwdArgs& a, int64_t n, hipStream_t s);
+
+#if !defined(FA_FWD_PART) || FA_FWD_PART == 1
+hipError_t fwd16_bf16(int dk, int dv, bool dropout, bool xmask, const FwdArgs& a, int64_t n, hipStream_t s) {
+    return fwd16_dims<__bf16>(dk, dv, dropout, xmask, a, n, s);
+}
+
+hipError_t launch_fwd16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, bool xmask, const FwdArgs& a,
                         int64_t n_items, hipStream_t stream) {
     if (n_items <= 0) return hipSuccess;
-    if (dtype == FA_BF16) return fwd16_dims<__bf16>(head_dim_k, head_dim_v, dropout, a, n_items, stream);
-    return fwd16_dims<_Float16>(head_dim_k, head_dim_v, dropout, a, n_items, stream);
+    return dtype == FA_BF16 ? fwd16_bf16(head_dim_k, head_dim_v, dropout, xmask, a, n_items, stream)
+                            : fwd16_f16(head_dim_k, head_dim_v, dropout, xmask, a, n_items, stream);
+}
+#endif
+
+#if !defined(FA_FWD_PART) || FA_FWD_PART == 2
+hipError_t fwd16_f16(int dk, int dv, bool dropout, bool xmask, const FwdArgs& a, int64_t n, hipStream_t s) {
+    return fwd16_dims<_Float16>(dk, dv, dropout, xmask, a, n, s);
 }
 
 template <int DK, int DV>
@@ -381,5 +426,7 @@ hipError_t launch_fwd32(int head_dim_k, int head_dim_v, bool dropout, const FwdA
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
+
+#endif
 
 }  // namespace fa

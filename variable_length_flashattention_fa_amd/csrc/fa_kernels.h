@@ -9,6 +9,27 @@
 
 namespace fa {
 
+// Explicit attention mask as the kernels see it: element (b, n, i, j) at
+// amask[b * am_sb + n * am_sn + i * am_sq + j]; amask == nullptr: no explicit mask.
+struct MaskArg {
+    const uint8_t* amask = nullptr;
+    int64_t am_sb = 0;
+    int64_t am_sn = 0;
+    int32_t am_sq = 0;
+};
+
+template <typename A>
+inline void set_mask(A& a, const fa_mask_t* m) {
+    if (m == nullptr) {
+        a.mask = MaskArg{};
+        return;
+    }
+    a.mask.amask = m->data;
+    a.mask.am_sb = m->stride_b;
+    a.mask.am_sn = m->stride_n;
+    a.mask.am_sq = static_cast<int32_t>(m->stride_q);
+}
+
 struct TensorArg {
     const void* data;
     int64_t stride_t;
@@ -33,6 +54,7 @@ struct MainArgs {
     const fa_work_item_t* items;    // key-block items (kBlockKv32 keys, kTileQ32 query tiles)
     const fa_work_item_t* items_q;  // query-block items (FA32_FWD_BLOCK queries)
     const uint8_t* drop_mask;
+    MaskArg mask;
     int32_t tq;
     int32_t heads;   // query heads
     int32_t group;   // query heads per key/value head
@@ -76,18 +98,19 @@ struct Bwd16Args {
     const fa_work_item_t* items_q;   // query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles)
     const uint8_t* drop_mask;
     int64_t drop_bytes;  // size of the dropout mask in bytes (bounds its reads)
+    MaskArg mask;
     int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float exp_scale, inv_keep, scale;
 };
 
 // dK/dV kernel over n_items key-block items x key/value heads (each sums its group of query heads).
 // Head dims (Q/K, V): (128, 128), (128, 64) or (64, 64).
-hipError_t launch_dkdv16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const Bwd16Args& a,
-                         int64_t n_items, hipStream_t stream);
+hipError_t launch_dkdv16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, bool xmask,
+                         const Bwd16Args& a, int64_t n_items, hipStream_t stream);
 
 // dQ kernel over n_items query-block items x query heads; the same head dims.
-hipError_t launch_dq16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const Bwd16Args& a,
-                       int64_t n_items, hipStream_t stream);
+hipError_t launch_dq16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, bool xmask,
+                       const Bwd16Args& a, int64_t n_items, hipStream_t stream);
 
 // ---- forward ----------------------------------------------------------------------------------
 // Y = Dropout(Softmax(Mask(scale Q K^T))) V and the row statistics, over query-block items.
@@ -103,14 +126,15 @@ struct FwdArgs {
     const fa_work_item_t* items;  // query-block items
     const uint8_t* drop_mask;
     int64_t drop_bytes;  // size of the dropout mask in bytes (bounds its reads)
+    MaskArg mask;
     int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float scale, exp_scale, inv_keep;
 };
 
 // bf16 / fp16 forward over n_items query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles).
 // Head dims (Q/K, V): (128, 128), (128, 64) or (64, 64).
-hipError_t launch_fwd16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, const FwdArgs& a,
-                        int64_t n_items, hipStream_t stream);
+hipError_t launch_fwd16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, bool xmask,
+                        const FwdArgs& a, int64_t n_items, hipStream_t stream);
 // fp32 forward over n_items query-block items (FA32_FWD_BLOCK queries); the same head dims.
 hipError_t launch_fwd32(int head_dim_k, int head_dim_v, bool dropout, const FwdArgs& a, int64_t n_items,
                         hipStream_t stream);

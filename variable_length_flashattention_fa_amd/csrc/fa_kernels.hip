@@ -145,6 +145,7 @@ struct DevArgs {
     const fa_work_item_t* items;    // key-block items (dK / dV)
     const fa_work_item_t* items_q;  // query-block items (dQ)
     const uint8_t* drop_mask;
+    MaskArg mask;
     int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float exp_scale, inv_keep, scale;
 };
@@ -218,6 +219,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
         const T* __restrict__ gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
         const T* __restrict__ gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
         const int64_t drop_row0 = DROP ? it.drop_base + static_cast<int64_t>(n) * L * K : 0;
+        // this (sequence, head) block of the explicit mask, if any
+        const uint8_t* mblk =
+            p.mask.amask == nullptr ? nullptr : p.mask.amask + it.seq * p.mask.am_sb + n * p.mask.am_sn;
 
         for (int t = it.tile_begin; t < it.tile_end; ++t) {
             const int q0 = t * BQ;
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
             }
 
             // Is every pair of the (tile, block) admitted and in range?
-            bool full = (q0 + BQ <= L) && (j0 + BKV <= K);
+            bool full = mblk == nullptr && (q0 + BQ <= L) && (j0 + BKV <= K);
             if (p.mode == FA_MASK_CAUSAL) {
                 full = full && (j0 + BKV - 1 <= q0 + off);
             } else if (p.mode == FA_MASK_BAND) {
@@ -302,6 +306,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
                         } else if (p.mode == FA_MASK_BAND) {
                             adm = adm && (jw >= i + off - p.pre) && (jw <= i + off + p.nxt);
                         }
+                        if (adm && mblk != nullptr) adm = mblk[static_cast<int64_t>(i) * p.mask.am_sq + jw] == 0;
                         pv = adm ? pv : 0.f;
                         if constexpr (DROP) {
                             if (adm) {
@@ -411,7 +416,13 @@ __global__ __launch_bounds__(2 * FA32_FWD_BLOCK) void bwd_dq32_kernel(const DevA
     for (int d = 0; d < HV; ++d) dyr[d] = dy[d];
     const float2 st = p.rowstat[static_cast<int64_t>(n) * p.tq + row];  // {D_i, beta_i}
     const int64_t bit0 = it.drop_base + (static_cast<int64_t>(n) * L + qi) * K;
+    // this query's row of the explicit mask, if any (both lanes of the query skip the same keys)
+    const uint8_t* mrow = p.mask.amask == nullptr
+                              ? nullptr
+                              : p.mask.amask + it.seq * p.mask.am_sb + n * p.mask.am_sn +
+                                    static_cast<int64_t>(qi) * p.mask.am_sq;
     for (int j = klo; j <= khi; ++j) {
+        if (mrow != nullptr && mrow[j] != 0) continue;
         const float* kr = kb + static_cast<int64_t>(j) * p.k_st;
         const float* vr = vb + static_cast<int64_t>(j) * p.v_st;
         float sc = 0.f;
@@ -505,6 +516,7 @@ static DevArgs dev_args(const MainArgs& a) {
     d.items = a.items;
     d.items_q = a.items_q;
     d.drop_mask = a.drop_mask;
+    d.mask = a.mask;
     d.tq = a.tq;
     d.heads = a.heads;
     d.group = a.group;

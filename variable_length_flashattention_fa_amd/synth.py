@@ -158,6 +158,16 @@ def keep_bits(rng, lq: List[int], lkv: List[int], heads: int, keep_prob: float) 
     return out if out.size else np.zeros(1, dtype=np.uint8)
 
 
+def explicit_mask(seed: int, shape, frac: float, empty_rows=()) -> np.ndarray:
+    """A seeded uint8 attention mask (1 = excluded) of the given shape: each element is 1 with
+    probability frac; the rows listed in empty_rows (last-but-one axis) are excluded entirely."""
+    rng = np.random.default_rng(seed)
+    m = (rng.random(shape) < frac).astype(np.uint8)
+    for r in empty_rows:
+        m[..., r, :] = 1
+    return m
+
+
 def make(wl: Workload, seed: Optional[int] = None) -> Inputs:
     """Draw the inputs of a workload on the CPU, following the recipe in the module docstring."""
     rng = np.random.default_rng(wl.seed if seed is None else seed)
