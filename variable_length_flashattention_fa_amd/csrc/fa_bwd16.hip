@@ -554,7 +554,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 // dQ
 // ------------------------------------------------------------------------------------------------
 // Workgroup: 8 waves (two per SIMD), FA16_DQ_BLOCK = 256 queries; wave w owns queries 32w ..
-// 32w+31 and keeps their Q and dY rows (in accumulation registers), statistics and dQ^T
+// 32w+31 and keeps their Q and dY rows, statistics and dQ^T
 // accumulator.  Key tiles of FA16_DQ_TILE_K = 64 rows are walked as two 32-key steps:
 //   S^T = K Q^T, dP^T = V dY^T   (A = K / V rows from LDS, B = Q / dY)
 //   dS^T = Ps (dP Z/kp - D)      (each lane holds one query: its D and beta are scalars)
@@ -625,15 +625,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         const vec* qr = reinterpret_cast<const vec*>(static_cast<const T*>(p.q) + row * p.q_st + n * p.q_sh);
         const vec* dr = reinterpret_cast<const vec*>(static_cast<const T*>(p.dy) + row * p.dy_st + n * p.dy_sh);
 #pragma unroll
-        for (int s = 0; s < SK; ++s) {
-            qreg[s] = ok ? qr[2 * s + h] : vec{};
-            asm volatile("" : "+a"(qreg[s]));
-        }
+        for (int s = 0; s < SK; ++s) qreg[s] = ok ? qr[2 * s + h] : vec{};
 #pragma unroll
-        for (int s = 0; s < SV; ++s) {
-            dyreg[s] = ok ? dr[2 * s + h] : vec{};
-            asm volatile("" : "+a"(dyreg[s]));
-        }
+        for (int s = 0; s < SV; ++s) dyreg[s] = ok ? dr[2 * s + h] : vec{};
         if (ok) {
             const float2 st = p.rowstat[static_cast<int64_t>(n) * p.tq + it.q_start + qi];
             delta = st.x;

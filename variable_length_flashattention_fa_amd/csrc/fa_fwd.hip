@@ -14,7 +14,7 @@ namespace fa {
 
 // ------------------------------------------------------------------------------------------------
 // bf16 / fp16.  Workgroup: 8 waves (two per SIMD), FA16_DQ_BLOCK = 256 queries; wave w owns
-// queries 32w .. 32w+31 and keeps their Q rows (B operands, in accumulation registers), the
+// queries 32w .. 32w+31 and keeps their Q rows (B operands), the
 // online-softmax state and an O^T accumulator.  Key tiles of FA16_DQ_TILE_K = 64 rows are
 // walked as two 32-key steps:
 //   S^T = K Q^T                            (A = K rows from LDS)
@@ -85,7 +85,6 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             qreg[s] = ok ? qr[2 * s + h] : vec{};
-            asm volatile("" : "+a"(qreg[s]));
         }
     }
     // keys this lane's query admits, [klo, khi]: element a of a step at key k0s (key
