@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import DEV, assert_close, gpu_backward, log, make, oracle_backward, run_small
+from gpu_common import DEV, assert_close, gpu_backward, log, make, oracle_backward, oracle_forward, run_small
 from oracle import fa_oracle as O
 from test_gpu_forward import run_fwd
 from variable_length_flashattention_fa_amd import binding as B
@@ -100,7 +100,8 @@ def test_explicit_mask_forward_then_backward():
     dq, dk, dv = B.varlen_bwd(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, atten_mode=O.MASK_CAUSAL,
                               keep_prob=0.9, drop_mask=drop, scale=scale, atten_mask=am)
     torch.cuda.synchronize()
-    ref = oracle_backward(inp, y.cpu(), smax.cpu().numpy(), ssum.cpu().numpy(), O.MASK_CAUSAL, 0, 0, 0.9, scale,
-                          atten_mask=am_np)
+    # the oracle's own chain: its forward's Y and statistics, then its backward
+    yo, mo, lo = oracle_forward(inp, O.MASK_CAUSAL, 0, 0, 0.9, scale, atten_mask=am_np)
+    ref = oracle_backward(inp, yo, mo, lo, O.MASK_CAUSAL, 0, 0, 0.9, scale, atten_mask=am_np)
     for name, g, o in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         assert_close(name, g.double().cpu().numpy(), o, torch.bfloat16)

@@ -60,10 +60,10 @@ def test_grouped_forward_dropout_unequal_lengths():
 
 
 def test_grouped_forward_then_backward():
-    """Our grouped-head forward feeds our backward; the result matches the oracle end to end."""
+    """Our grouped-head forward feeds our backward; the chain matches the oracle's forward then backward."""
     import torch
 
-    from gpu_common import DEV, assert_close, oracle_backward
+    from gpu_common import DEV, assert_close, oracle_backward, oracle_forward
     from variable_length_flashattention_fa_amd import binding as B
 
     inp = make((300, 520), 4, 128, "bf16", mode=O.MASK_CAUSAL, kp=0.9, seed=28, kv_heads=2)
@@ -77,6 +77,61 @@ def test_grouped_forward_then_backward():
     B.fa_varlen_bwd(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, O.MASK_CAUSAL, 0, 0, 0.9, drop, scale,
                     4, dq, dk, dv)
     torch.cuda.synchronize()
-    ref = oracle_backward(inp, y.cpu(), smax.cpu().numpy(), ssum.cpu().numpy(), O.MASK_CAUSAL, 0, 0, 0.9, scale)
+    # the oracle's own chain: its forward's Y and statistics, then its backward
+    yo, mo, lo = oracle_forward(inp, O.MASK_CAUSAL, 0, 0, 0.9, scale)
+    ref = oracle_backward(inp, yo, mo, lo, O.MASK_CAUSAL, 0, 0, 0.9, scale)
     for name, g, o in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         assert_close(name, g.double().cpu().numpy(), o, torch.bfloat16)
+
+
+def test_grouped_narrow_v_full_size_sampled():
+    """16 sequences of U[256, 4096] tokens (34,320 in all), 32 query heads over 8 key/value heads,
+    Dk = 128, Dv = 64, bf16 causal: the whole backward on the GPU, sampled rows and keys against
+    the oracle.  Y and the statistics come from the plain torch forward used for full-size inputs."""
+    import time
+
+    import torch
+
+    from gpu_common import DEV, assert_close, log
+    from variable_length_flashattention_fa_amd import binding as B
+    from variable_length_flashattention_fa_amd import synth
+    from variable_length_flashattention_fa_amd.inputs_forward import forward_stats
+
+    t0 = time.time()
+    base = synth.workload(2)
+    wl = synth.Workload("grouped_narrow_v_16seq", "bf16", base.lengths, 32, 128, O.MASK_CAUSAL, seed=29,
+                        kv_heads=8, head_dim_v=64)
+    log(f"full-size grouped / narrow-V case: T={wl.tokens}, N=32 over 8, Dk=128, Dv=64")
+    inp = synth.make(wl)
+    dev = torch.device(DEV)
+    q, k, v, dy = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.dy))
+    y, smax, ssum = forward_stats(q, k, v, inp.cu_q, inp.cu_kv, mode=wl.mode, scale=wl.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B.fa_varlen_bwd(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, wl.mode, 0, 0, 1.0, None, wl.scale, 32,
+                    dq, dk, dv)
+    torch.cuda.synchronize()
+    log(f"  backward done {time.time() - t0:.1f}s; sampling against the oracle")
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    yh, smh, ssh = synth.as_float_array(y.cpu()), smax.cpu().numpy(), ssum.cpu().numpy()
+    qh, kh, vh, dyh = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v, inp.dy))
+    rng = np.random.default_rng(2029)
+    lens = np.diff(inp.cu_q)
+    kw = dict(mode=wl.mode, scale=wl.scale, head_num=32)
+    gq, oq, gk, ok_, gv, ov = [], [], [], [], [], []
+    for b, n in ((0, 0), (len(lens) - 1, 31), (int(rng.integers(len(lens))), int(rng.integers(32)))):
+        L = int(lens[b])
+        idx = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, L // 2, L - 2, L - 1],
+                                        rng.integers(0, L, 12)]).clip(0, L - 1))
+        oq.append(O.backward_dq_rows(qh, kh, vh, dyh, yh, smh, ssh, inp.cu_q, inp.cu_kv, b, n, idx, **kw))
+        gq.append(dq[inp.cu_q[b] + idx, n].double().numpy())
+        hk = n // 4
+        a, c = O.backward_dkdv_cols(qh, kh, vh, dyh, yh, smh, ssh, inp.cu_q, inp.cu_kv, b, hk, idx, **kw)
+        ok_.append(a)
+        ov.append(c)
+        gk.append(dk[inp.cu_kv[b] + idx, hk].double().numpy())
+        gv.append(dv[inp.cu_kv[b] + idx, hk].double().numpy())
+    for name, g, o in (("dq", gq, oq), ("dk", gk, ok_), ("dv", gv, ov)):
+        assert_close(name, np.concatenate(g), np.concatenate(o), torch.bfloat16)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    log(f"  sampled parity ok ({time.time() - t0:.1f}s)")

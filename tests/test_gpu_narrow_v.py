@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import DEV, assert_close, make, oracle_backward, run_small
+from gpu_common import DEV, assert_close, make, oracle_backward, oracle_forward, run_small
 from oracle import fa_oracle as O
 from test_gpu_forward import run_fwd
 from variable_length_flashattention_fa_amd import binding as B
@@ -48,7 +48,7 @@ def test_narrow_v_forward_dropout():
 
 
 def test_narrow_v_forward_then_backward():
-    """Our forward (Dv = 64) feeds our backward; the result matches the oracle end to end."""
+    """Our forward (Dv = 64) feeds our backward; the chain matches the oracle's forward then backward."""
     inp = make((300, 520), 4, 128, "bf16", mode=O.MASK_CAUSAL, kp=0.9, seed=46, dim_v=64, kv_heads=1)
     scale = 1.0 / np.sqrt(128)
     dev = torch.device(DEV)
@@ -61,6 +61,8 @@ def test_narrow_v_forward_then_backward():
     B.fa_varlen_bwd(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, O.MASK_CAUSAL, 0, 0, 0.9, drop, scale,
                     4, dq, dk, dv)
     torch.cuda.synchronize()
-    ref = oracle_backward(inp, y.cpu(), smax.cpu().numpy(), ssum.cpu().numpy(), O.MASK_CAUSAL, 0, 0, 0.9, scale)
+    # the oracle's own chain: its forward's Y and statistics, then its backward
+    yo, mo, lo = oracle_forward(inp, O.MASK_CAUSAL, 0, 0, 0.9, scale)
+    ref = oracle_backward(inp, yo, mo, lo, O.MASK_CAUSAL, 0, 0, 0.9, scale)
     for name, g, o in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         assert_close(name, g.double().cpu().numpy(), o, torch.bfloat16)

@@ -35,10 +35,15 @@ def _admit(rows: torch.Tensor, lkv: int, lq: int, mode: int, pre: int, nxt: int)
 def forward_stats(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_q, cu_kv, *, mode: int, pre: int = 0,
                   nxt: int = 0, keep_prob: float = 1.0, drop_mask: torch.Tensor | None = None, scale: float,
                   row_chunk: int = 2048):
-    """Returns (y [T, N, D] in q.dtype, softmax_max [N, T, 8] fp32, softmax_sum [N, T, 8] fp32)."""
+    """Returns (y [T, N, Dv] in q.dtype, softmax_max [N, T, 8] fp32, softmax_sum [N, T, 8] fp32).
+
+    k and v may hold fewer heads than q (a divisor of N): query head n reads key/value head
+    n // (N / Nkv).  v may have a smaller head dim than q and k.
+    """
     dev = q.device
     tq, heads, d = q.shape
-    y = torch.zeros_like(q)
+    group = heads // k.shape[1]
+    y = torch.zeros(tq, heads, v.shape[2], dtype=q.dtype, device=dev)
     mx = torch.full((heads, tq), float("-inf"), dtype=torch.float32, device=dev)
     sm = torch.zeros((heads, tq), dtype=torch.float32, device=dev)
     cu_q = [int(x) for x in cu_q]
@@ -51,8 +56,12 @@ def forward_stats(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_q, cu_kv
             bit_base += heads * lq * lkv
             continue
         qb = q[q0:q1].float().permute(1, 0, 2).contiguous()            # [N, Lq, D]
-        kt = k[k0:k1].float().permute(1, 2, 0).contiguous()            # [N, D, Lkv]
-        vb = v[k0:k1].float().permute(1, 0, 2).contiguous()            # [N, Lkv, D]
+        kt = k[k0:k1].float().permute(1, 2, 0)                          # [Nkv, D, Lkv]
+        vb = v[k0:k1].float().permute(1, 0, 2)                          # [Nkv, Lkv, Dv]
+        if group > 1:
+            kt = kt.repeat_interleave(group, dim=0)                     # [N, D, Lkv]
+            vb = vb.repeat_interleave(group, dim=0)
+        kt, vb = kt.contiguous(), vb.contiguous()
         for r0 in range(0, lq, row_chunk):
             r1 = min(lq, r0 + row_chunk)
             rows = torch.arange(r0, r1, device=dev, dtype=torch.int64)
@@ -74,7 +83,7 @@ def forward_stats(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_q, cu_kv
                 del bit
                 p = p * (z.float() / keep_prob)
                 del z
-            yb = torch.matmul(p, vb)                                     # [N, rc, D]
+            yb = torch.matmul(p, vb)                                     # [N, rc, Dv]
             del p
             y[q0 + r0:q0 + r1] = yb.permute(1, 0, 2).to(q.dtype)
             mx[:, q0 + r0:q0 + r1] = m
