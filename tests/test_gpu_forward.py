@@ -108,6 +108,15 @@ def test_forward_dropout_band_unaligned_bits():
     run_fwd(inp, O.MASK_BAND, 40, 7, kp=0.7)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_forward_negative_and_zero_scale(dtype, scale):
+    # a negative scale turns the row max into the row min of the raw scores; a zero scale makes
+    # every admitted key equally likely
+    inp = make((100, 257, 1, 64), 2, 128, dtype, mode=O.MASK_CAUSAL, seed=13)
+    run_fwd(inp, O.MASK_CAUSAL, scale=scale)
+
+
 def test_forward_non_contiguous_views():
     inp = make((90, 200), 2, 128, "bf16", mode=O.MASK_CAUSAL, seed=5)
 

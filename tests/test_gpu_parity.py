@@ -106,6 +106,12 @@ def test_non_contiguous_views():
     run_small(inp, O.MASK_CAUSAL, views=views)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_negative_scale(dtype):
+    inp = make((130, 77, 300), 2, 64, dtype, mode=O.MASK_BAND, pre=60, nxt=5, seed=17)
+    run_small(inp, O.MASK_BAND, 60, 5, scale=-0.09)
+
+
 def test_single_token_sequences():
     inp = make((1, 1, 1, 1), 2, 128, "bf16", mode=O.MASK_CAUSAL, seed=14)
     (dq, dk, dv), _, _ = run_small(inp, O.MASK_CAUSAL)
