@@ -137,6 +137,11 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BAND = 2 };
  *
  * Calls on different streams share one library workspace per device and
  * must not overlap in time.
+ *
+ * Graph capture: the first call with a given sequence layout, mask mode and dtype path builds
+ * and uploads a work list (a host-synchronous copy) and may grow the workspace.  Later calls
+ * with the same layout only enqueue kernels on stream, so they can be recorded into a HIP graph
+ * and replayed; make one uncaptured call first.
  */
 int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
                   const fa_tensor_t* dy, const fa_tensor_t* y,

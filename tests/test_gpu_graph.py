@@ -1,0 +1,59 @@
+"""Graph capture: once a layout's work list is cached, a call only enqueues kernels (no
+allocation, copy or synchronisation), so the backward and the forward can be recorded into a HIP
+graph. Each replay must reproduce the eager result bit for bit (every path is deterministic);
+replays are separated by eager work and synchronisations."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import DEV, log, make
+from oracle import fa_oracle as O
+from variable_length_flashattention_fa_amd import binding as B
+from variable_length_flashattention_fa_amd.inputs_forward import forward_stats
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_and_forward_replay_in_a_graph(dtype):
+    inp = make((700, 129, 1024), 4, 128, dtype, mode=O.MASK_CAUSAL, kp=0.9, seed=61, kv_heads=2)
+    dev = torch.device(DEV)
+    q, k, v, dy = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.dy))
+    drop = torch.from_numpy(inp.drop_mask).to(dev)
+    scale = 1.0 / np.sqrt(128)
+    y, smax, ssum = forward_stats(q, k, v, inp.cu_q, inp.cu_kv, mode=O.MASK_CAUSAL, keep_prob=0.9, drop_mask=drop,
+                                  scale=scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    yf = torch.empty_like(y)
+    mf, lf = torch.empty_like(smax), torch.empty_like(ssum)
+
+    def calls():
+        B.fa_varlen_bwd(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, O.MASK_CAUSAL, 0, 0, 0.9, drop, scale, 4,
+                        dq, dk, dv)
+        B.fa_varlen_fwd(q, k, v, inp.cu_q, inp.cu_kv, O.MASK_CAUSAL, 0, 0, 0.9, drop, scale, 4, yf, mf, lf)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        calls()  # eager: builds and caches both work lists, sizes the workspace
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dq, dk, dv, yf, mf, lf)]
+
+    log(f"capturing the backward and the forward ({dtype})")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(3):
+        for t in (dq, dk, dv, yf, mf, lf):
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((dq, dk, dv, yf, mf, lf), ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager call"
+    # eager again after the replays: still the same
+    calls()
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv, yf, mf, lf), ref):
+        assert torch.equal(a, b)
