@@ -30,6 +30,11 @@
  * Errors are detected before any device work is enqueued; on a non-OK
  * status nothing has been launched and fa_last_error() describes the cause.
  * On FA_OK the work is enqueued asynchronously on `stream`.
+ *
+ * Determinism (the page's constraints section makes a deterministic mode
+ * opt-in): every entry point here is deterministic.  No kernel uses atomics,
+ * each output row has one owner and a fixed summation order, so repeated
+ * calls on the same inputs give bitwise identical results.
  */
 #ifndef FA_VARLEN_H
 #define FA_VARLEN_H
