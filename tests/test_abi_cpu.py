@@ -307,3 +307,39 @@ def test_forward_narrow_v():
 
 def test_forward_empty_input_is_ok():
     assert _fwd(q=_t(0), y=_t(0), cu_q=(0, 0), cu_kv=(0, 10), smax=None, ssum=None)[0] == B.FA_OK
+
+
+# --- the Python binding's checks of what the raw pointers hide -------------------------------
+
+def _cpu_args(dtype=None):
+    import torch
+    dt = dtype or torch.bfloat16
+    q = torch.zeros(10, 2, 64, dtype=dt)
+    st = torch.zeros(2, 10, 8, dtype=torch.float32)
+    return q, st
+
+
+def test_binding_rejects_host_tensors():
+    q, st = _cpu_args()
+    with pytest.raises(ValueError, match="device tensor"):
+        B.fa_varlen_bwd(q, q, q, q, q, st, st, (0, 10), (0, 10), 0, 0, 0, 1.0, None, 0.125, 2, q, q, q)
+    with pytest.raises(ValueError, match="device tensor"):
+        B.fa_varlen_fwd(q, q, q, (0, 10), (0, 10), 0, 0, 0, 1.0, None, 0.125, 2, q, st, st)
+
+
+def test_binding_checks_shapes_and_mask_sizes(monkeypatch):
+    import torch
+    # stand-in device placement so the shape checks can run without a GPU
+    q, st = _cpu_args()
+    monkeypatch.setattr(torch.Tensor, "is_cuda", property(lambda self: True))
+    with pytest.raises(ValueError, match=r"\[N, Tq, 8\]"):
+        B._check_args(q, {}, dict(softmax_max=st[:, :9]), (0, 10), (0, 10), 1.0, None, None)
+    with pytest.raises(ValueError, match=r"\[N, Tq, 8\]"):
+        B._check_args(q, {}, dict(softmax_max=st.double()), (0, 10), (0, 10), 1.0, None, None)
+    drop = torch.zeros(24, dtype=torch.uint8)  # 2 heads * 10 * 10 bits need 25 bytes
+    with pytest.raises(ValueError, match="25 bytes"):
+        B._check_args(q, {}, {}, (0, 10), (0, 10), 0.9, drop, None)
+    B._check_args(q, {}, {}, (0, 10), (0, 10), 0.9, torch.zeros(25, dtype=torch.uint8), None)
+    with pytest.raises(ValueError, match="atten_mask axes"):
+        B._check_args(q, {}, {}, (0, 10), (0, 10), 1.0, None, torch.zeros(2, 2, 10, 10, dtype=torch.uint8))
+    B._check_args(q, {}, {}, (0, 10), (0, 10), 1.0, None, torch.zeros(1, 2, 10, 10, dtype=torch.uint8))

@@ -157,6 +157,30 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_args(q, tensors: dict, stats: dict, cu_q, cu_kv, keep_prob, drop_mask, atten_mask) -> None:
+    """Checks what the C ABI cannot see behind its raw pointers: every tensor lives on q's device,
+    the statistics are [N, Tq, 8] fp32 and contiguous, the dropout mask holds enough bits and an
+    explicit mask's batch and head axes are 1 or full.  Raises ValueError."""
+    if q is None:
+        return  # the library reports the null pointer
+    for name, t in dict(tensors, **stats, drop_mask=drop_mask, atten_mask=atten_mask).items():
+        if t is not None and (not t.is_cuda or t.device != q.device):
+            raise ValueError(f"{name} must be a device tensor on {q.device}")
+    heads, tq = q.shape[1], q.shape[0]
+    for name, t in stats.items():
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (heads, tq, 8) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 [N, Tq, 8] = [{heads}, {tq}, 8] tensor")
+    lq = np.diff(np.asarray(cu_q, dtype=np.int64))
+    lk = np.diff(np.asarray(cu_kv, dtype=np.int64))
+    if drop_mask is not None and keep_prob < 1.0 and lq.size == lk.size:
+        need = (int(np.sum(heads * lq * lk)) + 7) // 8
+        if drop_mask.dtype != torch.uint8 or drop_mask.numel() < need:
+            raise ValueError(f"drop_mask must be uint8 with at least {need} bytes")
+    if atten_mask is not None and atten_mask.dim() == 4:
+        if atten_mask.shape[0] not in (1, lq.size) or atten_mask.shape[1] not in (1, heads):
+            raise ValueError("atten_mask axes must be [B or 1, N or 1, Sq, Skv]")
+
+
 def fa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dy: torch.Tensor, y: torch.Tensor,
                   softmax_max: torch.Tensor, softmax_sum: torch.Tensor, cu_seqlens_q, cu_seqlens_kv,
                   atten_mode: int, pre_tokens: int, next_tokens: int, keep_prob: float,
@@ -168,6 +192,8 @@ def fa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dy: torch.T
     raises FaError on a non-OK status.
     """
     lib = load()
+    _check_args(q, dict(k=k, v=v, dy=dy, y=y, dq=dq, dk=dk, dv=dv), dict(softmax_max=softmax_max,
+                softmax_sum=softmax_sum), cu_seqlens_q, cu_seqlens_kv, keep_prob, drop_mask, None)
     tq, tk, tv, tdy, ty = (tensor_desc(x) for x in (q, k, v, dy, y))
     tdq, tdk, tdv = (tensor_desc(x) for x in (dq, dk, dv))
     sq, aq = _seqlens(cu_seqlens_q)
@@ -199,6 +225,8 @@ def fa_varlen_bwd_masked(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q,
                          head_num: int, dq, dk, dv, stream=None) -> None:
     """fa_varlen_bwd with an explicit mask tensor (see mask_desc); same conventions."""
     lib = load()
+    _check_args(q, dict(k=k, v=v, dy=dy, y=y, dq=dq, dk=dk, dv=dv), dict(softmax_max=softmax_max,
+                softmax_sum=softmax_sum), cu_seqlens_q, cu_seqlens_kv, keep_prob, drop_mask, atten_mask)
     tq, tk, tv, tdy, ty = (tensor_desc(x) for x in (q, k, v, dy, y))
     tdq, tdk, tdv = (tensor_desc(x) for x in (dq, dk, dv))
     tm = mask_desc(atten_mask)
@@ -261,6 +289,8 @@ def fa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
     non-OK status.
     """
     lib = load()
+    _check_args(q, dict(k=k, v=v, y=y), dict(softmax_max=softmax_max, softmax_sum=softmax_sum), cu_seqlens_q,
+                cu_seqlens_kv, keep_prob, drop_mask, None)
     tq, tk, tv, ty = (tensor_desc(x) for x in (q, k, v, y))
     sq, aq = _seqlens(cu_seqlens_q)
     sk, ak = _seqlens(cu_seqlens_kv)
@@ -290,6 +320,8 @@ def fa_varlen_fwd_masked(q, k, v, cu_seqlens_q, cu_seqlens_kv, atten_mode: int, 
                          softmax_sum, stream=None) -> None:
     """fa_varlen_fwd with an explicit mask tensor (see mask_desc); same conventions."""
     lib = load()
+    _check_args(q, dict(k=k, v=v, y=y), dict(softmax_max=softmax_max, softmax_sum=softmax_sum), cu_seqlens_q,
+                cu_seqlens_kv, keep_prob, drop_mask, atten_mask)
     tq, tk, tv, ty = (tensor_desc(x) for x in (q, k, v, y))
     tm = mask_desc(atten_mask)
     sq, aq = _seqlens(cu_seqlens_q)
