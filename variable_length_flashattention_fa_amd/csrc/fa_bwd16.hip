@@ -605,7 +605,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     for (int u = 0; u < TWK; ++u) koff[u] = dma_offset<DK>(w * TWK + u, lane, p.k_st) - 1024 * u;
 #pragma unroll
     for (int u = 0; u < TWV; ++u) voff[u] = dma_offset<DV>(w * TWV + u, lane, p.v_st) - 1024 * u;
-    auto issue = [&](int kt, int b) {
+    auto issue = [&](int kt, int b) __attribute__((always_inline)) {
         const int k0 = kt * BK;
         const i32x4 rk = buffer_desc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st));
         const i32x4 rv = buffer_desc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st));
@@ -669,6 +669,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     f32x16 accQ[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i) accQ[i] = zero16();
+    // Without dropout, dP^T - D is formed by the MFMA chain itself: it starts from -D (the lane's
+    // query) instead of zero.  With dropout the keep bit scales dP but not D, so it starts at zero.
+    constexpr bool FOLD_D = !DROP;
+    f32x16 pinit;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pinit[i] = FOLD_D ? -delta : 0.f;
 
     // explicit mask block of this (sequence, head); this lane reads row qi
     __amdgpu_buffer_rsrc_t mrs;
@@ -678,7 +684,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     }
 
     // one 32-key step (keys k0s .. k0s + 31, rows 32 kh of the tile in cK / cV)
-    auto kstep = [&](const T* cK, const T* cV, int k0s) {
+    auto kstep = [&](const T* cK, const T* cV, int k0s) __attribute__((always_inline)) {
         // explicit mask bytes of keys k0s + 4h + cc(a), issued before the products that hide them
         uint32_t mk[16];
         if constexpr (XM) {
@@ -689,7 +695,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
                 mk[a] = __builtin_amdgcn_raw_buffer_load_b8(mrs, mrow + 8 * (a >> 2) + (a & 3), 0, 0);
         }
         f32x16 accS = zero16();
-        f32x16 accP = zero16();
+        f32x16 accP = pinit;
 #pragma unroll
         for (int s = 0; s < SV; ++s) {
             const vec ak = lds_row<vec>(cK, loK.row[s]);
@@ -702,7 +708,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         // dS^T = Ps (dP Z/kp - D); element (key k0s + 4h + cc(a), query qi)
         const bool full = !XM && wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
         uint32_t dsw[2][4];
-        auto softmax_grad = [&](auto masked_tag) {
+        auto softmax_grad = [&](auto masked_tag) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked_tag)::value;
             const int lo_h = kbase - k0s;
 #pragma unroll
@@ -726,7 +732,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
                         }
                         ds[e] = pv * (accP[a + e] * zk - delta);
                     } else {
-                        ds[e] = pv * (accP[a + e] - delta);
+                        ds[e] = pv * accP[a + e];  // accP already holds dP - D
                     }
                 }
                 dsw[a >> 3][(a & 7) >> 1] = pack2<T>(ds[0], ds[1]);
@@ -748,16 +754,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         }
     };
 
-    if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
-    int b = 0;
-    for (int kt = it.tile_begin; kt < it.tile_end; ++kt) {
+    // one key tile in buffer B (a constant, so that every LDS address of the tile is a fixed
+    // offset from the lane's own)
+    auto tile = [&](int kt, auto bc) __attribute__((always_inline)) {
+        constexpr int B = decltype(bc)::value;
         wait_dma();
-        __syncthreads();  // tile kt is in buffer b; every wave is done with buffer b ^ 1
-        if (kt + 1 < it.tile_end) issue(kt + 1, b ^ 1);
-        kstep(sK[b], sV[b], kt * BK);
-        kstep(sK[b] + 32 * DK, sV[b] + 32 * DV, kt * BK + 32);
-        b ^= 1;
+        __syncthreads();  // tile kt is in buffer B; every wave is done with buffer B ^ 1
+        if (kt + 1 < it.tile_end) issue(kt + 1, B ^ 1);
+        kstep(sK[B], sV[B], kt * BK);
+        kstep(sK[B] + 32 * DK, sV[B] + 32 * DV, kt * BK + 32);
+    };
+    if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
+    int kt = it.tile_begin;
+    for (; kt + 1 < it.tile_end; kt += 2) {
+        tile(kt, IC<0>{});
+        tile(kt + 1, IC<1>{});
     }
+    if (kt < it.tile_end) tile(kt, IC<0>{});
 
     // epilogue: dQ = scale * (dQ^T)^T; the lane holds query qi, head-dim rows
     // nd*32 + 8g + 4h + 0..3 (four consecutive values)
