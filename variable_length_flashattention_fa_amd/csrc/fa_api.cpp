@@ -66,7 +66,7 @@ bool aligned16(const fa_tensor_t* t) {
 }
 
 struct Workspace {
-    float2* rowstat = nullptr;
+    float* rowstat = nullptr;  // planes of -D and beta
     size_t rowstat_bytes = 0;
     fa_work_item_t* items = nullptr;
     size_t items_cap = 0;
@@ -420,8 +420,8 @@ extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
 
     {
         void* ptr = ws.rowstat;
-        int g = grow(&ptr, &ws.rowstat_bytes, static_cast<size_t>(tq * heads) * sizeof(float2), "row statistics");
-        ws.rowstat = static_cast<float2*>(ptr);
+        int g = grow(&ptr, &ws.rowstat_bytes, static_cast<size_t>(tq * heads) * 2 * sizeof(float), "row statistics");
+        ws.rowstat = static_cast<float*>(ptr);
         if (g != FA_OK) return g;
     }
 

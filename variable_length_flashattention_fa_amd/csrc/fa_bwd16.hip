@@ -96,7 +96,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     // buffer b: Q tile at sBuf[b], dY tile at sBuf[b] + TILEQ (one array, so that the reads of
     // both tiles share one base address and differ by an immediate offset)
     __shared__ __attribute__((aligned(16))) T sBuf[NB][TILEQ + TILED];
-    __shared__ __attribute__((aligned(16))) float2 sSt[NB][BQ];
+    // row statistics of buffer b: sSt[b][0] = -D, sSt[b][1] = beta of the tile's rows
+    __shared__ __attribute__((aligned(16))) float sSt[NB][2][BQ];
+    // Without dropout the dP chain of a step starts from -D of its rows, so that it ends with
+    // dP - D; with dropout the keep bit scales dP but not D, and the chain starts from zero.
+    constexpr bool FOLD_D = !DROP;
     auto qtile = [&](int b) -> T* { return sBuf[b]; };
     auto dtile = [&](int b) -> T* { return sBuf[b] + TILEQ; };
 
@@ -133,7 +137,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         int n = hk * p.group;
         const T* gq = nullptr;
         const T* gdy = nullptr;
-        const float2* gstat = nullptr;
+        const float* gstat = nullptr;  // -D of the head's rows; beta follows one plane later
+        const int64_t plane = static_cast<int64_t>(p.heads) * p.tq;
         __amdgpu_buffer_rsrc_t mrs;
         int qoff[TWQ];
         int dyoff[TWD];
@@ -193,9 +198,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             const uint32_t md = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(dtile(b) + w * TWD * 512)));
             dma_pair<TWQ, TWD>(__builtin_amdgcn_readfirstlane(mq), rq, qoff, __builtin_amdgcn_readfirstlane(md), rd,
                                dyoff);
-            if (w == NW - 1 && lane < BQ / 2) {
-                const i32x4 rs = buffer_desc(gstat + q0, q0 < L ? static_cast<uint32_t>(min(L - q0, BQ) * 8) : 0u);
-                dma16_async(sSt[b], rs, lane * 16);
+            if (w == NW - 1 && lane < BQ / 4) {
+                // rows past the sequence read as zero
+                const uint32_t nbytes = q0 < L ? static_cast<uint32_t>(min(L - q0, BQ) * 4) : 0u;
+                dma16_async(sSt[b][0], buffer_desc(gstat + q0, nbytes), lane * 16);
+                dma16_async(sSt[b][1], buffer_desc(gstat + plane + q0, nbytes), lane * 16);
             }
         };
 
@@ -237,11 +244,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 }
             }
         };
-        // statistics {delta, beta} of rows 32*sm + 8g + 4h + 0..3
+        // statistics of rows 32*sm + 8g + 4h + 0..3: dst[0] = -D (needed only with dropout),
+        // dst[1] = beta
         auto read_stats = [&](const Where& wh, int g, f32x4* dst) {
-            const float2* base = sSt[wh.sb] + 32 * wh.sm + 8 * g + 4 * h;
-            dst[0] = *reinterpret_cast<const f32x4*>(base);
-            dst[1] = *reinterpret_cast<const f32x4*>(base + 2);
+            const int r = 32 * wh.sm + 8 * g + 4 * h;
+            if constexpr (!FOLD_D) dst[0] = *reinterpret_cast<const f32x4*>(&sSt[wh.sb][0][r]);
+            dst[1] = *reinterpret_cast<const f32x4*>(&sSt[wh.sb][1][r]);
+        };
+        // -D of the X rows 32*xm + 4h + 8*(a/4) + a%4, in accumulator order: the start of the dP chain
+        auto read_dinit = [&](const Where& wh, f32x16& dst) {
+            if constexpr (FOLD_D) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(&sSt[wh.xb][0][32 * wh.xm + 8 * g + 4 * h]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[4 * g + r] = v[r];
+                }
+            }
         };
 
         // pipeline state carried from step to step
@@ -249,6 +268,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         f32x4 stC[4][2];       // statistics of the softmax rows of the step
         f32x16 sC = zero16();  // S and dP consumed by this step's softmax gradient
         f32x16 pC = zero16();
+        f32x16 dX = zero16();  // start of this step's dP chain (-D of its X rows, or zero)
         vec pkY[2];            // packed P and dS consumed by this step's Y (two 16-row halves)
         vec dsY[2];
         uint32_t dbC[16];      // dropout mask bytes and bit base of the softmax rows
@@ -279,6 +299,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             const int lo_h = lo_base - (t * BQ + 32 * wh.sm);
             f32x16 sN = zero16();
             f32x16 pN = zero16();
+            f32x16 dXn = zero16();
             uint32_t pkw[2][4];
             uint32_t dsw[2][4];
             vec nopr[LA];
@@ -322,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                             sN = Op16<T>::mfma(a, kreg[s], s == 0 ? zero16() : sN);
                             pin(sN);
                         } else {
-                            pN = Op16<T>::mfma(a, vreg[s], s == 0 ? zero16() : pN);
+                            pN = Op16<T>::mfma(a, vreg[s], s == 0 ? dX : pN);
                             pin(pN);
                         }
                     }
@@ -344,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     if constexpr (p_slot(a, NOPS) == k) {
                         float x = sC[a];
                         pin(x);
-                        const float bt = stC[a / 4][(a % 4) / 2][2 * (a % 2) + 1];
+                        const float bt = stC[a / 4][1][a % 4];
                         const float e = __builtin_amdgcn_exp2f(x * p.exp_scale - bt);
                         if constexpr (MASKED) {
                             bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(rng);
@@ -358,15 +379,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     if constexpr (d_slot(a, NOPS) == k) {
                         float y = pC[a];
                         pin(y);
-                        const float dl = stC[a / 4][(a % 4) / 2][2 * (a % 2)];
                         if constexpr (DROP) {
+                            const float ndl = stC[a / 4][0][a % 4];
                             const int u = dcC + cc * K;
                             const bool keep = __builtin_amdgcn_ubfe(dbC[a], u & 7, 1) != 0;
                             pdv[a] = keep ? pv[a] * p.inv_keep : 0.f;
-                            dsv[a] = pv[a] * ((keep ? y * p.inv_keep : 0.f) - dl);
+                            dsv[a] = pv[a] * ((keep ? y * p.inv_keep : 0.f) + ndl);
                         } else {
                             pdv[a] = pv[a];
-                            dsv[a] = pv[a] * (y - dl);
+                            dsv[a] = pv[a] * y;  // y = dP - D
                         }
                         if constexpr (a % 2 == 1) {
                             pkw[a / 8][(a % 8) / 2] = pack2<T>(pdv[a - 1], pdv[a]);
@@ -395,7 +416,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     });
                 } else if constexpr (KIND != kStepLast) {
                     nopr[kr - NOPS] = read_op(nw, IC<kr - NOPS>{});
-                    if constexpr (kr == NOPS && (NKIND == kStepA || NKIND == kStepB)) read_stats(nw, 0, stN);
+                    if constexpr (kr == NOPS && (NKIND == kStepA || NKIND == kStepB)) {
+                        read_stats(nw, 0, stN);
+                        read_dinit(nw, dXn);
+                    }
                 }
                 // ---- dropout mask byte of X element k
                 if constexpr (DROP && HX && k < 16) {
@@ -444,6 +468,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 if constexpr (NKIND == kStepA || NKIND == kStepB) {
                     stC[0][0] = stN[0];
                     stC[0][1] = stN[1];
+                    dX = dXn;
                 }
             }
         };
@@ -476,7 +501,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             n = hk * p.group + r;
             gq = static_cast<const T*>(p.q) + static_cast<int64_t>(it.q_start) * p.q_st + n * p.q_sh;
             gdy = static_cast<const T*>(p.dy) + static_cast<int64_t>(it.q_start) * p.dy_st + n * p.dy_sh;
-            gstat = p.rowstat + static_cast<int64_t>(n) * p.tq + it.q_start;
+            gstat = p.rowstat + static_cast<int64_t>(n) * p.tq + it.q_start;  // plane of -D
             if constexpr (XM) {
                 const uint8_t* mb = p.mask.amask + it.seq * p.mask.am_sb + n * p.mask.am_sn;
                 mrs = raw_rsrc(mb, static_cast<uint32_t>((L - 1) * p.mask.am_sq + K));
@@ -502,6 +527,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 static_for<0, LA>([&](auto kc) {
                     if constexpr (decltype(kc)::value % 2 == 0) opr[decltype(kc)::value] = read_op(w0, kc);
                 });
+                read_dinit(w0, dX);
             }
             step(IC<kStepFirst>{}, IC<kStepA>{}, IC<0>{}, tb, 0, 0);
             int b = 0;
@@ -617,7 +643,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     // this lane's Q and dY rows (B operands of S^T = K Q^T and dP^T = V dY^T) and statistics
     vec qreg[SK];
     vec dyreg[SV];
-    float delta = 0.f;
+    float ndelta = 0.f;  // -D of this lane's query
     float beta = 0.f;
     {
         const bool ok = qi < L;
@@ -629,9 +655,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 #pragma unroll
         for (int s = 0; s < SV; ++s) dyreg[s] = ok ? dr[2 * s + h] : vec{};
         if (ok) {
-            const float2 st = p.rowstat[static_cast<int64_t>(n) * p.tq + it.q_start + qi];
-            delta = st.x;
-            beta = st.y;
+            const int64_t o = static_cast<int64_t>(n) * p.tq + it.q_start + qi;
+            ndelta = p.rowstat[o];
+            beta = p.rowstat[static_cast<int64_t>(p.heads) * p.tq + o];
         }
     }
     // keys this lane's query admits, [klo, khi]; element a of a step starting at key k0s
@@ -674,7 +700,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     constexpr bool FOLD_D = !DROP;
     f32x16 pinit;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pinit[i] = FOLD_D ? -delta : 0.f;
+    for (int i = 0; i < 16; ++i) pinit[i] = FOLD_D ? ndelta : 0.f;
 
     // explicit mask block of this (sequence, head); this lane reads row qi
     __amdgpu_buffer_rsrc_t mrs;
@@ -730,7 +756,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
                                 it.drop_base + (static_cast<int64_t>(n) * L + qi) * K + k0s + cc + 4 * h;
                             zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
                         }
-                        ds[e] = pv * (accP[a + e] * zk - delta);
+                        ds[e] = pv * fmaf(accP[a + e], zk, ndelta);
                     } else {
                         ds[e] = pv * accP[a + e];  // accP already holds dP - D
                     }

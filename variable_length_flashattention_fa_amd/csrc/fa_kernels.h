@@ -36,10 +36,12 @@ struct TensorArg {
     int64_t stride_h;
 };
 
-// Row pass: delta[n, t] = sum_d dY * Y (fp32, over V's head dim), beta[n, t] = max*log2(e) +
-// log2(sum), stored as float2 {delta, beta} in rowstat[n * tq + t].
+// Row pass: D[n, t] = sum_d dY * Y (fp32, over V's head dim) and beta[n, t] = max*log2(e) +
+// log2(sum).  rowstat holds two planes of heads * tq floats: rowstat[n * tq + t] = -D[n, t]
+// (negated: the kernels start their dP accumulators from it) and
+// rowstat[heads * tq + n * tq + t] = beta[n, t].
 hipError_t launch_preprocess(int32_t dtype, int head_dim_v, TensorArg dy, TensorArg y,
-                             const float* softmax_max, const float* softmax_sum, float2* rowstat,
+                             const float* softmax_max, const float* softmax_sum, float* rowstat,
                              int64_t tq, int64_t heads, hipStream_t stream);
 
 struct MainArgs {
@@ -50,7 +52,7 @@ struct MainArgs {
     int64_t dk_st, dk_sh;
     void* dv;
     int64_t dv_st, dv_sh;
-    const float2* rowstat;
+    const float* rowstat;  // planes of -D and beta (see launch_preprocess)
     const fa_work_item_t* items;    // key-block items (kBlockKv32 keys, kTileQ32 query tiles)
     const fa_work_item_t* items_q;  // query-block items (FA32_FWD_BLOCK queries)
     const uint8_t* drop_mask;
@@ -93,7 +95,7 @@ struct Bwd16Args {
     void* dk;
     void* dv;
     int64_t dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh;
-    const float2* rowstat;
+    const float* rowstat;  // planes of -D and beta (see launch_preprocess)
     const fa_work_item_t* items_kv;  // key-block items (FA16_DKDV_BLOCK keys, FA16_DKDV_TILE_Q tiles)
     const fa_work_item_t* items_q;   // query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles)
     const uint8_t* drop_mask;

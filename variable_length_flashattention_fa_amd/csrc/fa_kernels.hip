@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
                                                          const T* __restrict__ y, int64_t y_st, int64_t y_sh,
                                                          const float* __restrict__ smax,
                                                          const float* __restrict__ ssum,
-                                                         float2* __restrict__ rowstat, int64_t tq, int heads) {
+                                                         float* __restrict__ rowstat, int64_t tq, int heads) {
     constexpr int VEC = 16 / sizeof(T);
     constexpr int TPR = D / VEC;    // threads per (token, head) row of dY and Y (D = V's head dim)
     constexpr int RPB = 256 / TPR;
@@ -123,7 +123,9 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
         const int64_t s = (static_cast<int64_t>(n) * tq + t) * 8;
         const float mx = smax[s];
         const float sm = ssum[s];
-        rowstat[static_cast<int64_t>(n) * tq + t] = make_float2(part, mx * kLog2e + __builtin_amdgcn_logf(sm));
+        const int64_t o = static_cast<int64_t>(n) * tq + t;
+        rowstat[o] = -part;
+        rowstat[static_cast<int64_t>(heads) * tq + o] = mx * kLog2e + __builtin_amdgcn_logf(sm);
     }
 }
 
@@ -141,7 +143,7 @@ struct DevArgs {
     void* dk;
     void* dv;
     int64_t dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh;
-    const float2* rowstat;
+    const float* rowstat;
     const fa_work_item_t* items;    // key-block items (dK / dV)
     const fa_work_item_t* items_q;  // query-block items (dQ)
     const uint8_t* drop_mask;
@@ -258,7 +260,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
             }
             if (tid < BQ) {
                 const int qi = q0 + tid;
-                sStat[tid] = qi < L ? p.rowstat[static_cast<int64_t>(n) * p.tq + it.q_start + qi] : make_float2(0.f, 0.f);
+                const int64_t o = static_cast<int64_t>(n) * p.tq + it.q_start + qi;
+                const int64_t plane = static_cast<int64_t>(p.heads) * p.tq;
+                sStat[tid] = qi < L ? make_float2(-p.rowstat[o], p.rowstat[plane + o]) : make_float2(0.f, 0.f);
             }
             __syncthreads();
 
@@ -414,7 +418,8 @@ __global__ __launch_bounds__(2 * FA32_FWD_BLOCK) void bwd_dq32_kernel(const DevA
     }
 #pragma unroll
     for (int d = 0; d < HV; ++d) dyr[d] = dy[d];
-    const float2 st = p.rowstat[static_cast<int64_t>(n) * p.tq + row];  // {D_i, beta_i}
+    const int64_t so = static_cast<int64_t>(n) * p.tq + row;
+    const float2 st = make_float2(-p.rowstat[so], p.rowstat[static_cast<int64_t>(p.heads) * p.tq + so]);  // {D_i, beta_i}
     const int64_t bit0 = it.drop_base + (static_cast<int64_t>(n) * L + qi) * K;
     // this query's row of the explicit mask, if any (both lanes of the query skip the same keys)
     const uint8_t* mrow = p.mask.amask == nullptr
@@ -453,7 +458,7 @@ __global__ __launch_bounds__(2 * FA32_FWD_BLOCK) void bwd_dq32_kernel(const DevA
 // ----------------------------------------------------------------------------
 
 template <typename T, int D>
-static hipError_t preprocess_t(TensorArg dy, TensorArg y, const float* smax, const float* ssum, float2* rowstat,
+static hipError_t preprocess_t(TensorArg dy, TensorArg y, const float* smax, const float* ssum, float* rowstat,
                                int64_t tq, int64_t heads, hipStream_t stream) {
     constexpr int TPR = D / (16 / sizeof(T));
     constexpr int RPB = 256 / TPR;
@@ -466,7 +471,7 @@ static hipError_t preprocess_t(TensorArg dy, TensorArg y, const float* smax, con
 }
 
 hipError_t launch_preprocess(int32_t dtype, int head_dim_v, TensorArg dy, TensorArg y, const float* smax,
-                             const float* ssum, float2* rowstat, int64_t tq, int64_t heads, hipStream_t stream) {
+                             const float* ssum, float* rowstat, int64_t tq, int64_t heads, hipStream_t stream) {
 #define FA_PRE(T, D) return preprocess_t<T, D>(dy, y, smax, ssum, rowstat, tq, heads, stream)
     if (dtype == FA_BF16) { if (head_dim_v == 128) FA_PRE(__bf16, 128); FA_PRE(__bf16, 64); }
     if (dtype == FA_F16) { if (head_dim_v == 128) FA_PRE(_Float16, 128); FA_PRE(_Float16, 64); }
