@@ -65,6 +65,30 @@ struct Interleave {
     static constexpr int index(int j) { return j < 2 * M ? j / 2 : M + (j - 2 * M); }
 };
 
+// Order of two MFMA chains of NA and NB instructions in which chain A leads with LEAD
+// instructions, then B and A alternate while both last, then the rest of the longer one.
+template <int NA, int NB, int LEAD>
+struct LeadInterleave {
+    static constexpr bool pick_a(int x, int a, int b) {
+        return a < NA && (b >= NB || a < LEAD || (x - LEAD) % 2 == 1);
+    }
+    static constexpr bool is_a(int j) {
+        int a = 0, b = 0;
+        for (int x = 0; x < j; ++x) (pick_a(x, a, b) ? a : b) += 1;
+        return pick_a(j, a, b);
+    }
+    static constexpr int index(int j) {
+        int a = 0, b = 0;
+        for (int x = 0; x < j; ++x) (pick_a(x, a, b) ? a : b) += 1;
+        return pick_a(j, a, b) ? a : b;
+    }
+    static constexpr int first_b() {  // slot of chain B's first instruction
+        int x = 0;
+        while (is_a(x)) ++x;
+        return x;
+    }
+};
+
 // Slots of the softmax-gradient work of element a (16 per step) among the NOPS slots: P at
 // p_slot(a), dS at d_slot(a) (the same slot when NOPS == 16, P first).
 constexpr int p_slot(int a, int nops) { return a * nops / 16; }
@@ -88,19 +112,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     constexpr int TILED = BQ * DV;
     constexpr int TWQ = TILEQ / 8 / 64 / NW;  // DMA instructions per wave and Q tile
     constexpr int TWD = TILED / 8 / 64 / NW;  // ... and dY tile
-    using XS = Interleave<SK, SV>;        // X slots: S (chain A) and dP (chain B)
+    // Without dropout the dP chain of a step starts from -D of its rows, so that it ends with
+    // dP - D; with dropout the keep bit scales dP but not D, and the chain starts from zero.
+    constexpr bool FOLD_D = !DROP;
+    // X slots: S (chain A) and dP (chain B); S leads by two so that the start of the dP chain
+    // (-D of the step's rows) can be read from LDS LA slots ahead, within the step
+    // (with dropout the chain starts at zero and the plain alternation is kept)
+    using XS = std::conditional_t<FOLD_D, LeadInterleave<SK, SV, 2>, Interleave<SK, SV>>;
+    constexpr int KD = FOLD_D ? 2 * LeadInterleave<SK, SV, 2>::first_b() : LA;  // slot of the first dP MFMA
     using YS = Interleave<SV, SK>;        // Y slots: dV (chain A) and dK (chain B)
     static_assert(BQ == 64 && BKV == 32 * NW && (TILED / 8 / 64) % NW == 0 && NOPS >= 16 && LA % 2 == 0 &&
-                  LA < NOPS && DV <= DK, "tile shape");
+                  LA < NOPS && DV <= DK && KD >= LA, "tile shape");
 
     // buffer b: Q tile at sBuf[b], dY tile at sBuf[b] + TILEQ (one array, so that the reads of
     // both tiles share one base address and differ by an immediate offset)
     __shared__ __attribute__((aligned(16))) T sBuf[NB][TILEQ + TILED];
     // row statistics of buffer b: sSt[b][0] = -D, sSt[b][1] = beta of the tile's rows
     __shared__ __attribute__((aligned(16))) float sSt[NB][2][BQ];
-    // Without dropout the dP chain of a step starts from -D of its rows, so that it ends with
-    // dP - D; with dropout the keep bit scales dP but not D, and the chain starts from zero.
-    constexpr bool FOLD_D = !DROP;
     auto qtile = [&](int b) -> T* { return sBuf[b]; };
     auto dtile = [&](int b) -> T* { return sBuf[b] + TILEQ; };
 
@@ -268,7 +296,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         f32x4 stC[4][2];       // statistics of the softmax rows of the step
         f32x16 sC = zero16();  // S and dP consumed by this step's softmax gradient
         f32x16 pC = zero16();
-        f32x16 dX = zero16();  // start of this step's dP chain (-D of its X rows, or zero)
         vec pkY[2];            // packed P and dS consumed by this step's Y (two 16-row halves)
         vec dsY[2];
         uint32_t dbC[16];      // dropout mask bytes and bit base of the softmax rows
@@ -299,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             const int lo_h = lo_base - (t * BQ + 32 * wh.sm);
             f32x16 sN = zero16();
             f32x16 pN = zero16();
-            f32x16 dXn = zero16();
+            f32x16 dX = zero16();  // start of this step's dP chain (-D of its X rows, or zero)
             uint32_t pkw[2][4];
             uint32_t dsw[2][4];
             vec nopr[LA];
@@ -406,6 +433,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 }
                 // ---- LDS reads for slot k + LA (of the next step near the end)
                 constexpr int kr = k + LA;
+                if constexpr (HX && kr == KD) read_dinit(wh, dX);
                 if constexpr (kr < NOPS) {
                     if constexpr ((kr % 2 == 0 && HX) || (kr % 2 == 1 && HY)) opr[kr] = read_op(wh, IC<kr>{});
                     // statistics of elements 4g .. 4g + 3, LA slots before the first of them (group 0
@@ -416,10 +444,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     });
                 } else if constexpr (KIND != kStepLast) {
                     nopr[kr - NOPS] = read_op(nw, IC<kr - NOPS>{});
-                    if constexpr (kr == NOPS && (NKIND == kStepA || NKIND == kStepB)) {
-                        read_stats(nw, 0, stN);
-                        read_dinit(nw, dXn);
-                    }
+                    if constexpr (kr == NOPS && (NKIND == kStepA || NKIND == kStepB)) read_stats(nw, 0, stN);
                 }
                 // ---- dropout mask byte of X element k
                 if constexpr (DROP && HX && k < 16) {
@@ -468,7 +493,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 if constexpr (NKIND == kStepA || NKIND == kStepB) {
                     stC[0][0] = stN[0];
                     stC[0][1] = stN[1];
-                    dX = dXn;
                 }
             }
         };
@@ -527,7 +551,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 static_for<0, LA>([&](auto kc) {
                     if constexpr (decltype(kc)::value % 2 == 0) opr[decltype(kc)::value] = read_op(w0, kc);
                 });
-                read_dinit(w0, dX);
             }
             step(IC<kStepFirst>{}, IC<kStepA>{}, IC<0>{}, tb, 0, 0);
             int b = 0;
