@@ -115,11 +115,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     // Without dropout the dP chain of a step starts from -D of its rows, so that it ends with
     // dP - D; with dropout the keep bit scales dP but not D, and the chain starts from zero.
     constexpr bool FOLD_D = !DROP;
-    // X slots: S (chain A) and dP (chain B); S leads by two so that the start of the dP chain
+    // X slots: S (chain A) and dP (chain B); S leads by LA / 2 so that the start of the dP chain
     // (-D of the step's rows) can be read from LDS LA slots ahead, within the step
     // (with dropout the chain starts at zero and the plain alternation is kept)
-    using XS = std::conditional_t<FOLD_D, LeadInterleave<SK, SV, 2>, Interleave<SK, SV>>;
-    constexpr int KD = FOLD_D ? 2 * LeadInterleave<SK, SV, 2>::first_b() : LA;  // slot of the first dP MFMA
+    using XL = LeadInterleave<SK, SV, LA / 2>;
+    using XS = std::conditional_t<FOLD_D, XL, Interleave<SK, SV>>;
+    constexpr int KD = FOLD_D ? 2 * XL::first_b() : LA;  // slot of the first dP MFMA
     using YS = Interleave<SV, SK>;        // Y slots: dV (chain A) and dK (chain B)
     static_assert(BQ == 64 && BKV == 32 * NW && (TILED / 8 / 64) % NW == 0 && NOPS >= 16 && LA % 2 == 0 &&
                   LA < NOPS && DV <= DK && KD >= LA, "tile shape");
