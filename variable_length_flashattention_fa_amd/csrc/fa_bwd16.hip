@@ -107,11 +107,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     constexpr int NX = SK + SV;           // X MFMAs per step (as many Y MFMAs)
     constexpr int NOPS = 2 * NX;          // slots per step: X and Y MFMAs alternate
     constexpr int LA = 4;                 // LDS reads run LA slots ahead of their MFMA
-    constexpr int NB = 3;                 // query tile buffers
+    // Query tile buffers.  With four, the copy of a tile has two tile periods to land before the
+    // barrier that waits for it.  With dropout or an explicit mask, byte loads interleave with the
+    // tile copies in the load counter, so those kernels keep three buffers and wait for all loads.
+    constexpr int NB = DROP || XM ? 3 : 4;
     constexpr int TILEQ = BQ * DK;
     constexpr int TILED = BQ * DV;
     constexpr int TWQ = TILEQ / 8 / 64 / NW;  // DMA instructions per wave and Q tile
     constexpr int TWD = TILED / 8 / 64 / NW;  // ... and dY tile
+    static_assert(TWQ + TWD < 16, "load counter");
     // Without dropout the dP chain of a step starts from -D of its rows, so that it ends with
     // dP - D; with dropout the keep bit scales dP but not D, and the chain starts from zero.
     constexpr bool FOLD_D = !DROP;
@@ -225,14 +229,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             const i32x4 rd = buffer_desc(gdy + static_cast<int64_t>(q0) * p.dy_st, tile_bytes(L - q0, BQ, p.dy_st));
             const uint32_t mq = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(qtile(b) + w * TWQ * 512)));
             const uint32_t md = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(dtile(b) + w * TWD * 512)));
-            dma_pair<TWQ, TWD>(__builtin_amdgcn_readfirstlane(mq), rq, qoff, __builtin_amdgcn_readfirstlane(md), rd,
-                               dyoff);
+            // statistics first: the last TWQ + TWD loads a wave issues for a tile are its Q / dY copies
             if (w == NW - 1 && lane < BQ / 4) {
                 // rows past the sequence read as zero
                 const uint32_t nbytes = q0 < L ? static_cast<uint32_t>(min(L - q0, BQ) * 4) : 0u;
                 dma16_async(sSt[b][0], buffer_desc(gstat + q0, nbytes), lane * 16);
                 dma16_async(sSt[b][1], buffer_desc(gstat + plane + q0, nbytes), lane * 16);
             }
+            dma_pair<TWQ, TWD>(__builtin_amdgcn_readfirstlane(mq), rq, qoff, __builtin_amdgcn_readfirstlane(md), rd,
+                               dyoff);
         };
 
         // where a step reads: X rows 32*xm.. of buffer xb, softmax statistics of rows 32*sm..
@@ -426,11 +431,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     }
                 });
                 // ---- tile barrier: tile t + 1 has landed and every wave is done with the buffer
-                // of tile t - 1, which then receives tile t + 2
+                // of tile t - 1, which then receives tile t + NB - 1 (with four buffers, tile t + 2
+                // may still be in flight)
                 if constexpr (KIND == kStepA && k == NOPS - LA) {
-                    wait_dma();
+                    if constexpr (NB == 4) {
+                        if (t + 2 < te) {
+                            wait_dma_but<TWQ + TWD>();
+                        } else {
+                            wait_dma();
+                        }
+                    } else {
+                        wait_dma();
+                    }
                     __syncthreads();
-                    if (t + 2 < te) issue(t + 2, wh.yb);
+                    if (t + NB - 1 < te) issue(t + NB - 1, wh.yb);
                 }
                 // ---- LDS reads for slot k + LA (of the next step near the end)
                 constexpr int kr = k + LA;
@@ -540,11 +554,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     dsY[i] = vec{};
                 }
             }
-            // prologue: tiles tb and tb + 1 in flight, zeros in the third buffer (read by the Y of
-            // the step before the first, whose packed P / dS are zero)
-            issue(tb, 0);
-            if (tb + 1 < te) issue(tb + 1, 1);
-            for (int i = threadIdx.x; i < (TILEQ + TILED) / 8; i += 64 * NW) reinterpret_cast<vec*>(sBuf[2])[i] = vec{};
+            // prologue: tiles tb .. tb + NB - 2 in flight, zeros in the last buffer (read by the Y
+            // of the step before the first, whose packed P / dS are zero)
+#pragma unroll
+            for (int i = 0; i < NB - 1; ++i)
+                if (tb + i < te) issue(tb + i, i);
+            for (int i = threadIdx.x; i < (TILEQ + TILED) / 8; i += 64 * NW)
+                reinterpret_cast<vec*>(sBuf[NB - 1])[i] = vec{};
             wait_dma();
             __syncthreads();
             {

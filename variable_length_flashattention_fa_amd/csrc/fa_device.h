@@ -83,6 +83,13 @@ __device__ __forceinline__ void dma_stats32(float2* dst, const float2* g, int va
 }
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// vmcnt(N): all but the N most recently issued vector-memory loads have completed (loads
+// complete in issue order for this count)
+template <int N>
+__device__ __forceinline__ void wait_dma_but() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
 
 // The same 16-byte-per-lane HBM -> LDS copy issued from inline assembly: the compiler then
 // does not track the LDS write, so it adds no wait between the copy of the next tile and the
