@@ -103,15 +103,14 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
     constexpr int VEC = 16 / sizeof(T);
     constexpr int TPR = D / VEC;    // threads per (token, head) row of dY and Y (D = V's head dim)
     constexpr int RPB = 256 / TPR;
+    // one head per grid row, consecutive tokens per block: the statistics reads and the plane
+    // writes of a block are contiguous
     const int sub = threadIdx.x % TPR;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
-    const bool valid = r < tq * heads;
+    const int n = blockIdx.y;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
+    const bool valid = t < tq;
     float part = 0.f;
-    int64_t t = 0;
-    int n = 0;
     if (valid) {
-        t = r / heads;
-        n = static_cast<int>(r - t * heads);
         const Chunk<T> a = *reinterpret_cast<const Chunk<T>*>(dy + t * dy_st + n * dy_sh + sub * VEC);
         const Chunk<T> b = *reinterpret_cast<const Chunk<T>*>(y + t * y_st + n * y_sh + sub * VEC);
 #pragma unroll
@@ -462,9 +461,8 @@ static hipError_t preprocess_t(TensorArg dy, TensorArg y, const float* smax, con
                                int64_t tq, int64_t heads, hipStream_t stream) {
     constexpr int TPR = D / (16 / sizeof(T));
     constexpr int RPB = 256 / TPR;
-    const int64_t rows = tq * heads;
-    const int64_t blocks = (rows + RPB - 1) / RPB;
-    preprocess_kernel<T, D><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+    const int64_t blocks = (tq + RPB - 1) / RPB;
+    preprocess_kernel<T, D><<<dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(heads)), dim3(256), 0, stream>>>(
         static_cast<const T*>(dy.data), dy.stride_t, dy.stride_h, static_cast<const T*>(y.data), y.stride_t,
         y.stride_h, smax, ssum, rowstat, tq, static_cast<int>(heads));
     return hipGetLastError();
