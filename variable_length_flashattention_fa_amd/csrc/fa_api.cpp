@@ -427,10 +427,6 @@ extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
 
     fa::TensorArg tdy{dy->data, dy->stride_t, dy->stride_h};
     fa::TensorArg ty{y->data, y->stride_t, y->stride_h};
-    e = timed(0, s, [&] {
-        return fa::launch_preprocess(dtype, dv_dim, tdy, ty, softmax_max, softmax_sum, ws.rowstat, tq, heads, s);
-    });
-    if (e != hipSuccess) return runtime_error("preprocess launch", e);
 
     const float exp_scale = static_cast<float>(scale * 1.4426950408889634);
     const float inv_keep = static_cast<float>(1.0 / keep_prob);
@@ -458,6 +454,11 @@ extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
         a.dv_st = dv->stride_t;
         a.dv_sh = dv->stride_h;
         a.rowstat = ws.rowstat;
+        a.y = y->data;
+        a.y_st = y->stride_t;
+        a.y_sh = y->stride_h;
+        a.softmax_max = softmax_max;
+        a.softmax_sum = softmax_sum;
         a.items_kv = ws.items;
         a.items_q = ws.items + ws.n_items;
         a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
@@ -480,12 +481,19 @@ extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
         a.scale = static_cast<float>(scale);
         fa::set_mask(a, atten_mask);
         const bool xm = atten_mask != nullptr;
-        e = timed(1, s, [&] { return fa::launch_dkdv16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, ws.n_items, s); });
-        if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
+        // the dQ kernel also writes the row statistics planes (no separate row pass on this path);
+        // the dK/dV kernel reads them, so it runs second
         e = timed(3, s, [&] { return fa::launch_dq16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, ws.n_q_items, s); });
         if (e != hipSuccess) return runtime_error("dQ kernel launch", e);
+        e = timed(1, s, [&] { return fa::launch_dkdv16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, ws.n_items, s); });
+        if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
         return FA_OK;
     }
+
+    e = timed(0, s, [&] {
+        return fa::launch_preprocess(dtype, dv_dim, tdy, ty, softmax_max, softmax_sum, ws.rowstat, tq, heads, s);
+    });
+    if (e != hipSuccess) return runtime_error("preprocess launch", e);
 
     fa::MainArgs a;
     a.q = {q->data, q->stride_t, q->stride_h};

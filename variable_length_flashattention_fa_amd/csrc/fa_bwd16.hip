@@ -690,14 +690,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         const int64_t row = it.q_start + (ok ? qi : 0);
         const vec* qr = reinterpret_cast<const vec*>(static_cast<const T*>(p.q) + row * p.q_st + n * p.q_sh);
         const vec* dr = reinterpret_cast<const vec*>(static_cast<const T*>(p.dy) + row * p.dy_st + n * p.dy_sh);
+        const vec* yr = reinterpret_cast<const vec*>(static_cast<const T*>(p.y) + row * p.y_st + n * p.y_sh);
+        vec yreg[SV];
 #pragma unroll
         for (int s = 0; s < SK; ++s) qreg[s] = ok ? qr[2 * s + h] : vec{};
 #pragma unroll
-        for (int s = 0; s < SV; ++s) dyreg[s] = ok ? dr[2 * s + h] : vec{};
+        for (int s = 0; s < SV; ++s) {
+            dyreg[s] = ok ? dr[2 * s + h] : vec{};
+            yreg[s] = ok ? yr[2 * s + h] : vec{};
+        }
+        // The row pass of the backward, done here for the workgroup's queries: D = sum over V's
+        // head dim of dY * Y in fp32 (each lane half holds every other 8-element chunk of the
+        // row) and beta = max * log2(e) + log2(sum) from element 0 of the forward statistics.
+        // Written to the row statistics planes, which the dK/dV kernel reads afterwards.
+        float part = 0.f;
+#pragma unroll
+        for (int s = 0; s < SV; ++s) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += static_cast<float>(dyreg[s][e]) * static_cast<float>(yreg[s][e]);
+        }
+        part += __shfl_xor(part, 32);
+        ndelta = -part;
         if (ok) {
-            const int64_t o = static_cast<int64_t>(n) * p.tq + it.q_start + qi;
-            ndelta = p.rowstat[o];
-            beta = p.rowstat[static_cast<int64_t>(p.heads) * p.tq + o];
+            const int64_t o = static_cast<int64_t>(n) * p.tq + row;
+            beta = p.softmax_max[8 * o] * 1.4426950408889634f + __builtin_amdgcn_logf(p.softmax_sum[8 * o]);
+            if (h == 0) {
+                p.rowstat[o] = ndelta;
+                p.rowstat[static_cast<int64_t>(p.heads) * p.tq + o] = beta;
+            }
         }
     }
     // keys this lane's query admits, [klo, khi]; element a of a step starting at key k0s

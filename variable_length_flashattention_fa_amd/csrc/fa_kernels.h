@@ -95,7 +95,13 @@ struct Bwd16Args {
     void* dk;
     void* dv;
     int64_t dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh;
-    const float* rowstat;  // planes of -D and beta (see launch_preprocess)
+    // planes of -D and beta (layout as in launch_preprocess): written by the dQ kernel, which computes
+    // them for its rows from dY, Y and the forward statistics, and read by the dK/dV kernel after it
+    float* rowstat;
+    const void* y;
+    int64_t y_st, y_sh;
+    const float* softmax_max;  // [heads, tq, 8]; element 0 of each row is read
+    const float* softmax_sum;
     const fa_work_item_t* items_kv;  // key-block items (FA16_DKDV_BLOCK keys, FA16_DKDV_TILE_Q tiles)
     const fa_work_item_t* items_q;   // query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles)
     const uint8_t* drop_mask;
@@ -106,6 +112,7 @@ struct Bwd16Args {
 };
 
 // dK/dV kernel over n_items key-block items x key/value heads (each sums its group of query heads).
+// Reads the row statistics planes, so it runs after the dQ kernel.
 // Head dims (Q/K, V): (128, 128), (128, 64) or (64, 64).
 hipError_t launch_dkdv16(int32_t dtype, int head_dim_k, int head_dim_v, bool dropout, bool xmask,
                          const Bwd16Args& a, int64_t n_items, hipStream_t stream);
