@@ -67,7 +67,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     for (int u = 0; u < TWK; ++u) koff[u] = dma_offset<DK>(w * TWK + u, lane, p.k_st) - 1024 * u;
 #pragma unroll
     for (int u = 0; u < TWV; ++u) voff[u] = dma_offset<DV>(w * TWV + u, lane, p.v_st) - 1024 * u;
-    auto issue = [&](int kt, int b) {
+    auto issue = [&](int kt, int b) __attribute__((always_inline)) {
         const int k0 = kt * BK;
         const i32x4 rk = buffer_desc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st));
         const i32x4 rv = buffer_desc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st));
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     float mref = -INFINITY;   // the max the P values and O^T are relative to
     float lsum = 0.f;         // sum of P over this lane's keys (relative to mref)
 
-    auto kstep = [&](const T* cK, const T* cV, int k0s) {
+    auto kstep = [&](const T* cK, const T* cV, int k0s) __attribute__((always_inline)) {
         // explicit mask bytes of keys k0s + 4h + cc(a), issued before the product that hides them
         uint32_t mk[16];
         if constexpr (XM) {
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         }
         const bool full = !XM && wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
         float x[16];
-        auto scores = [&](auto masked_tag) {
+        auto scores = [&](auto masked_tag) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked_tag)::value;
             const int lo_h = kbase - k0s;
 #pragma unroll
@@ -246,16 +246,23 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         }
     };
 
-    if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
-    int b = 0;
-    for (int kt = it.tile_begin; kt < it.tile_end; ++kt) {
+    // one key tile in buffer B (a constant, so that every LDS address of the tile is a fixed
+    // offset from the lane's own)
+    auto tile = [&](int kt, auto bc) __attribute__((always_inline)) {
+        constexpr int B = decltype(bc)::value;
         wait_dma();
-        __syncthreads();
-        if (kt + 1 < it.tile_end) issue(kt + 1, b ^ 1);
-        kstep(sK[b], sV[b], kt * BK);
-        kstep(sK[b] + 32 * DK, sV[b] + 32 * DV, kt * BK + 32);
-        b ^= 1;
+        __syncthreads();  // tile kt is in buffer B; every wave is done with buffer B ^ 1
+        if (kt + 1 < it.tile_end) issue(kt + 1, B ^ 1);
+        kstep(sK[B], sV[B], kt * BK);
+        kstep(sK[B] + 32 * DK, sV[B] + 32 * DV, kt * BK + 32);
+    };
+    if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
+    int kt = it.tile_begin;
+    for (; kt + 1 < it.tile_end; kt += 2) {
+        tile(kt, IC<0>{});
+        tile(kt + 1, IC<1>{});
     }
+    if (kt < it.tile_end) tile(kt, IC<0>{});
 
     // epilogue: the two lane halves' sums; Y = O / l; statistics in natural units
     const float ltot = lsum + __shfl_xor(lsum, 32);
