@@ -67,27 +67,60 @@ def test_checker_flags_a_planted_hazard():
     assert len(_hazards(text)) == 1
 
 
-@pytest.mark.slow
-def test_no_valu_to_asm_mfma_hazard(tmp_path):
-    hipcc = os.environ.get("HIPCC") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc"))
+def _hipcc():
+    return os.environ.get("HIPCC") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc")
+                                       else shutil.which("hipcc"))
+
+
+@pytest.fixture(scope="module")
+def kernel_asm(tmp_path_factory):
+    """Assembly of every 16-bit kernel part, compiled with the library's flags: {(source, part): text}."""
+    hipcc = _hipcc()
     if not hipcc:
         pytest.skip("hipcc not available")
-    # the asm MFMAs live in the dK/dV kernels: compile parts 1 (bf16) and 2 (fp16) side by side
     import concurrent.futures as cf
+    tmp = tmp_path_factory.mktemp("asm")
+    parts = [("fa_bwd16.hip", "FA_BWD16_PART", i) for i in (1, 2, 3, 4)] + [("fa_fwd.hip", "FA_FWD_PART", i) for i in (1, 2)]
 
-    def compile_part(part):
-        out = tmp_path / f"bwd16_p{part}.s"
+    def compile_part(job):
+        src, macro, part = job
+        out = tmp / f"{src}.{part}.s"
         cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
                "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-               "-mllvm", "-amdgpu-mfma-vgpr-form", f"-DFA_BWD16_PART={part}", "--cuda-device-only", "-S",
-               "-o", str(out), os.path.join(CSRC, "fa_bwd16.hip")]
+               "-mllvm", "-amdgpu-mfma-vgpr-form", f"-D{macro}={part}", "--cuda-device-only", "-S",
+               "-o", str(out), os.path.join(CSRC, src)]
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
         assert r.returncode == 0, r.stdout[-2000:]
         return out.read_text()
 
-    with cf.ThreadPoolExecutor(max_workers=2) as ex:
-        texts = list(ex.map(compile_part, (1, 2)))
+    with cf.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        texts = list(ex.map(compile_part, parts))
+    return {(src, part): t for (src, _, part), t in zip(parts, texts)}
+
+
+@pytest.mark.slow
+def test_no_valu_to_asm_mfma_hazard(kernel_asm):
+    # the asm MFMAs live in the dK/dV kernels: parts 1 (bf16) and 2 (fp16)
+    texts = [kernel_asm[("fa_bwd16.hip", 1)], kernel_asm[("fa_bwd16.hip", 2)]]
     assert "v_mfma_f32_32x32x16_bf16 a[" in texts[0]  # the asm MFMAs are there
     assert "v_mfma_f32_32x32x16_f16 a[" in texts[1]
     for text in texts:
         assert _hazards(text) == []
+
+
+@pytest.mark.slow
+def test_no_register_spills_or_scratch(kernel_asm):
+    """Every backward and forward kernel of these parts fits its vector registers: no VGPR spills and no
+    private (scratch) segment, so no scratch memory traffic anywhere.  Scalar registers may spill
+    into VGPR lanes (v_writelane / v_readlane, no memory); those sit outside the tile loops."""
+    checked = 0
+    for text in kernel_asm.values():
+        names = re.findall(r"^\s+\.name:\s+(_ZN2fa\w+)$", text, re.M)
+        vspills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)
+        private = re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)
+        assert names and len(vspills) == len(names) and len(private) == len(names), "metadata layout changed"
+        assert [n for n, x in zip(names, vspills) if int(x)] == []
+        assert [n for n, x in zip(names, private) if int(x)] == []
+        checked += len(names)
+    # 4 backward parts x 12 instances; forward part 1 (bf16) 12, part 2 (fp16) 12 plus 6 fp32 forward instances
+    assert checked == 78
