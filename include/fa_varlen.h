@@ -228,8 +228,9 @@ int64_t fa_varlen_worklist(const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t*
 /*
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
  * fa_varlen_bwd / fa_varlen_fwd call records a pair of HIP events around each
- * of its kernels on the call's stream: index 0 the row preprocess, 1 the dK/dV
- * kernel, 2 (unused), 3 the dQ kernel, 4 the forward.
+ * of its kernels on the call's stream: index 0 the separate row pass (fp32 inputs
+ * only; for bf16 / fp16 the dQ kernel does it), 1 the dK/dV kernel, 2 (unused),
+ * 3 the dQ kernel, 4 the forward.
  */
 void fa_profile_enable(int on);
 
