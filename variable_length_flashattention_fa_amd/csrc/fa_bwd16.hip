@@ -762,6 +762,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) pinit[i] = FOLD_D ? ndelta : 0.f;
 
+    // bit offset of this lane's query row from the wave's first row in the dropout stream
+    const uint32_t drow = static_cast<uint32_t>(col) * static_cast<uint32_t>(K);
+
     // explicit mask block of this (sequence, head); this lane reads row qi
     __amdgpu_buffer_rsrc_t mrs;
     if constexpr (XM) {
@@ -772,14 +775,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     // one 32-key step (keys k0s .. k0s + 31, rows 32 kh of the tile in cK / cV)
     auto kstep = [&](const T* cK, const T* cV, int k0s) __attribute__((always_inline)) {
         // explicit mask bytes of keys k0s + 4h + cc(a), issued before the products that hide them
+        // (with dropout as well: after them, like the dropout window, to stay within the registers)
         uint32_t mk[16];
-        if constexpr (XM) {
+        auto load_mask_bytes = [&]() __attribute__((always_inline)) {
             const uint32_t mrow = static_cast<uint32_t>(qi) * static_cast<uint32_t>(p.mask.am_sq) +
                                   static_cast<uint32_t>(k0s + 4 * h);
 #pragma unroll
             for (int a = 0; a < 16; ++a)
                 mk[a] = __builtin_amdgcn_raw_buffer_load_b8(mrs, mrow + 8 * (a >> 2) + (a & 3), 0, 0);
-        }
+        };
+        if constexpr (XM && !DROP) load_mask_bytes();
+        // dropout bits of keys k0s .. k0s + 31 of this lane's query: contiguous in the bit stream, so
+        // five byte loads and one funnel shift give them as a 32-bit window (bit t = key k0s + t).
+        // The buffer starts at the byte that holds the bit of (wave's first query, key k0s), so
+        // lane offsets stay small; bytes past the end of the mask read as zero.  Issued before the
+        // products that hide their latency -- except with an explicit mask as well, whose 16 byte
+        // registers are live there too: then after them, which keeps the kernel within its registers.
+        uint32_t win = 0;
+        auto load_window = [&]() __attribute__((always_inline)) {
+            const int64_t b0 = it.drop_base + (static_cast<int64_t>(n) * L + i0) * K + k0s;
+            const int64_t byte0 = b0 >> 3;
+            const int64_t left = p.drop_bytes - byte0;
+            const __amdgpu_buffer_rsrc_t drs = raw_rsrc(
+                p.drop_mask + byte0, left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left)));
+            const uint32_t lb = static_cast<uint32_t>(b0 & 7) + drow;
+            const uint32_t byte = lb >> 3;
+            uint32_t lo = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lo |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(drs, byte + i, 0, 0)) << (8 * i);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b8(drs, byte + 4, 0, 0);
+            win = __builtin_amdgcn_alignbit(hi, lo, lb & 7);
+        };
+        if constexpr (DROP && !XM) load_window();
         f32x16 accS = zero16();
         f32x16 accP = pinit;
 #pragma unroll
@@ -791,6 +819,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         }
 #pragma unroll
         for (int s = SV; s < SK; ++s) accS = Op16<T>::mfma(lds_row<vec>(cK, loK.row[s]), qreg[s], accS);
+        if constexpr (DROP && XM) {
+            load_mask_bytes();
+            load_window();
+        }
         // dS^T = Ps (dP Z/kp - D); element (key k0s + 4h + cc(a), query qi)
         const bool full = !XM && wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
         uint32_t dsw[2][4];
@@ -810,12 +842,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
                         pv = adm ? pv : 0.f;
                     }
                     if constexpr (DROP) {
-                        float zk = 0.f;
-                        if (pv != 0.f) {
-                            const int64_t bit =
-                                it.drop_base + (static_cast<int64_t>(n) * L + qi) * K + k0s + cc + 4 * h;
-                            zk = ((p.drop_mask[bit >> 3] >> (bit & 7)) & 1) ? p.inv_keep : 0.f;
-                        }
+                        const float zk = __builtin_amdgcn_ubfe(win, cc + 4 * h, 1) != 0 ? p.inv_keep : 0.f;
                         ds[e] = pv * fmaf(accP[a + e], zk, ndelta);
                     } else {
                         ds[e] = pv * accP[a + e];  // accP already holds dP - D
