@@ -85,7 +85,7 @@ std::mutex g_mutex;
 std::unordered_map<int, Workspace> g_ws;
 
 // ---- optional per-kernel event timing ----
-constexpr int kKernels = 5;  // 0 preprocess, 1 dK/dV, 2 (unused), 3 dQ, 4 forward
+constexpr int kKernels = 5;  // 0 row pass (fp32 path), 1 dK/dV, 2 (unused), 3 dQ, 4 forward
 struct EventPair {
     int kernel;
     hipEvent_t start;

@@ -4,17 +4,18 @@
 // dQ = scale dS K, dK = scale dS^T Q, with dP = dY V^T and
 // dS = Ps o (dP o Z/kp - D), D_i = sum_d dY_i,d Y_i,d; Ps is rebuilt from the
 // forward row statistics as exp2(S * scale * log2 e - beta_i) with
-// beta_i = max_i * log2 e + log2(sum_i) (computed by the row preprocess).
+// beta_i = max_i * log2 e + log2(sum_i).
 //
-// Two kernels; each wave owns 32 rows of the resident block:
+// Two kernels, launched dq first; each wave owns 32 rows of the resident block:
 //   dkdv: 4 waves (one per SIMD), one workgroup per (block of 128 keys, key/value head).
 //         Each wave keeps its keys' K and V rows and dK / dV accumulators in registers,
 //         and walks, for every query head that reads the key/value head, the 64-row
 //         query tiles that can see the block:
 //           S = Q K^T, dP = dY V^T        (A from the Q / dY tile, B from K / V regs)
 //           dV += Pd^T dY, dK += dS^T Q   (A straight from the S / dP accumulators)
-//   dq:   8 waves (two per SIMD), one workgroup per (block of 256 queries, head).  Each wave keeps its
-//         queries' Q and dY rows, row statistics and dQ^T accumulator in
+//   dq:   8 waves (two per SIMD), one workgroup per (block of 256 queries, head).  Its prologue
+//         computes D and beta of its queries (the row pass) and writes them for the dkdv kernel.
+//         Each wave keeps its queries' Q and dY rows, row statistics and dQ^T accumulator in
 //         registers, and walks the 32-row key tiles they can see:
 //           S^T = K Q^T, dP^T = V dY^T    (A from the K / V tile, B from Q / dY regs)
 //           dQ^T += K^T dS^T              (B straight from the dP^T accumulator)
@@ -41,9 +42,9 @@ namespace fa {
 // so that the exponentials and the dS arithmetic of one step run under the matrix products of
 // its neighbours (one wave per SIMD: nothing else would fill the gaps).  dK and dV accumulate
 // in the accumulation registers through MFMAs written in assembly; S and dP use ordinary
-// VGPRs, where the VALU reads them.  Query tiles rotate through three LDS buffers: while tiles
-// t and t + 1 are read, tile t + 2 is copied in; one barrier per tile, between its two steps,
-// hands the buffer of tile t - 1 back.
+// VGPRs, where the VALU reads them.  Query tiles rotate through four LDS buffers (three with
+// dropout or an explicit mask): while tiles t and t + 1 are read, tiles t + 2 (and t + 3) are
+// copied in; one barrier per tile, between its two steps, hands the buffer of tile t - 1 back.
 
 // Kinds of pipeline step.  For the tile in buffer b (tile t):
 //   A: X = rows 32.. of tile t (buffer b), softmax = rows 0.. of tile t, Y = rows 32.. of tile

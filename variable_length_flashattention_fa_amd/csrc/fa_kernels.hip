@@ -1,5 +1,5 @@
-// gfx950 (CDNA4) kernels of the varlen attention backward: the row preprocess (all dtypes) and
-// the fp32 path.
+// gfx950 (CDNA4) kernels of the varlen attention backward for fp32 inputs: the row pass
+// (preprocess) and the dK/dV and dQ kernels.  (For bf16 / fp16 the dQ kernel does the row pass.)
 //
 // The backward follows the formulas section of the "FlashAttention梯度V2" page
 // (dV = P^T dY, dQ = scale dS K, dK = scale dS^T Q) with the softmax Jacobian
