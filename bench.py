@@ -15,6 +15,11 @@ Also reported:
                 average duration (HIP events on the launch stream, recorded by
                 the library during the timed steps) against the bf16 MFMA peak;
   kernels       the same figure for every kernel (GB/s for the HBM-bound ones);
+  cold_layout   calls whose sequence layout is new to the library (work lists
+                built and uploaded in the call), device and host time per call;
+  workloads     (default run) ms per call and useful TFLOP/s of the other 16-bit
+                workloads: 2 (bf16 causal, 16 sequences), 4 (bf16 band 2048/0,
+                8 x 8192), 5 (fp16 causal with dropout, 32 sequences);
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
                 same workload (a few (sequence, head) units), as a baseline.
 """
@@ -163,6 +168,105 @@ def cpu_baseline(inp, y_host, smax_h, ssum_h, wl, units_wanted: int):
     }
 
 
+def cold_layout_calls(B, q, k, v, dy, y, smax, ssum, inp, wl, drop, dq, dk, dv, stream, count: int = 8) -> dict:
+    """Calls whose sequence layout the library has not seen: the first two sequences' boundary
+    moves by 1..count tokens (same tensors, same total), so each call builds its work lists and
+    uploads them.  Reports device time per call (HIP events), host time per call, and the host
+    time of the same number of calls with a cached layout."""
+    import numpy as np
+    import torch
+
+    lens = np.diff(inp.cu_q)
+    if len(lens) < 2 or wl.keep_prob < 1.0:
+        return None
+    layouts = []
+    for i in range(1, count + 1):
+        l2 = lens.copy()
+        l2[0] += i
+        l2[1] -= i
+        layouts.append(np.concatenate([[0], np.cumsum(l2)]).astype(np.int64))
+
+    def call(cu):
+        B.fa_varlen_bwd(q, k, v, dy, y, smax, ssum, cu, cu, wl.mode, wl.pre, wl.nxt, wl.keep_prob, drop, wl.scale,
+                        wl.heads, dq, dk, dv, stream=stream)
+
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    host = 0.0
+    ev[0].record(stream)
+    for cu in layouts:
+        t0 = time.perf_counter()
+        call(cu)
+        host += time.perf_counter() - t0
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    cold_ms = ev[0].elapsed_time(ev[1]) / count
+    host_cached = 0.0
+    for _ in range(count):
+        t0 = time.perf_counter()
+        call(inp.cu_q)
+        host_cached += time.perf_counter() - t0
+    torch.cuda.synchronize()
+    return {"ms_per_call": cold_ms, "host_us_per_call": host / count * 1e6,
+            "cached_host_us_per_call": host_cached / count * 1e6, "calls": count,
+            "note": "each call has a sequence layout not seen before (the boundary of the first two sequences "
+                    "moves by 1..calls tokens): its work lists are built and uploaded asynchronously"}
+
+
+def other_workload(number: int, steps: int, warmup: int) -> dict:
+    """ms per call and useful TFLOP/s of another workload, timed like the headline one."""
+    import torch
+
+    from variable_length_flashattention_fa_amd import binding as B
+    from variable_length_flashattention_fa_amd import synth
+    from variable_length_flashattention_fa_amd.inputs_forward import forward_stats, pair_count
+
+    wl = synth.workload(number)
+    t0 = time.time()
+    log(f"workload {number}: {wl.name}; drawing inputs")
+    inp = synth.make(wl)
+    dev = torch.device("cuda:0")
+    q, k, v, dy = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.dy))
+    drop = torch.from_numpy(inp.drop_mask).to(dev) if inp.drop_mask is not None else None
+    y, smax, ssum = forward_stats(q, k, v, inp.cu_q, inp.cu_kv, mode=wl.mode, pre=wl.pre, nxt=wl.nxt,
+                                  keep_prob=wl.keep_prob, drop_mask=drop, scale=wl.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        B.fa_varlen_bwd(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt, wl.keep_prob,
+                        drop, wl.scale, wl.heads, dq, dk, dv, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    B.profile_read()
+    B.profile_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    B.profile_enable(False)
+    prof = B.profile_read()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    pairs = pair_count(inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt)
+    tflops = 10.0 * wl.heads * wl.head_dim * pairs / (ms * 1e-3) / 1e12
+    kernels = {name: ms_ / max(n, 1) for name, (ms_, n) in prof.items() if n}
+    log(f"workload {number}: {ms:.3f} ms/call, {tflops:.0f} useful TFLOP/s ({time.time() - t0:.1f}s)")
+    del q, k, v, dy, y, smax, ssum, dq, dk, dv, drop
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "ms_per_call": ms, "useful_TFLOP/s": tflops,
+            "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "dtype": wl.dtype, "steps": steps,
+            "kernel_avg_ms": {("bwd_dkdv16_kernel" if k_ == "bwd_main" else "bwd_dq16_kernel" if k_ == "bwd_dq"
+                               else k_): v_ for k_, v_ in kernels.items()},
+            "config": {"sequences": len(wl.lengths), "tokens": wl.tokens, "heads": wl.heads,
+                       "head_dim": wl.head_dim, "mask": ["none", "causal", "band"][wl.mode],
+                       "pre_tokens": wl.pre, "next_tokens": wl.nxt, "keep_prob": wl.keep_prob,
+                       "admitted_pairs_per_head": pairs}}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +275,8 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (default 3)")
     ap.add_argument("--cpu-units", type=int, default=16, help="(sequence, head) units for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the other 16-bit workloads (2, 4, 5) reported under 'workloads'")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="copy this many MiB device-to-device once before the timed steps, with the runtime's "
                          "blit kernel and with an elementwise kernel (plain copies of known size, for "
@@ -269,8 +375,6 @@ def main(argv=None):
     B.profile_enable(False)
     fwd_prof = B.profile_read()
     log(f"forward: {fwd_ms:.3f} ms/call")
-    measured_peak = {w: B.mfma_peak(w) for w in (1, 2)}
-    log(f"measured bf16 MFMA rate: {measured_peak[1]:.0f} TFLOP/s (1 wave/SIMD), {measured_peak[2]:.0f} (2 waves/SIMD)")
 
     pairs = pair_count(inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt)
     useful = 10.0 * wl.heads * wl.head_dim * pairs
@@ -301,9 +405,6 @@ def main(argv=None):
     dominant = max((k for k in kernels if "TFLOP/s" in kernels[k]), key=lambda k: kernels[k]["avg_ms"])
     achieved = kernels[dominant]["TFLOP/s"]
     main_avg = kernels[dominant]["avg_ms"]
-    if q.dtype != torch.float32:
-        kernels["bwd_dkdv16_kernel"]["frac_of_measured_peak"] = kernels["bwd_dkdv16_kernel"]["TFLOP/s"] / max(measured_peak.values())
-        kernels["bwd_dq16_kernel"]["frac_of_measured_peak"] = kernels["bwd_dq16_kernel"]["TFLOP/s"] / max(measured_peak.values())
 
     dtype_name = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[q.dtype]
     out = {
@@ -324,9 +425,6 @@ def main(argv=None):
                    "next_tokens": wl.nxt, "keep_prob": wl.keep_prob, "admitted_pairs_per_head": pairs},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "max": call_ms[-1]},
-        "measured_mfma_peak": {"tflops_1_wave_per_simd": measured_peak[1], "tflops_2_waves_per_simd": measured_peak[2],
-                               "frac_of_measured": value / max(measured_peak.values()),
-                               "dominant_kernel_frac_of_measured": achieved / max(measured_peak.values())},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for(wl.name, dominant),
                      "kernel": dominant, "avg_ms": main_avg},
@@ -340,6 +438,15 @@ def main(argv=None):
             "note": "Y and statistics for the same inputs; useful work 4*N*D per admitted pair (two contractions)",
         },
     }
+
+    out["cold_layout"] = cold_layout_calls(B, q, k, v, dy, y, smax, ssum, inp, wl, drop, dq, dk, dv, stream)
+    log(f"cold layout: {out['cold_layout']['ms_per_call']:.3f} ms/call, host "
+        f"{out['cold_layout']['host_us_per_call']:.0f} us vs {out['cold_layout']['cached_host_us_per_call']:.0f} us cached")
+    if args.workload == 3 and not args.no_extra_workloads:
+        out["workloads"] = {}
+        for number in (2, 4, 5):
+            r = other_workload(number, steps=min(args.steps, 10), warmup=args.warmup)
+            out["workloads"][r.pop("workload")] = r
 
     if not args.no_cpu_baseline:
         y_host = synth.as_float_array(y.cpu())

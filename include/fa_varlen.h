@@ -19,7 +19,7 @@
  * Argument list and error classes follow the page's 函数原型 (prototypes),
  * 参数说明 (parameter table) and 返回值 (return codes) sections, collapsed
  * into one call: there is no separate workspace query, the library keeps its
- * own workspace.
+ * own workspace (see fa_varlen_bwd).
  *
  * Ownership: the caller owns every tensor, both cu_seqlens arrays and the
  * stream.  Tensor and statistics pointers are DEVICE pointers; cu_seqlens
@@ -140,13 +140,22 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_BAND = 2 };
  * allows return FA_ERR_UNSUPPORTED.
  * Tq == 0 returns FA_OK with nothing launched.
  *
- * Calls on different streams share one library workspace per device and
- * must not overlap in time.
+ * Library memory: the work lists (which tiles each workgroup visits) are built on the host once
+ * per sequence layout (cu_seqlens, mask mode and window, heads, dtype path), uploaded with an
+ * asynchronous copy on `stream` from pinned staging memory, and never modified afterwards; the
+ * host does not wait for the device, also when the layout changes.  Up to 64 layouts stay cached
+ * per device; an evicted list's memory is reused only after its last uses have completed.  The
+ * row statistics (8 bytes per query token and head) live in a buffer per stream, so calls on
+ * different streams may overlap.  A stream's buffer grows when a call needs more (the host then
+ * waits for that stream once).  fa_release() frees everything.
  *
- * Graph capture: the first call with a given sequence layout, mask mode and dtype path builds
- * and uploads a work list (a host-synchronous copy) and may grow the workspace.  Later calls
- * with the same layout only enqueue kernels on stream, so they can be recorded into a HIP graph
- * and replayed; make one uncaptured call first.
+ * Graph capture: a call made while `stream` is being captured allocates and uploads nothing.  It
+ * needs a cached list for its layout and a large enough row-statistics buffer on that stream,
+ * i.e. one earlier uncaptured call with the same layout and at least as many tokens on the same
+ * stream; otherwise it returns FA_ERR_UNSUPPORTED.  The list and the buffer it records are then
+ * kept for the graph until fa_release(): later calls, with any layout, never modify or reuse
+ * them, so the graph can be replayed at any time.  Replays of one graph must not overlap each
+ * other (they share that buffer).
  */
 int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
                   const fa_tensor_t* dy, const fa_tensor_t* y,
@@ -179,8 +188,10 @@ int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_te
 /* Thread-local description of the last non-OK status (empty string if none). */
 const char* fa_last_error(void);
 
-/* Frees the library's cached device workspace and work lists (synchronises
- * the device first).  The next fa_varlen_bwd call re-allocates them. */
+/* Frees the library's cached work lists, staging memory and row-statistics
+ * buffers, including those kept for captured graphs (synchronises every device
+ * first; graphs that recorded calls must not be replayed afterwards).  The next
+ * call re-allocates what it needs. */
 void fa_release(void);
 
 /* One work item: a block of rows of one sequence that a workgroup keeps
@@ -253,7 +264,8 @@ int fa_profile_read(double* ms, int64_t* launches, int capacity);
  * no admitted key gets max -inf, sum 0 and a zero Y row.  The statistics are those of the
  * softmax before dropout, which is what fa_varlen_bwd expects.
  * Returns the status codes of fa_varlen_bwd.  FA_ERR_UNSUPPORTED also when dropout is on and
- * a sequence has Lq * Lkv >= 2^34.  Asynchronous on stream; the same workspace rules apply.
+ * a sequence has Lq * Lkv >= 2^34.  Asynchronous on stream; its work lists follow the rules of
+ * fa_varlen_bwd (it has no row statistics).
  */
 int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
                   const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
@@ -270,13 +282,6 @@ int fa_varlen_fwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_te
                          const uint8_t* drop_mask, const fa_mask_t* atten_mask, double scale,
                          int64_t head_num, const fa_tensor_t* y, float* softmax_max, float* softmax_sum,
                          void* stream);
-
-/* Measured matrix-core ceiling of the current device (a diagnostic, not part of the
- * operator): runs a kernel of independent bf16 32x32x16 MFMAs, one workgroup per compute
- * unit with waves_per_simd (1 or 2) waves on each SIMD, on the null stream, synchronously,
- * and writes its rate in TFLOP/s to *tflops.  Returns FA_OK, FA_ERR_NULLPTR (tflops null),
- * FA_ERR_INVALID (waves_per_simd not 1 or 2) or FA_ERR_RUNTIME. */
-int fa_mfma_peak(int32_t waves_per_simd, double* tflops);
 
 #ifdef __cplusplus
 }

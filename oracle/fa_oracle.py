@@ -214,31 +214,56 @@ def forward_rows(q, k, v, cu_q, cu_kv, b: int, n: int, rows, *, mode: int = MASK
     return _forward_rows(qr, ks, vs, q1 - q0, rows, scale, mode, pre, nxt, keep_prob, drop_mask, bit0, xm)
 
 
+def _forward_pool_unit(job):
+    b, n = job
+    st = _POOL_STATE
+    q, k, cu_q, cu_kv, head_num = st["q"], st["k"], st["cu_q"], st["cu_kv"], st["head_num"]
+    q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+    k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
+    bit0 = int(st["bases"][b]) + n * (q1 - q0) * (k1 - k0)
+    hk = kv_head(n, head_num, k.shape[1])
+    return (b, n) + forward_unit(q[q0:q1, n], k[k0:k1, hk], st["v"][k0:k1, hk], st["scale"], st["mode"],
+                                 st["pre"], st["nxt"], st["keep_prob"], st["drop_mask"], bit0,
+                                 explicit_mask_block(st["atten_mask"], b, n, q1 - q0, k1 - k0))
+
+
 def forward(q, k, v, cu_q, cu_kv, *, mode: int = MASK_NONE, pre: int = 0, nxt: int = 0,
-            keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int, atten_mask=None):
+            keep_prob: float = 1.0, drop_mask=None, scale: float, head_num: int, atten_mask=None,
+            workers: int = 1):
     """Varlen forward over TND tensors; returns Y [T, N, Dv], m [N, T], l [N, T] (fp64).
 
     q is [Tq, N, Dk]; k and v are [Tkv, Nkv, Dk] and [Tkv, Nkv, Dv] with N a multiple of Nkv (R15).
+    With workers > 1 the (sequence, head) units run in a fork-based process pool, each computed
+    exactly as with workers == 1.
     """
     tq = q.shape[0]
     y = np.zeros((tq, head_num, v.shape[2]), dtype=np.float64)
     m = np.full((head_num, tq), -np.inf, dtype=np.float64)
     l = np.zeros((head_num, tq), dtype=np.float64)
     bases = dropout_bit_bases(cu_q, cu_kv, head_num)
-    for b in range(len(cu_q) - 1):
+    units = [(b, n) for b in range(len(cu_q) - 1) for n in range(head_num) if cu_q[b + 1] > cu_q[b]]
+
+    def put(b, n, yb, mb, lb):
         q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
-        k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
-        if q1 == q0:
-            continue
-        for n in range(head_num):
+        y[q0:q1, n] = yb
+        m[n, q0:q1] = mb
+        l[n, q0:q1] = lb
+
+    if workers <= 1 or len(units) <= 1:
+        for b, n in units:
+            q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+            k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
             bit0 = int(bases[b]) + n * (q1 - q0) * (k1 - k0)
             hk = kv_head(n, head_num, k.shape[1])
-            yb, mb, lb = forward_unit(q[q0:q1, n], k[k0:k1, hk], v[k0:k1, hk], scale,
-                                      mode, pre, nxt, keep_prob, drop_mask, bit0,
-                                      explicit_mask_block(atten_mask, b, n, q1 - q0, k1 - k0))
-            y[q0:q1, n] = yb
-            m[n, q0:q1] = mb
-            l[n, q0:q1] = lb
+            put(b, n, *forward_unit(q[q0:q1, n], k[k0:k1, hk], v[k0:k1, hk], scale,
+                                    mode, pre, nxt, keep_prob, drop_mask, bit0,
+                                    explicit_mask_block(atten_mask, b, n, q1 - q0, k1 - k0)))
+        return y, m, l
+    state = dict(q=q, k=k, v=v, cu_q=np.asarray(cu_q, dtype=np.int64), cu_kv=np.asarray(cu_kv, dtype=np.int64),
+                 bases=bases, scale=scale, mode=mode, pre=pre, nxt=nxt, keep_prob=keep_prob,
+                 drop_mask=drop_mask, atten_mask=atten_mask, head_num=head_num)
+    for b, n, yb, mb, lb in _pool_map(_forward_pool_unit, units, state, workers):
+        put(b, n, yb, mb, lb)
     return y, m, l
 
 
@@ -386,10 +411,17 @@ def backward(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, *, mode: int
                                      keep_prob, drop_mask, bit0, xmask=xm))
         return dq, dk, dv
 
-    import multiprocessing as mp
     state = dict(q=q, k=k, v=v, dy=dy, y=y, m=mstat, l=lstat, cu_q=cu_q, cu_kv=cu_kv,
                  bases=bases, scale=scale, mode=mode, pre=pre, nxt=nxt,
                  keep_prob=keep_prob, drop_mask=drop_mask, atten_mask=atten_mask)
+    for b, n, dqs, dks, dvs in _pool_map(_pool_unit, units, state, workers):
+        put(b, n, dqs, dks, dvs)
+    return dq, dk, dv
+
+
+def _pool_map(fn, jobs, state, workers):
+    """fn over jobs in a fork-based process pool whose workers see `state`; results in job order."""
+    import multiprocessing as mp
     ctx = mp.get_context("fork")
     # one BLAS thread per worker: the pool supplies the parallelism
     old = {key: os.environ.get(key) for key in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
@@ -397,15 +429,14 @@ def backward(q, k, v, dy, y, softmax_max, softmax_sum, cu_q, cu_kv, *, mode: int
         os.environ[key] = "1"
     try:
         with ctx.Pool(processes=workers, initializer=_pool_init, initargs=(state,)) as pool:
-            for b, n, dqs, dks, dvs in pool.imap(_pool_unit, units):
-                put(b, n, dqs, dks, dvs)
+            for r in pool.imap(fn, jobs):
+                yield r
     finally:
         for key, val in old.items():
             if val is None:
                 os.environ.pop(key, None)
             else:
                 os.environ[key] = val
-    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

@@ -19,22 +19,46 @@ def tol_for(dtype):
     return 1e-5 if dtype == torch.float32 else 1e-2
 
 
-def assert_close(name, g, o, dtype):
+def assert_close(name, g, o, dtype, zero_bound=0.0):
+    """The parity criterion on one output tensor: relative Frobenius error <= 1e-5 (fp32) or 1e-2
+    (bf16 / fp16) and max |gpu - oracle| <= 5e-2 * max |oracle|.
+
+    For an all-zero oracle tensor the relative criterion is undefined: every GPU value must then
+    lie within `zero_bound` of zero (0: exact zeros; see cancellation_bound for the one case where
+    the oracle's zero is an exact cancellation the GPU reproduces only up to fp32 rounding)."""
     g = np.asarray(g, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
-    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values (unwritten or overflowed elements)"
     ref = np.linalg.norm(o)
     err = np.linalg.norm(g - o)
     mx = np.max(np.abs(o)) if o.size else 0.0
     if ref == 0.0:
-        # The relative criterion is undefined for an all-zero reference.  Where the
-        # zero comes from cancellation (dP - D with Ps = 1) fp32 leaves a residue of
-        # order 1e-7; rows with no admitted key are checked for exact zeros separately.
-        assert np.max(np.abs(g)) <= 1e-5, f"{name}: expected zeros, max |gpu| = {np.max(np.abs(g)):.3e}"
+        got = np.max(np.abs(g)) if g.size else 0.0
+        assert got <= zero_bound, f"{name}: expected zeros (bound {zero_bound:.3e}), max |gpu| = {got:.3e}"
         return
     rel = err / ref
+    log(f"  {name}: relative Frobenius error {rel:.3e}, max abs error {np.max(np.abs(g - o)):.3e} "
+        f"(max |ref| {mx:.3e})")
     assert rel <= tol_for(dtype), f"{name}: relative Frobenius error {rel:.3e}"
     assert np.max(np.abs(g - o)) <= 5e-2 * mx, f"{name}: max abs error {np.max(np.abs(g - o)):.3e} vs {mx:.3e}"
+
+
+def cancellation_bound(inp, scale, rows_per_key=1):
+    """Bound on |dQ| and |dK| where the oracle's dS is exactly zero because dP_ij = D_i.
+
+    That happens when a row's admitted keys all carry the same V row as Y (e.g. one-token
+    sequences: P = 1, Y = V_j).  The GPU forms dP_ij = dY_i . V_j with the matrix cores and D_i =
+    dY_i . Y_i in its row pass: two fp32 sums of the same Dv products in different orders, each
+    within gamma = Dv * 2^-24 * sum_d |dY_id V_jd| <= gamma * ||dY_i|| ||V_j|| of the exact value,
+    so |dP - D| <= 2 gamma ||dY_i|| ||V_j||.  Then |dQ_i| = |scale| |sum_j P_ij (dP - D)_ij K_j|
+    <= |scale| max |dP - D| max |K| (the P_ij sum to 1), and |dK_j| <= |scale| rows_per_key
+    max |dP - D| max |Q| (rows_per_key bounds sum_i P_ij).  Returned as (dq_bound, dk_bound)."""
+    f = lambda t: synth.as_float_array(t)  # noqa: E731
+    q, k, v, dy = f(inp.q), f(inp.k), f(inp.v), f(inp.dy)
+    dv_dim = v.shape[2]
+    gamma = dv_dim * 2.0 ** -24
+    r = 2.0 * gamma * np.max(np.linalg.norm(dy, axis=2)) * np.max(np.linalg.norm(v, axis=2))
+    return abs(scale) * r * np.max(np.abs(k)), abs(scale) * rows_per_key * r * np.max(np.abs(q))
 
 
 def oracle_forward(inp, mode, pre, nxt, kp, scale, atten_mask=None):
@@ -93,8 +117,9 @@ def run_small(inp, mode, pre=0, nxt=0, kp=1.0, scale=None, poison_empty=False, v
         ssum[empty] = np.nan
     ref = oracle_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, atten_mask=atten_mask)
     got = gpu_backward(inp, yt, smax, ssum, mode, pre, nxt, kp, scale, views=views, atten_mask=atten_mask)
-    for name, g, o in zip(("dq", "dk", "dv"), got, ref):
-        assert_close(name, g.double().numpy(), o, inp.q.dtype)
+    bq, bk = cancellation_bound(inp, scale, rows_per_key=int(np.max(np.diff(inp.cu_q))))
+    for name, g, o, zb in zip(("dq", "dk", "dv"), got, ref, (bq, bk, 0.0)):
+        assert_close(name, g.double().numpy(), o, inp.q.dtype, zero_bound=zb)
     return got, ref, (yt, smax, ssum)
 
 

@@ -9,6 +9,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 from variable_length_flashattention_fa_amd import binding as B
 
@@ -45,7 +46,8 @@ def _t(tokens, heads=2, dim=64, dtype=B.FA_BF16, data=FAKE):
 
 
 def _call(q=None, k=None, v=None, dy=None, y=None, smax=FAKE, ssum=FAKE, cu_q=(0, 10), cu_kv=(0, 10),
-          mode=0, pre=0, nxt=0, kp=1.0, drop=None, scale=0.125, head_num=2, dq=None, dk=None, dv=None):
+          mode=0, pre=0, nxt=0, kp=1.0, drop=None, scale=0.125, head_num=2, dq=None, dk=None, dv=None,
+          entry="fa_varlen_bwd"):
     tq = cu_q[-1]
     tk = cu_kv[-1]
     q = q if q is not None else _t(tq)
@@ -62,7 +64,7 @@ def _call(q=None, k=None, v=None, dy=None, y=None, smax=FAKE, ssum=FAKE, cu_q=(0
     sk = B.FaSeqlens(ak.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ak.size - 1)
     lib = B.load()
     ref = lambda x: None if x is None else ctypes.byref(x)  # noqa: E731
-    st = lib.fa_varlen_bwd(ref(q), ref(k), ref(v), ref(dy), ref(y),
+    st = getattr(lib, entry)(ref(q), ref(k), ref(v), ref(dy), ref(y),
                            None if smax is None else ctypes.c_void_p(smax),
                            None if ssum is None else ctypes.c_void_p(ssum), ctypes.byref(sq), ctypes.byref(sk),
                            mode, pre, nxt, kp, None if drop is None else ctypes.c_void_p(drop), scale,
@@ -231,20 +233,27 @@ def test_empty_query_returns_ok_without_device_work():
     assert st == B.FA_OK, msg
 
 
+def _no_gpu():
+    # counting devices does not initialise the GPU on this image
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a host without a GPU: the HIP runtime must fail")
+def test_hip_failure_is_reported_as_runtime_error():
+    # a valid call on a host where the HIP runtime has no device: the first HIP call fails, and the
+    # status is FA_ERR_RUNTIME with the runtime's message (nothing can have been launched)
+    st, msg = _call()
+    assert st == B.FA_ERR_RUNTIME, (st, msg)
+    assert msg and "hipGetDevice" in msg, msg
+    st, msg = _fwd()
+    assert st == B.FA_ERR_RUNTIME, (st, msg)
+    assert msg
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         B.load(str(tmp_path / "libfa_varlen.so"))
 
-
-def test_mfma_peak_rejects_bad_arguments():
-    lib = B.load()
-    out = ctypes.c_double(0.0)
-    assert lib.fa_mfma_peak(2, None) == 1  # FA_ERR_NULLPTR
-    assert lib.fa_mfma_peak(3, ctypes.byref(out)) == 2  # FA_ERR_INVALID
-    assert lib.fa_mfma_peak(0, ctypes.byref(out)) == 2
-
-
-# --- forward entry point ----------------------------------------------------------------------
 
 def _fwd(q=None, k=None, v=None, y=None, smax=FAKE, ssum=FAKE, cu_q=(0, 10), cu_kv=(0, 10), mode=0, pre=0,
          nxt=0, kp=1.0, drop=None, scale=0.125, head_num=2):

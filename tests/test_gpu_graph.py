@@ -1,6 +1,6 @@
-"""Graph capture: once a layout's work list is cached, a call only enqueues kernels (no
-allocation, copy or synchronisation), so the backward and the forward can be recorded into a HIP
-graph. Each replay must reproduce the eager result bit for bit (every path is deterministic);
+"""Graph capture: once a layout's work list is cached and the stream has a row-statistics buffer,
+a call only enqueues kernels (no allocation, copy or synchronisation), so the backward and the
+forward can be recorded into a HIP graph. Each replay must reproduce the eager result bit for bit (every path is deterministic);
 replays are separated by eager work and synchronisations."""
 import numpy as np
 import pytest
@@ -42,7 +42,9 @@ def test_backward_and_forward_replay_in_a_graph(dtype):
 
     log(f"capturing the backward and the forward ({dtype})")
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    # captured on the stream of the uncaptured call: its row-statistics buffer is the one the graph
+    # records (the library allocates nothing while a stream is being captured)
+    with torch.cuda.graph(graph, stream=side):
         calls()
     for rep in range(3):
         for t in (dq, dk, dv, yf, mf, lf):

@@ -322,6 +322,50 @@ def test_forward_matches_torch_logsumexp():
             np.testing.assert_allclose(y[sl, n], (torch.softmax(s, -1) @ tv).numpy(), rtol=0, atol=1e-13)
 
 
+def test_stats_page_layout_against_torch_logsumexp():
+    """The page's parameter table gives softmaxMax / softmaxSum the shape [N, T, 8] (reading R6:
+    the row value repeated over the last axis, fp32).  Read every one of the 8 entries of every
+    (head, token) back by explicit indexing and compare max + log(sum) with torch's logsumexp of
+    that row's scaled, masked scores: a swapped N / T axis, a missing repeat or a value left
+    unrounded fails here (N != T, and the fp32 rounding is checked to the ulp)."""
+    rng = np.random.default_rng(31)
+    heads, lens = 3, (5, 9)
+    q, k, v, dy, cu_q, cu_kv, _ = _rand_case(rng, lens, None, heads=heads, dim=8)
+    _, m, l = O.forward(q, k, v, cu_q, cu_kv, mode=O.MASK_CAUSAL, scale=0.7, head_num=heads)
+    mm, ll = O.stats_to_page_layout(m, l)
+    tq = int(cu_q[-1])
+    assert mm.shape == (heads, tq, 8) and ll.shape == (heads, tq, 8)
+    assert mm.dtype == np.float32 and ll.dtype == np.float32
+    for b in range(len(lens)):
+        for n in range(heads):
+            tqn = torch.from_numpy(q[cu_q[b]:cu_q[b + 1], n])
+            tkn = torch.from_numpy(k[cu_kv[b]:cu_kv[b + 1], n])
+            s = 0.7 * tqn @ tkn.T
+            s = s.masked_fill(~torch.ones_like(s, dtype=torch.bool).tril(), float("-inf"))
+            lse = torch.logsumexp(s, dim=-1).numpy()
+            rowmax = s.max(dim=-1).values.numpy()
+            for i, t in enumerate(range(int(cu_q[b]), int(cu_q[b + 1]))):
+                for e in range(8):
+                    # each entry is the fp32 value nearest the exact one
+                    assert abs(float(mm[n, t, e]) - rowmax[i]) <= 0.5 * abs(np.spacing(np.float32(rowmax[i])))
+                    got = float(mm[n, t, e]) + math.log(float(ll[n, t, e]))
+                    assert abs(got - lse[i]) <= 4 * np.spacing(np.float32(abs(lse[i]) + 1.0))
+
+
+def test_process_pool_forward_and_backward_equal_serial():
+    rng = np.random.default_rng(32)
+    q, k, v, dy, cu_q, cu_kv, drop = _rand_case(rng, (20, 3, 33), None, heads=3, dim=8, keep_prob=0.8)
+    kw = dict(mode=O.MASK_BAND, pre=5, nxt=2, keep_prob=0.8, drop_mask=drop, scale=0.4, head_num=3)
+    y1, m1, l1 = O.forward(q, k, v, cu_q, cu_kv, **kw)
+    y4, m4, l4 = O.forward(q, k, v, cu_q, cu_kv, workers=4, **kw)
+    for a, c in ((y1, y4), (m1, m4), (l1, l4)):
+        np.testing.assert_array_equal(a, c)
+    g1 = O.backward(q, k, v, dy, y1, m1, l1, cu_q, cu_kv, **kw)
+    g4 = O.backward(q, k, v, dy, y1, m1, l1, cu_q, cu_kv, workers=4, **kw)
+    for a, c in zip(g1, g4):
+        np.testing.assert_array_equal(a, c)
+
+
 # --- P4: packed == each sequence alone (bitwise) -----------------------------------------
 
 def _slice_bits(drop, start, count):

@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libfa_varlen.so")
+# FA_VARLEN_LIB may name another build of the same library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("FA_VARLEN_LIB") or os.path.join(_PKG, "lib", "libfa_varlen.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_NULLPTR, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_RUNTIME = 0, 1, 2, 3, 4
@@ -55,7 +56,7 @@ class FaError(RuntimeError):
 _lib = None
 
 EXPORTS = ("fa_varlen_bwd", "fa_varlen_bwd_masked", "fa_varlen_fwd", "fa_varlen_fwd_masked", "fa_last_error",
-           "fa_release", "fa_varlen_worklist", "fa_profile_enable", "fa_profile_read", "fa_mfma_peak")
+           "fa_release", "fa_varlen_worklist", "fa_profile_enable", "fa_profile_read")
 KERNEL_NAMES = ("preprocess", "bwd_main", "unused", "bwd_dq", "fwd")
 
 
@@ -99,8 +100,6 @@ def load(path: Optional[str] = None):
     lib.fa_profile_enable.restype = None
     lib.fa_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     lib.fa_profile_read.restype = ctypes.c_int
-    lib.fa_mfma_peak.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
-    lib.fa_mfma_peak.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -181,16 +180,8 @@ def _check_args(q, tensors: dict, stats: dict, cu_q, cu_kv, keep_prob, drop_mask
             raise ValueError("atten_mask axes must be [B or 1, N or 1, Sq, Skv]")
 
 
-def fa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dy: torch.Tensor, y: torch.Tensor,
-                  softmax_max: torch.Tensor, softmax_sum: torch.Tensor, cu_seqlens_q, cu_seqlens_kv,
-                  atten_mode: int, pre_tokens: int, next_tokens: int, keep_prob: float,
-                  drop_mask: Optional[torch.Tensor], scale: float, head_num: int, dq: torch.Tensor,
-                  dk: torch.Tensor, dv: torch.Tensor, stream=None) -> None:
-    """Same arguments as the C entry point; tensors are device tensors, cu_seqlens host sequences.
-
-    Enqueues the backward on `stream` (default: torch's current stream) and
-    raises FaError on a non-OK status.
-    """
+def _bwd(entry: str, q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
+         pre_tokens, next_tokens, keep_prob, drop_mask, scale, head_num, dq, dk, dv, stream) -> None:
     lib = load()
     _check_args(q, dict(k=k, v=v, dy=dy, y=y, dq=dq, dk=dk, dv=dv), dict(softmax_max=softmax_max,
                 softmax_sum=softmax_sum), cu_seqlens_q, cu_seqlens_kv, keep_prob, drop_mask, None)
@@ -201,22 +192,33 @@ def fa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dy: torch.T
     for st in (softmax_max, softmax_sum):
         if st is not None and not st.is_contiguous():
             raise ValueError("softmax statistics must be contiguous [N, T, 8] fp32")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
-    elif isinstance(stream, torch.cuda.Stream):
-        stream = stream.cuda_stream
+    stream = _stream(q, stream)
 
     def ref(x):
         return None if x is None else ctypes.byref(x)
 
-    status = lib.fa_varlen_bwd(ref(tq), ref(tk), ref(tv), ref(tdy), ref(ty), _ptr(softmax_max),
-                               _ptr(softmax_sum), ctypes.byref(sq), ctypes.byref(sk), int(atten_mode),
-                               int(pre_tokens), int(next_tokens), float(keep_prob), _ptr(drop_mask),
-                               float(scale), int(head_num), ref(tdq), ref(tdk), ref(tdv),
-                               ctypes.c_void_p(int(stream)))
+    status = getattr(lib, entry)(ref(tq), ref(tk), ref(tv), ref(tdy), ref(ty), _ptr(softmax_max),
+                                 _ptr(softmax_sum), ctypes.byref(sq), ctypes.byref(sk), int(atten_mode),
+                                 int(pre_tokens), int(next_tokens), float(keep_prob), _ptr(drop_mask),
+                                 float(scale), int(head_num), ref(tdq), ref(tdk), ref(tdv),
+                                 ctypes.c_void_p(int(stream)))
     del aq, ak
     if status != FA_OK:
         raise FaError(status, last_error())
+
+
+def fa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dy: torch.Tensor, y: torch.Tensor,
+                  softmax_max: torch.Tensor, softmax_sum: torch.Tensor, cu_seqlens_q, cu_seqlens_kv,
+                  atten_mode: int, pre_tokens: int, next_tokens: int, keep_prob: float,
+                  drop_mask: Optional[torch.Tensor], scale: float, head_num: int, dq: torch.Tensor,
+                  dk: torch.Tensor, dv: torch.Tensor, stream=None) -> None:
+    """Same arguments as the C entry point; tensors are device tensors, cu_seqlens host sequences.
+
+    Enqueues the backward on `stream` (default: torch's current stream) and
+    raises FaError on a non-OK status.
+    """
+    _bwd("fa_varlen_bwd", q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
+         pre_tokens, next_tokens, keep_prob, drop_mask, scale, head_num, dq, dk, dv, stream)
 
 
 def fa_varlen_bwd_masked(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
@@ -297,10 +299,7 @@ def fa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
     for st in (softmax_max, softmax_sum):
         if st is not None and not st.is_contiguous():
             raise ValueError("softmax statistics must be contiguous [N, T, 8] fp32")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
-    elif isinstance(stream, torch.cuda.Stream):
-        stream = stream.cuda_stream
+    stream = _stream(q, stream)
 
     def ref(x):
         return None if x is None else ctypes.byref(x)
@@ -395,11 +394,3 @@ def profile_read() -> dict:
         raise FaError(-n, last_error())
     return {KERNEL_NAMES[i]: (ms[i], cnt[i]) for i in range(min(n, k))}
 
-
-def mfma_peak(waves_per_simd: int = 2) -> float:
-    """Measured bf16 MFMA rate of the current device in TFLOP/s (see fa_mfma_peak)."""
-    out = ctypes.c_double(0.0)
-    st = load().fa_mfma_peak(int(waves_per_simd), ctypes.byref(out))
-    if st != 0:
-        raise FaError(st, last_error())
-    return out.value

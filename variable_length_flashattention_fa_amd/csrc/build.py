@@ -23,7 +23,8 @@ LIBNAME = "libfa_varlen.so"
 # would need copying back.  fa_bwd16.hip and fa_fwd.hip compile in parts (one per kernel and
 # dtype), in parallel.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-HIP_UNITS = [("fa_kernels.hip", "fa_kernels", []), ("fa_probe.hip", "fa_probe", []), ("fa_api.cpp", "fa_api", [])]
+HIP_UNITS = [("fa_kernels.hip", "fa_kernels", []), ("fa_api.cpp", "fa_api", []),
+             ("fa_workspace.cpp", "fa_workspace", []),]
 HIP_UNITS += [("fa_bwd16.hip", f"fa_bwd16_p{i}", _VGPR_FORM + [f"-DFA_BWD16_PART={i}"]) for i in (1, 2, 3, 4)]
 HIP_UNITS += [("fa_fwd.hip", f"fa_fwd_p{i}", _VGPR_FORM + [f"-DFA_FWD_PART={i}"]) for i in (1, 2)]
 HIP_SOURCES = sorted({u[0] for u in HIP_UNITS})
@@ -79,12 +80,55 @@ def build(arch: str = "gfx950", verbose: bool = False) -> str:
     return out
 
 
+# Host sources of the C ABI (validation, work lists, library memory): the ones the CPU sanitizer
+# build instruments.
+HOST_SANITIZED = ["fa_worklist.cpp", "fa_api.cpp", "fa_workspace.cpp"]
+SANITIZED_LIBNAME = "libfa_varlen_host_asan.so"
+
+
+def build_host_sanitized(arch: str = "gfx950") -> str:
+    """libfa_varlen_host_asan.so: the host sources compiled by g++ with AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the (uninstrumented) kernel objects of build().
+
+    For CPU tests of validation and work lists under the sanitizers (load it with libasan
+    preloaded).  Builds the kernel objects first if they are missing."""
+    objdir = os.path.join(PKG, "_build")
+    kernel_objs = [os.path.join(objdir, name + ".o") for src, name, _ in HIP_UNITS
+                   if src.endswith(".hip")]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build(arch)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+    flags = ["-O1", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{HERE}", f"-I{os.path.join(rocm, 'include')}",
+             "-D__HIP_PLATFORM_AMD__", "-Wall"] + san
+    sobjdir = os.path.join(objdir, "host_asan")
+    os.makedirs(sobjdir, exist_ok=True)
+    objs = []
+    jobs = []
+    for src in HOST_SANITIZED:
+        obj = os.path.join(sobjdir, src + ".o")
+        jobs.append(["g++"] + flags + ["-x", "c++", "-c", os.path.join(HERE, src), "-o", obj])
+        objs.append(obj)
+    with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        list(ex.map(_run, jobs))
+    out = os.path.join(LIBDIR, SANITIZED_LIBNAME)
+    tmp = out + ".tmp"
+    _run(["g++", "-shared"] + san + ["-o", tmp] + objs + kernel_objs +
+         [f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"])
+    os.replace(tmp, out)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--arch", default="gfx950")
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--host-sanitized", action="store_true",
+                    help="also build lib/libfa_varlen_host_asan.so (host sources under ASan / UBSan)")
     args = ap.parse_args(argv)
     print(build(args.arch, args.verbose))
+    if args.host_sanitized:
+        print(build_host_sanitized(args.arch))
 
 
 if __name__ == "__main__":

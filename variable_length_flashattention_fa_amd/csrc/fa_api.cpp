@@ -15,6 +15,7 @@
 
 #include "fa_internal.h"
 #include "fa_kernels.h"
+#include "fa_workspace.h"
 
 namespace fa {
 const char* last_error_cstr();
@@ -65,24 +66,6 @@ bool aligned16(const fa_tensor_t* t) {
            ((t->stride_h * es) % 16 == 0);
 }
 
-struct Workspace {
-    float* rowstat = nullptr;  // planes of -D and beta
-    size_t rowstat_bytes = 0;
-    fa_work_item_t* items = nullptr;
-    size_t items_cap = 0;
-    // cached work lists: their key and item counts (key-block items, then query-block items)
-    std::vector<int64_t> key;
-    int64_t n_items = 0;
-    int64_t n_q_items = 0;
-    // the forward's query-block list, cached the same way
-    fa_work_item_t* fwd_items = nullptr;
-    size_t fwd_items_cap = 0;
-    std::vector<int64_t> fwd_key;
-    int64_t n_fwd_items = 0;
-};
-
-std::mutex g_mutex;
-std::unordered_map<int, Workspace> g_ws;
 
 // ---- optional per-kernel event timing ----
 constexpr int kKernels = 5;  // 0 row pass (fp32 path), 1 dK/dV, 2 (unused), 3 dQ, 4 forward
@@ -125,21 +108,6 @@ int runtime_error(const char* what, hipError_t e) {
     return FA_ERR_RUNTIME;
 }
 
-int grow(void** ptr, size_t* cap, size_t need, const char* what) {
-    if (need <= *cap && *ptr != nullptr) return FA_OK;
-    if (*ptr != nullptr) {
-        hipError_t e = hipFree(*ptr);  // hipFree synchronises with outstanding work
-        *ptr = nullptr;
-        *cap = 0;
-        if (e != hipSuccess) return runtime_error(what, e);
-    }
-    size_t bytes = need < 256 ? 256 : need;
-    hipError_t e = hipMalloc(ptr, bytes);
-    if (e != hipSuccess) return runtime_error(what, e);
-    *cap = bytes;
-    return FA_OK;
-}
-
 // Checks an explicit mask view against the sequence layout (see fa_mask_t in fa_varlen.h).
 int check_mask(const fa_mask_t* m, const fa_seqlens_t* cq, const fa_seqlens_t* ck) {
     if (m->stride_b < 0 || m->stride_n < 0 || m->stride_q < 0 || m->rows < 0 || m->cols < 0) {
@@ -171,27 +139,17 @@ int check_mask(const fa_mask_t* m, const fa_seqlens_t* cq, const fa_seqlens_t* c
 extern "C" const char* fa_last_error(void) { return fa::last_error_cstr(); }
 
 extern "C" void fa_release(void) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    int cur = 0;
-    (void)hipGetDevice(&cur);
-    for (auto& kv : g_ws) {
-        (void)hipSetDevice(kv.first);
-        (void)hipDeviceSynchronize();
-        if (kv.second.rowstat) (void)hipFree(kv.second.rowstat);
-        if (kv.second.items) (void)hipFree(kv.second.items);
-        if (kv.second.fwd_items) (void)hipFree(kv.second.fwd_items);
-    }
-    g_ws.clear();
-    (void)hipSetDevice(cur);
+    std::lock_guard<std::mutex> lock(fa::state_mutex());
+    fa::release_all();
 }
 
 extern "C" void fa_profile_enable(int on) {
-    std::lock_guard<std::mutex> lock(g_mutex);
+    std::lock_guard<std::mutex> lock(fa::state_mutex());
     g_profile = on != 0;
 }
 
 extern "C" int fa_profile_read(double* ms, int64_t* launches, int capacity) {
-    std::lock_guard<std::mutex> lock(g_mutex);
+    std::lock_guard<std::mutex> lock(fa::state_mutex());
     double sum[kKernels] = {0, 0, 0, 0, 0};
     int64_t cnt[kKernels] = {0, 0, 0, 0, 0};
     int status = kKernels;
@@ -227,15 +185,15 @@ extern "C" int fa_varlen_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const f
                                 dv, stream);
 }
 
-extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
-                                    const fa_tensor_t* dy, const fa_tensor_t* y, const float* softmax_max,
-                                    const float* softmax_sum, const fa_seqlens_t* cu_seqlens_q,
-                                    const fa_seqlens_t* cu_seqlens_kv, int32_t atten_mode, int64_t pre_tokens,
-                                    int64_t next_tokens, double keep_prob, const uint8_t* drop_mask,
-                                    const fa_mask_t* atten_mask, double scale, int64_t head_num,
-                                    const fa_tensor_t* dq, const fa_tensor_t* dk, const fa_tensor_t* dv,
-                                    void* stream) {
-    fa::clear_error();
+namespace fa {
+
+int plan_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v, const fa_tensor_t* dy,
+             const fa_tensor_t* y, const float* softmax_max, const float* softmax_sum,
+             const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv, int32_t atten_mode,
+             int64_t pre_tokens, int64_t next_tokens, double keep_prob, const uint8_t* drop_mask,
+             const fa_mask_t* atten_mask, double scale, int64_t head_num, const fa_tensor_t* dq,
+             const fa_tensor_t* dk, const fa_tensor_t* dv, BwdPlan* plan) {
+    clear_error();
     // ---- null pointers (page: ACLNN_ERR_PARAM_NULLPTR) ----
     const fa_tensor_t* all[8] = {q, k, v, dy, y, dq, dk, dv};
     const char* names[8] = {"q", "k", "v", "dy", "y", "dq", "dk", "dv"};
@@ -342,96 +300,95 @@ extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
         }
     }
 
+    plan->q = q;
+    plan->k = k;
+    plan->v = v;
+    plan->dy = dy;
+    plan->y = y;
+    plan->dq = dq;
+    plan->dk = dk;
+    plan->dv = dv;
+    plan->softmax_max = softmax_max;
+    plan->softmax_sum = softmax_sum;
+    plan->cu_q = cu_seqlens_q->cu;
+    plan->cu_kv = cu_seqlens_kv->cu;
+    plan->batch = batch;
+    plan->mode = atten_mode;
+    plan->pre = atten_mode == FA_MASK_BAND ? clamp_window(pre_tokens) : 0;
+    plan->nxt = atten_mode == FA_MASK_BAND ? clamp_window(next_tokens) : 0;
+    plan->keep_prob = keep_prob;
+    plan->drop_mask = drop_mask;
+    plan->atten_mask = atten_mask;
+    plan->scale = scale;
+    return FA_OK;
+}
+
+std::vector<int64_t> bwd_list_key(const BwdPlan& p) {
+    std::vector<int64_t> key;
+    key.reserve(2 * (p.batch + 1) + 6);
+    key.push_back(0);  // backward lists
+    key.push_back(p.mode);
+    key.push_back(p.pre);
+    key.push_back(p.nxt);
+    key.push_back(p.q->heads);
+    key.push_back(p.q->dtype == FA_F32 ? 1 : 0);
+    key.insert(key.end(), p.cu_q, p.cu_q + p.batch + 1);
+    key.insert(key.end(), p.cu_kv, p.cu_kv + p.batch + 1);
+    return key;
+}
+
+void build_bwd_lists(const BwdPlan& p, std::vector<fa_work_item_t>& items, int64_t& n_first) {
+    const bool wide = p.q->dtype == FA_F32;
+    std::vector<fa_work_item_t> qlist;
+    if (wide) {
+        build_worklist(p.cu_q, p.cu_kv, p.batch, p.mode, p.pre, p.nxt, p.q->heads, FA_ITEMS_KEY_BLOCKS,
+                       kBlockKv32, kTileQ32, items);
+        build_worklist(p.cu_q, p.cu_kv, p.batch, p.mode, p.pre, p.nxt, p.q->heads, FA_ITEMS_QUERY_BLOCKS,
+                       FA32_FWD_BLOCK, FA32_FWD_BLOCK, qlist);
+    } else {
+        build_worklist(p.cu_q, p.cu_kv, p.batch, p.mode, p.pre, p.nxt, p.q->heads, FA_ITEMS_KEY_BLOCKS,
+                       FA16_DKDV_BLOCK, FA16_DKDV_TILE_Q, items);
+        build_worklist(p.cu_q, p.cu_kv, p.batch, p.mode, p.pre, p.nxt, p.q->heads, FA_ITEMS_QUERY_BLOCKS,
+                       FA16_DQ_BLOCK, FA16_DQ_TILE_K, qlist);
+    }
+    n_first = static_cast<int64_t>(items.size());
+    items.insert(items.end(), qlist.begin(), qlist.end());
+}
+
+size_t bwd_rowstat_bytes(const BwdPlan& p) {
+    return static_cast<size_t>(p.q->tokens * p.q->heads) * 2 * sizeof(float);
+}
+
+}  // namespace fa
+
+namespace fa {
+
+hipError_t launch_bwd(const BwdPlan& p, const fa_work_item_t* items, int64_t n_kv, int64_t n_q, float* rowstat,
+                      hipStream_t s, const char** what) {
+    const fa_tensor_t *q = p.q, *k = p.k, *v = p.v, *dy = p.dy, *y = p.y, *dq = p.dq, *dk = p.dk, *dv = p.dv;
+    const float* softmax_max = p.softmax_max;
+    const float* softmax_sum = p.softmax_sum;
+    const double keep_prob = p.keep_prob;
+    const uint8_t* drop_mask = p.drop_mask;
+    const fa_mask_t* atten_mask = p.atten_mask;
+    const double scale = p.scale;
+    const int64_t batch = p.batch;
+    const int64_t pre = p.pre;
+    const int64_t nxt = p.nxt;
     const int64_t tq = q->tokens;
     const int64_t heads = q->heads;
     const int d = static_cast<int>(q->head_dim);
     const int dv_dim = static_cast<int>(v->head_dim);
-    if (tq == 0) return FA_OK;  // empty input: nothing to compute
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t dtype = q->dtype;
     const bool wide = dtype == FA_F32;  // fp32 runs its own dK/dV and dQ kernels
-    const int64_t pre = atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0;
-    const int64_t nxt = atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0;
-
-    std::lock_guard<std::mutex> lock(g_mutex);
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return runtime_error("hipGetDevice", e);
-    Workspace& ws = g_ws[dev];
-
-    // work lists, rebuilt only when the sequence layout, mask or path changes:
-    // key-block items first, then (16-bit path) query-block items
-    std::vector<int64_t> key;
-    key.reserve(2 * (batch + 1) + 5);
-    key.push_back(atten_mode);
-    key.push_back(pre);
-    key.push_back(nxt);
-    key.push_back(heads);
-    key.push_back(wide ? 1 : 0);
-    key.insert(key.end(), cu_seqlens_q->cu, cu_seqlens_q->cu + batch + 1);
-    key.insert(key.end(), cu_seqlens_kv->cu, cu_seqlens_kv->cu + batch + 1);
-    if (key != ws.key) {
-        std::vector<fa_work_item_t> list, qlist;
-        if (wide) {
-            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
-                               FA_ITEMS_KEY_BLOCKS, fa::kBlockKv32, fa::kTileQ32, list);
-            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
-                               FA_ITEMS_QUERY_BLOCKS, fa::FA32_FWD_BLOCK, fa::FA32_FWD_BLOCK, qlist);
-        } else {
-            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
-                               FA_ITEMS_KEY_BLOCKS, fa::FA16_DKDV_BLOCK, fa::FA16_DKDV_TILE_Q, list);
-            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
-                               FA_ITEMS_QUERY_BLOCKS, fa::FA16_DQ_BLOCK, fa::FA16_DQ_TILE_K, qlist);
-        }
-        const int64_t n_kv = static_cast<int64_t>(list.size());
-        const int64_t n_q = static_cast<int64_t>(qlist.size());
-        list.insert(list.end(), qlist.begin(), qlist.end());
-        const int64_t n = n_kv + n_q;
-        size_t cap_bytes = ws.items_cap * sizeof(fa_work_item_t);
-        void* ptr = ws.items;
-        int g = grow(&ptr, &cap_bytes, static_cast<size_t>(n) * sizeof(fa_work_item_t), "work list");
-        ws.items = static_cast<fa_work_item_t*>(ptr);
-        ws.items_cap = cap_bytes / sizeof(fa_work_item_t);
-        if (g != FA_OK) {
-            ws.key.clear();
-            return g;
-        }
-        if (n > 0) {
-            // The previous list may still be read by kernels queued on this
-            // stream; wait for them, then copy synchronously (lists are small
-            // and reused by later calls with the same layout).
-            e = hipStreamSynchronize(s);
-            if (e != hipSuccess) {
-                ws.key.clear();
-                return runtime_error("stream synchronize", e);
-            }
-            e = hipMemcpy(ws.items, list.data(), static_cast<size_t>(n) * sizeof(fa_work_item_t),
-                          hipMemcpyHostToDevice);
-            if (e != hipSuccess) {
-                ws.key.clear();
-                return runtime_error("work list upload", e);
-            }
-        }
-        ws.key = key;
-        ws.n_items = n_kv;
-        ws.n_q_items = n_q;
-    }
-
-    {
-        void* ptr = ws.rowstat;
-        int g = grow(&ptr, &ws.rowstat_bytes, static_cast<size_t>(tq * heads) * 2 * sizeof(float), "row statistics");
-        ws.rowstat = static_cast<float*>(ptr);
-        if (g != FA_OK) return g;
-    }
-
-    fa::TensorArg tdy{dy->data, dy->stride_t, dy->stride_h};
-    fa::TensorArg ty{y->data, y->stride_t, y->stride_h};
+    hipError_t e = hipSuccess;
+    TensorArg tdy{dy->data, dy->stride_t, dy->stride_h};
+    TensorArg ty{y->data, y->stride_t, y->stride_h};
 
     const float exp_scale = static_cast<float>(scale * 1.4426950408889634);
     const float inv_keep = static_cast<float>(1.0 / keep_prob);
     if (!wide) {
-        fa::Bwd16Args a;
+        Bwd16Args a;
         a.q = q->data;
         a.k = k->data;
         a.v = v->data;
@@ -453,49 +410,58 @@ extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
         a.dk_sh = dk->stride_h;
         a.dv_st = dv->stride_t;
         a.dv_sh = dv->stride_h;
-        a.rowstat = ws.rowstat;
+        a.rowstat = rowstat;
         a.y = y->data;
         a.y_st = y->stride_t;
         a.y_sh = y->stride_h;
         a.softmax_max = softmax_max;
         a.softmax_sum = softmax_sum;
-        a.items_kv = ws.items;
-        a.items_q = ws.items + ws.n_items;
+        a.items_kv = items;
+        a.items_q = items + n_kv;
         a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
         {
             // the bit stream holds heads * Lq_b * Lkv_b bits per sequence
             int64_t bits = 0;
             for (int64_t b = 0; b < batch; ++b)
-                bits += heads * (cu_seqlens_q->cu[b + 1] - cu_seqlens_q->cu[b]) *
-                        (cu_seqlens_kv->cu[b + 1] - cu_seqlens_kv->cu[b]);
+                bits += heads * (p.cu_q[b + 1] - p.cu_q[b]) *
+                        (p.cu_kv[b + 1] - p.cu_kv[b]);
             a.drop_bytes = keep_prob < 1.0 ? (bits + 7) / 8 : 0;
         }
         a.tq = static_cast<int32_t>(tq);
         a.heads = static_cast<int32_t>(heads);
         a.group = static_cast<int32_t>(heads / k->heads);
-        a.mode = atten_mode;
+        a.mode = p.mode;
         a.pre = static_cast<int32_t>(pre);
         a.nxt = static_cast<int32_t>(nxt);
         a.exp_scale = exp_scale;
         a.inv_keep = inv_keep;
         a.scale = static_cast<float>(scale);
-        fa::set_mask(a, atten_mask);
+        set_mask(a, atten_mask);
         const bool xm = atten_mask != nullptr;
         // the dQ kernel also writes the row statistics planes (no separate row pass on this path);
         // the dK/dV kernel reads them, so it runs second
-        e = timed(3, s, [&] { return fa::launch_dq16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, ws.n_q_items, s); });
-        if (e != hipSuccess) return runtime_error("dQ kernel launch", e);
-        e = timed(1, s, [&] { return fa::launch_dkdv16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, ws.n_items, s); });
-        if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
-        return FA_OK;
+        e = timed(3, s, [&] { return launch_dq16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, n_q, s); });
+        if (e != hipSuccess) {
+            *what = "dQ kernel launch";
+            return e;
+        }
+        e = timed(1, s, [&] { return launch_dkdv16(dtype, d, dv_dim, keep_prob < 1.0, xm, a, n_kv, s); });
+        if (e != hipSuccess) {
+            *what = "dK/dV kernel launch";
+            return e;
+        }
+        return hipSuccess;
     }
 
     e = timed(0, s, [&] {
-        return fa::launch_preprocess(dtype, dv_dim, tdy, ty, softmax_max, softmax_sum, ws.rowstat, tq, heads, s);
+        return launch_preprocess(dtype, dv_dim, tdy, ty, softmax_max, softmax_sum, rowstat, tq, heads, s);
     });
-    if (e != hipSuccess) return runtime_error("preprocess launch", e);
+    if (e != hipSuccess) {
+            *what = "preprocess launch";
+            return e;
+        }
 
-    fa::MainArgs a;
+    MainArgs a;
     a.q = {q->data, q->stride_t, q->stride_h};
     a.k = {k->data, k->stride_t, k->stride_h};
     a.v = {v->data, v->stride_t, v->stride_h};
@@ -509,25 +475,71 @@ extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
     a.dv = dv->data;
     a.dv_st = dv->stride_t;
     a.dv_sh = dv->stride_h;
-    a.rowstat = ws.rowstat;
-    a.items = ws.items;
-    a.items_q = ws.items + ws.n_items;
+    a.rowstat = rowstat;
+    a.items = items;
+    a.items_q = items + n_kv;
     a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
     a.tq = static_cast<int32_t>(tq);
     a.heads = static_cast<int32_t>(heads);
     a.group = static_cast<int32_t>(heads / k->heads);
-    a.mode = atten_mode;
+    a.mode = p.mode;
     a.pre = static_cast<int32_t>(pre);
     a.nxt = static_cast<int32_t>(nxt);
     a.exp_scale = exp_scale;
     a.inv_keep = inv_keep;
     a.scale = static_cast<float>(scale);
-    fa::set_mask(a, atten_mask);
-    e = timed(1, s, [&] { return fa::launch_main(dtype, d, dv_dim, keep_prob < 1.0, a, ws.n_items, s); });
-    if (e != hipSuccess) return runtime_error("dK/dV kernel launch", e);
-    e = timed(3, s, [&] { return fa::launch_dq32(d, dv_dim, keep_prob < 1.0, a, ws.n_q_items, s); });
-    if (e != hipSuccess) return runtime_error("dQ kernel launch", e);
-    return FA_OK;
+    set_mask(a, atten_mask);
+    e = timed(1, s, [&] { return launch_main(dtype, d, dv_dim, keep_prob < 1.0, a, n_kv, s); });
+    if (e != hipSuccess) {
+            *what = "dK/dV kernel launch";
+            return e;
+        }
+    e = timed(3, s, [&] { return launch_dq32(d, dv_dim, keep_prob < 1.0, a, n_q, s); });
+    if (e != hipSuccess) {
+            *what = "dQ kernel launch";
+            return e;
+        }
+    return hipSuccess;
+}
+
+}  // namespace fa
+
+extern "C" int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                                    const fa_tensor_t* dy, const fa_tensor_t* y, const float* softmax_max,
+                                    const float* softmax_sum, const fa_seqlens_t* cu_seqlens_q,
+                                    const fa_seqlens_t* cu_seqlens_kv, int32_t atten_mode, int64_t pre_tokens,
+                                    int64_t next_tokens, double keep_prob, const uint8_t* drop_mask,
+                                    const fa_mask_t* atten_mask, double scale, int64_t head_num,
+                                    const fa_tensor_t* dq, const fa_tensor_t* dk, const fa_tensor_t* dv,
+                                    void* stream) {
+    fa::BwdPlan plan;
+    int st = fa::plan_bwd(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
+                          pre_tokens, next_tokens, keep_prob, drop_mask, atten_mask, scale, head_num, dq, dk, dv,
+                          &plan);
+    if (st != FA_OK) return st;
+    if (q->tokens == 0) return FA_OK;  // empty input: nothing to compute
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(fa::state_mutex());
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return runtime_error("hipGetDevice", e);
+    const fa::CaptureInfo ci = fa::capture_info(s);
+    fa::ListRef list;
+    st = fa::acquire_list(
+        dev, fa::bwd_list_key(plan),
+        [&](std::vector<fa_work_item_t>& items, int64_t& n_first) { fa::build_bwd_lists(plan, items, n_first); }, s,
+        ci, &list);
+    if (st != FA_OK) return st;
+    float* rowstat = nullptr;
+    st = fa::acquire_rowstat(dev, s, fa::bwd_rowstat_bytes(plan), ci, &rowstat);
+    if (st != FA_OK) return st;
+    const char* what = "";
+    e = fa::launch_bwd(plan, list.items, list.n_first, list.n_second, rowstat, s, &what);
+    // the list is noted as used even after a failed launch: an earlier kernel may have been enqueued
+    st = fa::note_list_use(dev, list, s, ci);
+    if (e != hipSuccess) return runtime_error(what, e);
+    return st;
 }
 
 // Forward: validation as in the backward (same page constraints, same codes), then one kernel
@@ -671,14 +683,14 @@ extern "C" int fa_varlen_fwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
     const int64_t pre = atten_mode == FA_MASK_BAND ? fa::clamp_window(pre_tokens) : 0;
     const int64_t nxt = atten_mode == FA_MASK_BAND ? fa::clamp_window(next_tokens) : 0;
 
-    std::lock_guard<std::mutex> lock(g_mutex);
+    std::lock_guard<std::mutex> lock(fa::state_mutex());
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return runtime_error("hipGetDevice", e);
-    Workspace& ws = g_ws[dev];
-
+    const fa::CaptureInfo ci = fa::capture_info(s);
     std::vector<int64_t> key;
-    key.reserve(2 * (batch + 1) + 5);
+    key.reserve(2 * (batch + 1) + 6);
+    key.push_back(1);  // forward list
     key.push_back(atten_mode);
     key.push_back(pre);
     key.push_back(nxt);
@@ -686,37 +698,17 @@ extern "C" int fa_varlen_fwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
     key.push_back(wide ? 1 : 0);
     key.insert(key.end(), cu_seqlens_q->cu, cu_seqlens_q->cu + batch + 1);
     key.insert(key.end(), cu_seqlens_kv->cu, cu_seqlens_kv->cu + batch + 1);
-    if (key != ws.fwd_key) {
-        std::vector<fa_work_item_t> list;
-        fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
-                           FA_ITEMS_QUERY_BLOCKS, wide ? fa::FA32_FWD_BLOCK : fa::FA16_DQ_BLOCK,
-                           wide ? fa::FA32_FWD_BLOCK : fa::FA16_DQ_TILE_K, list);
-        const int64_t n = static_cast<int64_t>(list.size());
-        size_t cap_bytes = ws.fwd_items_cap * sizeof(fa_work_item_t);
-        void* ptr = ws.fwd_items;
-        int g = grow(&ptr, &cap_bytes, static_cast<size_t>(n) * sizeof(fa_work_item_t), "forward work list");
-        ws.fwd_items = static_cast<fa_work_item_t*>(ptr);
-        ws.fwd_items_cap = cap_bytes / sizeof(fa_work_item_t);
-        if (g != FA_OK) {
-            ws.fwd_key.clear();
-            return g;
-        }
-        if (n > 0) {
-            e = hipStreamSynchronize(s);
-            if (e != hipSuccess) {
-                ws.fwd_key.clear();
-                return runtime_error("stream synchronize", e);
-            }
-            e = hipMemcpy(ws.fwd_items, list.data(), static_cast<size_t>(n) * sizeof(fa_work_item_t),
-                          hipMemcpyHostToDevice);
-            if (e != hipSuccess) {
-                ws.fwd_key.clear();
-                return runtime_error("forward work list upload", e);
-            }
-        }
-        ws.fwd_key = key;
-        ws.n_fwd_items = n;
-    }
+    fa::ListRef list;
+    st = fa::acquire_list(
+        dev, key,
+        [&](std::vector<fa_work_item_t>& items, int64_t& n_first) {
+            fa::build_worklist(cu_seqlens_q->cu, cu_seqlens_kv->cu, batch, atten_mode, pre, nxt, heads,
+                               FA_ITEMS_QUERY_BLOCKS, wide ? fa::FA32_FWD_BLOCK : fa::FA16_DQ_BLOCK,
+                               wide ? fa::FA32_FWD_BLOCK : fa::FA16_DQ_TILE_K, items);
+            n_first = static_cast<int64_t>(items.size());
+        },
+        s, ci, &list);
+    if (st != FA_OK) return st;
 
     fa::FwdArgs a;
     a.q = q->data;
@@ -733,7 +725,7 @@ extern "C" int fa_varlen_fwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
     a.y_sh = y->stride_h;
     a.smax = softmax_max;
     a.ssum = softmax_sum;
-    a.items = ws.fwd_items;
+    a.items = list.items;
     a.drop_mask = keep_prob < 1.0 ? drop_mask : nullptr;
     a.drop_bytes = keep_prob < 1.0 ? (drop_bits + 7) / 8 : 0;
     a.tq = static_cast<int32_t>(tq);
@@ -747,10 +739,11 @@ extern "C" int fa_varlen_fwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
     a.inv_keep = static_cast<float>(1.0 / keep_prob);
     fa::set_mask(a, atten_mask);
     e = timed(4, s, [&] {
-        return wide ? fa::launch_fwd32(d, dv_dim, keep_prob < 1.0, a, ws.n_fwd_items, s)
+        return wide ? fa::launch_fwd32(d, dv_dim, keep_prob < 1.0, a, list.n_first, s)
                     : fa::launch_fwd16(dtype, d, dv_dim, keep_prob < 1.0, atten_mask != nullptr, a,
-                                       ws.n_fwd_items, s);
+                                       list.n_first, s);
     });
+    st = fa::note_list_use(dev, list, s, ci);
     if (e != hipSuccess) return runtime_error("forward kernel launch", e);
-    return FA_OK;
+    return st;
 }

@@ -42,4 +42,47 @@ int64_t build_worklist(const int64_t* cu_q, const int64_t* cu_kv, int64_t batch,
                        int64_t nxt, int64_t heads, int32_t kind, int32_t block_rows, int32_t tile_rows,
                        std::vector<fa_work_item_t>& out);
 
+// A validated backward call: the caller's arguments, with the window bounds clamped.  Pointers
+// are borrowed for the duration of the call.
+struct BwdPlan {
+    const fa_tensor_t* q = nullptr;
+    const fa_tensor_t* k = nullptr;
+    const fa_tensor_t* v = nullptr;
+    const fa_tensor_t* dy = nullptr;
+    const fa_tensor_t* y = nullptr;
+    const fa_tensor_t* dq = nullptr;
+    const fa_tensor_t* dk = nullptr;
+    const fa_tensor_t* dv = nullptr;
+    const float* softmax_max = nullptr;
+    const float* softmax_sum = nullptr;
+    const int64_t* cu_q = nullptr;
+    const int64_t* cu_kv = nullptr;
+    int64_t batch = 0;
+    int32_t mode = 0;
+    int64_t pre = 0;
+    int64_t nxt = 0;
+    double keep_prob = 1.0;
+    const uint8_t* drop_mask = nullptr;
+    const fa_mask_t* atten_mask = nullptr;
+    double scale = 1.0;
+};
+
+// Every check of fa_varlen_bwd_masked (null pointers, the page's constraints, what is not built);
+// FA_OK fills *plan.  No device work.
+int plan_bwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v, const fa_tensor_t* dy,
+             const fa_tensor_t* y, const float* softmax_max, const float* softmax_sum,
+             const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv, int32_t atten_mode,
+             int64_t pre_tokens, int64_t next_tokens, double keep_prob, const uint8_t* drop_mask,
+             const fa_mask_t* atten_mask, double scale, int64_t head_num, const fa_tensor_t* dq,
+             const fa_tensor_t* dk, const fa_tensor_t* dv, BwdPlan* plan);
+
+// What identifies the backward's work lists: layout, window, heads and kernel path.
+std::vector<int64_t> bwd_list_key(const BwdPlan& p);
+
+// The backward's key-block list (n_first items) followed by its query-block list.
+void build_bwd_lists(const BwdPlan& p, std::vector<fa_work_item_t>& items, int64_t& n_first);
+
+// Bytes of the two row-statistics planes (-D and -beta) of a call.
+size_t bwd_rowstat_bytes(const BwdPlan& p);
+
 }  // namespace fa
