@@ -19,7 +19,7 @@
  * Argument list and error classes follow the page's 函数原型 (prototypes),
  * 参数说明 (parameter table) and 返回值 (return codes) sections, collapsed
  * into one call: there is no separate workspace query, the library keeps its
- * own workspace (see fa_varlen_bwd).
+ * own workspace (see fa_varlen_bwd) or, in fa_varlen_bwd_noalloc, a fixed one.
  *
  * Ownership: the caller owns every tensor, both cu_seqlens arrays and the
  * stream.  Tensor and statistics pointers are DEVICE pointers; cu_seqlens
@@ -185,13 +185,41 @@ int fa_varlen_bwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, const fa_te
                          const fa_tensor_t* dq, const fa_tensor_t* dk, const fa_tensor_t* dv,
                          void* stream);
 
+/*
+ * fa_varlen_bwd_noalloc -- fa_varlen_bwd for callers that cannot allocate device memory (code
+ * that must not call hipMalloc: tight serving loops, harnesses that forbid allocation, stream
+ * capture).  Arguments, results, kernels and status codes are those of fa_varlen_bwd.
+ *
+ * Instead of library allocations it uses one fixed device array per GPU (50 MiB, held from
+ * the first call until the process ends): 48 MiB for the row statistics, i.e. at most
+ * 6,291,456 query token-heads (Tq * N), and 2 MiB for the work lists.  Larger inputs return
+ * FA_ERR_UNSUPPORTED before any device work.  It calls no allocating routine.
+ *
+ * Every call on a GPU shares that array: calls that overlap in time on one GPU (on different
+ * streams, or with fa_varlen_bwd_noalloc calls from other threads) race and give wrong
+ * results.  When the sequence layout differs from the previous call's on that GPU, the new work
+ * list is copied into the array and the host waits for `stream` to finish; a call with the same
+ * layout only enqueues kernels (it can then also be recorded into a HIP graph; a layout change
+ * while `stream` is being captured returns FA_ERR_UNSUPPORTED).
+ */
+int fa_varlen_bwd_noalloc(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
+                          const fa_tensor_t* dy, const fa_tensor_t* y,
+                          const float* softmax_max, const float* softmax_sum,
+                          const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,
+                          int32_t atten_mode, int64_t pre_tokens, int64_t next_tokens,
+                          double keep_prob, const uint8_t* drop_mask,
+                          double scale, int64_t head_num,
+                          const fa_tensor_t* dq, const fa_tensor_t* dk, const fa_tensor_t* dv,
+                          void* stream);
+
 /* Thread-local description of the last non-OK status (empty string if none). */
 const char* fa_last_error(void);
 
 /* Frees the library's cached work lists, staging memory and row-statistics
  * buffers, including those kept for captured graphs (synchronises every device
  * first; graphs that recorded calls must not be replayed afterwards).  The next
- * call re-allocates what it needs. */
+ * call re-allocates what it needs.  The fixed array of fa_varlen_bwd_noalloc is
+ * not affected. */
 void fa_release(void);
 
 /* One work item: a block of rows of one sequence that a workgroup keeps

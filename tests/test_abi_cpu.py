@@ -239,15 +239,30 @@ def _no_gpu():
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="needs a host without a GPU: the HIP runtime must fail")
-def test_hip_failure_is_reported_as_runtime_error():
+@pytest.mark.parametrize("entry", ["fa_varlen_bwd", "fa_varlen_bwd_noalloc"])
+def test_hip_failure_is_reported_as_runtime_error(entry):
     # a valid call on a host where the HIP runtime has no device: the first HIP call fails, and the
     # status is FA_ERR_RUNTIME with the runtime's message (nothing can have been launched)
-    st, msg = _call()
+    st, msg = _call(entry=entry)
     assert st == B.FA_ERR_RUNTIME, (st, msg)
     assert msg and "hipGetDevice" in msg, msg
     st, msg = _fwd()
     assert st == B.FA_ERR_RUNTIME, (st, msg)
     assert msg
+
+
+def test_noalloc_rejects_inputs_beyond_its_fixed_space():
+    # 2^20 tokens x 7 heads needs 56 MiB of row statistics, more than the fixed 48 MiB: refused
+    # before any device work, with a message naming the limit
+    t = 1 << 20
+    st, msg = _call(q=_t(t, heads=7), k=_t(t, heads=7), v=_t(t, heads=7), dy=_t(t, heads=7), y=_t(t, heads=7),
+                    dq=_t(t, heads=7), dk=_t(t, heads=7), dv=_t(t, heads=7), cu_q=(0, t), cu_kv=(0, t),
+                    head_num=7, entry="fa_varlen_bwd_noalloc")
+    assert st == B.FA_ERR_UNSUPPORTED, (st, msg)
+    assert "6291456" in msg, msg
+    # and the same validation as fa_varlen_bwd
+    assert _call(q=_t(10, data=0), entry="fa_varlen_bwd_noalloc")[0] == B.FA_ERR_NULLPTR
+    assert _call(kp=1.5, entry="fa_varlen_bwd_noalloc")[0] == B.FA_ERR_INVALID
 
 
 def test_missing_library_fails_loudly(tmp_path):

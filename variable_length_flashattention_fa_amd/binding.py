@@ -55,7 +55,7 @@ class FaError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ("fa_varlen_bwd", "fa_varlen_bwd_masked", "fa_varlen_fwd", "fa_varlen_fwd_masked", "fa_last_error",
+EXPORTS = ("fa_varlen_bwd", "fa_varlen_bwd_noalloc", "fa_varlen_bwd_masked", "fa_varlen_fwd", "fa_varlen_fwd_masked", "fa_last_error",
            "fa_release", "fa_varlen_worklist", "fa_profile_enable", "fa_profile_read")
 KERNEL_NAMES = ("preprocess", "bwd_main", "unused", "bwd_dq", "fwd")
 
@@ -75,6 +75,8 @@ def load(path: Optional[str] = None):
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p,
                                   ctypes.c_double, ctypes.c_int64, T, T, T, ctypes.c_void_p]
     lib.fa_varlen_bwd.restype = ctypes.c_int
+    lib.fa_varlen_bwd_noalloc.argtypes = lib.fa_varlen_bwd.argtypes
+    lib.fa_varlen_bwd_noalloc.restype = ctypes.c_int
     lib.fa_varlen_fwd.argtypes = [T, T, T, S, S, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                   ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, T, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
@@ -219,6 +221,16 @@ def fa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dy: torch.T
     """
     _bwd("fa_varlen_bwd", q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv, atten_mode,
          pre_tokens, next_tokens, keep_prob, drop_mask, scale, head_num, dq, dk, dv, stream)
+
+
+def fa_varlen_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dy: torch.Tensor,
+                          y: torch.Tensor, softmax_max: torch.Tensor, softmax_sum: torch.Tensor, cu_seqlens_q,
+                          cu_seqlens_kv, atten_mode: int, pre_tokens: int, next_tokens: int, keep_prob: float,
+                          drop_mask: Optional[torch.Tensor], scale: float, head_num: int, dq: torch.Tensor,
+                          dk: torch.Tensor, dv: torch.Tensor, stream=None) -> None:
+    """The C entry point of the same name (no device allocation); conventions of fa_varlen_bwd."""
+    _bwd("fa_varlen_bwd_noalloc", q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+         atten_mode, pre_tokens, next_tokens, keep_prob, drop_mask, scale, head_num, dq, dk, dv, stream)
 
 
 def fa_varlen_bwd_masked(q, k, v, dy, y, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,

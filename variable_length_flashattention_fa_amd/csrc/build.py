@@ -24,7 +24,7 @@ LIBNAME = "libfa_varlen.so"
 # dtype), in parallel.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 HIP_UNITS = [("fa_kernels.hip", "fa_kernels", []), ("fa_api.cpp", "fa_api", []),
-             ("fa_workspace.cpp", "fa_workspace", []),]
+             ("fa_workspace.cpp", "fa_workspace", []), ("fa_noalloc.hip", "fa_noalloc", [])]
 HIP_UNITS += [("fa_bwd16.hip", f"fa_bwd16_p{i}", _VGPR_FORM + [f"-DFA_BWD16_PART={i}"]) for i in (1, 2, 3, 4)]
 HIP_UNITS += [("fa_fwd.hip", f"fa_fwd_p{i}", _VGPR_FORM + [f"-DFA_FWD_PART={i}"]) for i in (1, 2)]
 HIP_SOURCES = sorted({u[0] for u in HIP_UNITS})
