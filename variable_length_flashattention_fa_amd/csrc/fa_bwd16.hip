@@ -120,6 +120,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     // Without dropout the dP chain of a step starts from -D of its rows, so that it ends with
     // dP - D; with dropout the keep bit scales dP but not D, and the chain starts from zero.
     constexpr bool FOLD_D = !DROP;
+    // Likewise the S chain starts from -beta of its rows, with this lane's K row scaled by
+    // scale * log2(e) (once, before rounding to the operand type), so that it ends with
+    // S * scale * log2(e) - beta and P = exp2(acc).  Its start block is read at the end of the step
+    // before.  With dropout or an explicit mask those registers are taken: the plain form stays.
+    constexpr bool FOLD_B = !DROP && !XM;
     // X slots: S (chain A) and dP (chain B); S leads by LA / 2 so that the start of the dP chain
     // (-D of the step's rows) can be read from LDS LA slots ahead, within the step
     // (with dropout the chain starts at zero and the plain alternation is kept)
@@ -133,13 +138,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     // buffer b: Q tile at sBuf[b], dY tile at sBuf[b] + TILEQ (one array, so that the reads of
     // both tiles share one base address and differ by an immediate offset)
     __shared__ __attribute__((aligned(16))) T sBuf[NB][TILEQ + TILED];
-    // row statistics of buffer b: sSt[b][0] = -D, sSt[b][1] = beta of the tile's rows
+    // row statistics of buffer b: sSt[b][0] = -D, sSt[b][1] = -beta of the tile's rows
     __shared__ __attribute__((aligned(16))) float sSt[NB][2][BQ];
     auto qtile = [&](int b) -> T* { return sBuf[b]; };
     auto dtile = [&](int b) -> T* { return sBuf[b] + TILEQ; };
 
-    const fa_work_item_t it = p.items_kv[blockIdx.x];
-    const int hk = blockIdx.y;  // key/value head; query heads hk * group .. hk * group + group - 1 read it
+    const Unit unit = wg_unit(p.xcd_group != 0);
+    const fa_work_item_t it = p.items_kv[unit.item];
+    const int hk = unit.head;  // key/value head; query heads hk * group .. hk * group + group - 1 read it
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
     const int lane = threadIdx.x & 63;
     const int col = lane & 31;
@@ -198,6 +204,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             }
 #pragma unroll
             for (int s = SV; s < SK; ++s) kreg[s] = ok ? kr[2 * s + h] : vec{};
+            if constexpr (FOLD_B) {
+#pragma unroll
+                for (int s = 0; s < SK; ++s) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        kreg[s][e] = static_cast<T>(static_cast<float>(kreg[s][e]) * p.exp_scale);
+                }
+            }
         }
 
         // Query rows this lane's key admits, [lo_row, hi_row]; the element of step rows q0s..
@@ -280,11 +294,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             }
         };
         // statistics of rows 32*sm + 8g + 4h + 0..3: dst[0] = -D (needed only with dropout),
-        // dst[1] = beta
+        // dst[1] = -beta
         auto read_stats = [&](const Where& wh, int g, f32x4* dst) {
             const int r = 32 * wh.sm + 8 * g + 4 * h;
             if constexpr (!FOLD_D) dst[0] = *reinterpret_cast<const f32x4*>(&sSt[wh.sb][0][r]);
-            dst[1] = *reinterpret_cast<const f32x4*>(&sSt[wh.sb][1][r]);
+            if constexpr (!FOLD_B) dst[1] = *reinterpret_cast<const f32x4*>(&sSt[wh.sb][1][r]);
+        };
+        // -beta of the X rows, in accumulator order: the start of the S chain
+        auto read_binit = [&](const Where& wh, f32x16& dst) {
+            if constexpr (FOLD_B) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(&sSt[wh.xb][1][32 * wh.xm + 8 * g + 4 * h]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[4 * g + r] = v[r];
+                }
+            }
         };
         // -D of the X rows 32*xm + 4h + 8*(a/4) + a%4, in accumulator order: the start of the dP chain
         auto read_dinit = [&](const Where& wh, f32x16& dst) {
@@ -301,6 +326,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         // pipeline state carried from step to step
         vec opr[NOPS];         // operand of each slot, read LA slots ahead
         f32x4 stC[4][2];       // statistics of the softmax rows of the step
+        f32x16 bC = zero16();  // start of this step's S chain (-beta of its X rows, or zero)
         f32x16 sC = zero16();  // S and dP consumed by this step's softmax gradient
         f32x16 pC = zero16();
         vec pkY[2];            // packed P and dS consumed by this step's Y (two 16-row halves)
@@ -334,6 +360,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             f32x16 sN = zero16();
             f32x16 pN = zero16();
             f32x16 dX = zero16();  // start of this step's dP chain (-D of its X rows, or zero)
+            f32x16 bN = zero16();  // start of the next step's S chain
             uint32_t pkw[2][4];
             uint32_t dsw[2][4];
             vec nopr[LA];
@@ -374,7 +401,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                         vec a = opr[k];
                         pin(a);
                         if constexpr (XS::is_a(j)) {
-                            sN = Op16<T>::mfma(a, kreg[s], s == 0 ? zero16() : sN);
+                            sN = Op16<T>::mfma(a, kreg[s], s == 0 ? (FOLD_B ? bC : zero16()) : sN);
                             pin(sN);
                         } else {
                             pN = Op16<T>::mfma(a, vreg[s], s == 0 ? dX : pN);
@@ -399,8 +426,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     if constexpr (p_slot(a, NOPS) == k) {
                         float x = sC[a];
                         pin(x);
-                        const float bt = stC[a / 4][1][a % 4];
-                        const float e = __builtin_amdgcn_exp2f(x * p.exp_scale - bt);
+                        float e;
+                        if constexpr (FOLD_B) {
+                            e = __builtin_amdgcn_exp2f(x);  // x = S * scale * log2(e) - beta
+                        } else {
+                            e = __builtin_amdgcn_exp2f(x * p.exp_scale + stC[a / 4][1][a % 4]);
+                        }
                         if constexpr (MASKED) {
                             bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(rng);
                             if constexpr (XM) adm = adm && mkC[a] == 0;
@@ -461,6 +492,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 } else if constexpr (KIND != kStepLast) {
                     nopr[kr - NOPS] = read_op(nw, IC<kr - NOPS>{});
                     if constexpr (kr == NOPS && (NKIND == kStepA || NKIND == kStepB)) read_stats(nw, 0, stN);
+                    if constexpr (kr == NOPS && NKIND != kStepLast) read_binit(nw, bN);
                 }
                 // ---- dropout mask byte of X element k
                 if constexpr (DROP && HX && k < 16) {
@@ -506,6 +538,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             if constexpr (KIND != kStepLast) {
 #pragma unroll
                 for (int i = 0; i < LA; ++i) opr[i] = nopr[i];
+                if constexpr (FOLD_B && NKIND != kStepLast) bC = bN;
                 if constexpr (NKIND == kStepA || NKIND == kStepB) {
                     stC[0][0] = stN[0];
                     stC[0][1] = stN[1];
@@ -566,6 +599,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             __syncthreads();
             {
                 const Where w0 = where(kStepFirst, 0);
+                read_binit(w0, bC);
                 static_for<0, LA>([&](auto kc) {
                     if constexpr (decltype(kc)::value % 2 == 0) opr[decltype(kc)::value] = read_op(w0, kc);
                 });
@@ -643,8 +677,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     __shared__ __attribute__((aligned(16))) T sK[2][BK * DK];
     __shared__ __attribute__((aligned(16))) T sV[2][BK * DV];
 
-    const fa_work_item_t it = p.items_q[blockIdx.x];
-    const int n = blockIdx.y;
+    const Unit unit = wg_unit(p.xcd_group != 0);
+    const fa_work_item_t it = p.items_q[unit.item];
+    const int n = unit.head;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
     const int lane = threadIdx.x & 63;
     const int col = lane & 31;
@@ -717,7 +752,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             beta = p.softmax_max[8 * o] * 1.4426950408889634f + __builtin_amdgcn_logf(p.softmax_sum[8 * o]);
             if (h == 0) {
                 p.rowstat[o] = ndelta;
-                p.rowstat[static_cast<int64_t>(p.heads) * p.tq + o] = beta;
+                p.rowstat[static_cast<int64_t>(p.heads) * p.tq + o] = -beta;
             }
         }
     }
@@ -762,6 +797,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     f32x16 pinit;
 #pragma unroll
     for (int i = 0; i < 16; ++i) pinit[i] = FOLD_D ? ndelta : 0.f;
+    // Without dropout the S^T chain, too, does the softmax's affine step: the lane's Q row is
+    // scaled by scale * log2(e) (once, before rounding to the operand type) and the chain starts
+    // from -beta, so it ends with S * scale * log2(e) - beta and P = exp2(acc) needs no multiply.
+    // (With dropout or an explicit mask the registers are not there; the plain form stays.)
+    constexpr bool FOLD_B = !DROP && !XM;
+    f32x16 sinit;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sinit[i] = FOLD_B ? -beta : 0.f;
+    if constexpr (FOLD_B) {
+#pragma unroll
+        for (int s = 0; s < SK; ++s) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qreg[s][e] = static_cast<T>(static_cast<float>(qreg[s][e]) * p.exp_scale);
+        }
+    }
 
     // bit offset of this lane's query row from the wave's first row in the dropout stream
     const uint32_t drow = static_cast<uint32_t>(col) * static_cast<uint32_t>(K);
@@ -809,7 +859,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             win = __builtin_amdgcn_alignbit(hi, lo, lb & 7);
         };
         if constexpr (DROP && !XM) load_window();
-        f32x16 accS = zero16();
+        f32x16 accS = sinit;
         f32x16 accP = pinit;
 #pragma unroll
         for (int s = 0; s < SV; ++s) {
@@ -836,7 +886,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int cc = 8 * ((a + e) >> 2) + ((a + e) & 3);
-                    float pv = __builtin_amdgcn_exp2f(accS[a + e] * p.exp_scale - beta);
+                    float pv = FOLD_B ? __builtin_amdgcn_exp2f(accS[a + e])
+                                      : __builtin_amdgcn_exp2f(accS[a + e] * p.exp_scale - beta);
                     if constexpr (MASKED) {
                         bool adm = static_cast<unsigned>(cc - lo_h) <= static_cast<unsigned>(krng);
                         if constexpr (XM) adm = adm && mk[a + e] == 0;
@@ -904,17 +955,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 
 // ------------------------------------------------------------------------------------------------
 
+constexpr bool kXcdGrouping = true;  // whole heads per XCD when the head count allows (wg_unit)
+
 template <typename T, int DK, int DV, bool DROP, bool XM>
 static hipError_t launch_dkdv_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
+    Bwd16Args g = a;
+    g.xcd_group = kXcdGrouping && (a.heads / a.group) % 8 == 0;
     bwd_dkdv16_kernel<T, DK, DV, DROP, XM>
-        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads / a.group)), dim3(256), 0, stream>>>(a);
+        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads / a.group)), dim3(256), 0, stream>>>(g);
     return hipGetLastError();
 }
 
 template <typename T, int DK, int DV, bool DROP, bool XM>
 static hipError_t launch_dq_t(const Bwd16Args& a, int64_t n, hipStream_t stream) {
+    Bwd16Args g = a;
+    g.xcd_group = kXcdGrouping && a.heads % 8 == 0;
     bwd_dq16_kernel<T, DK, DV, DROP, XM>
-        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
+        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(g);
     return hipGetLastError();
 }
 

@@ -337,6 +337,25 @@ __device__ __forceinline__ uint32_t tile_bytes(int valid, int rows, int64_t st) 
 }
 
 
+// The (item, head) unit of this workgroup.  The hardware deals workgroups to the eight XCDs in
+// turn (linear id x + y * gridDim.x; XCD = id % 8), and each XCD has its own L2.  With `grouped`
+// (the host sets it when gridDim.y is a multiple of 8), XCD k runs the contiguous range k of the
+// head-major order -- whole heads, each with its items in the work list's longest-first order --
+// so the workgroups that read the same tiles of one (sequence, head) share an L2.  Without it the
+// unit is (blockIdx.x, blockIdx.y).
+struct Unit {
+    int item;
+    int head;
+};
+__device__ __forceinline__ Unit wg_unit(bool grouped) {
+    if (!grouped) return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y)};
+    const unsigned nx = gridDim.x;
+    const unsigned g = blockIdx.x + blockIdx.y * nx;
+    const unsigned per = (nx * gridDim.y) >> 3;
+    const unsigned u = (g & 7u) * per + (g >> 3);
+    return {static_cast<int>(u % nx), static_cast<int>(u / nx)};
+}
+
 template <int V>
 using IC = std::integral_constant<int, V>;
 

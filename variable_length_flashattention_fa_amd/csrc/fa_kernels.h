@@ -38,8 +38,8 @@ struct TensorArg {
 
 // Row pass: D[n, t] = sum_d dY * Y (fp32, over V's head dim) and beta[n, t] = max*log2(e) +
 // log2(sum).  rowstat holds two planes of heads * tq floats: rowstat[n * tq + t] = -D[n, t]
-// (negated: the kernels start their dP accumulators from it) and
-// rowstat[heads * tq + n * tq + t] = beta[n, t].
+// and rowstat[heads * tq + n * tq + t] = -beta[n, t] (both negated: the kernels start their dP
+// and S accumulators from them).
 hipError_t launch_preprocess(int32_t dtype, int head_dim_v, TensorArg dy, TensorArg y,
                              const float* softmax_max, const float* softmax_sum, float* rowstat,
                              int64_t tq, int64_t heads, hipStream_t stream);
@@ -52,7 +52,7 @@ struct MainArgs {
     int64_t dk_st, dk_sh;
     void* dv;
     int64_t dv_st, dv_sh;
-    const float* rowstat;  // planes of -D and beta (see launch_preprocess)
+    const float* rowstat;  // planes of -D and -beta (see launch_preprocess)
     const fa_work_item_t* items;    // key-block items (kBlockKv32 keys, kTileQ32 query tiles)
     const fa_work_item_t* items_q;  // query-block items (FA32_FWD_BLOCK queries)
     const uint8_t* drop_mask;
@@ -95,7 +95,7 @@ struct Bwd16Args {
     void* dk;
     void* dv;
     int64_t dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh;
-    // planes of -D and beta (layout as in launch_preprocess): written by the dQ kernel, which computes
+    // planes of -D and -beta (layout as in launch_preprocess): written by the dQ kernel, which computes
     // them for its rows from dY, Y and the forward statistics, and read by the dK/dV kernel after it
     float* rowstat;
     const void* y;
@@ -109,6 +109,7 @@ struct Bwd16Args {
     MaskArg mask;
     int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float exp_scale, inv_keep, scale;
+    int32_t xcd_group;  // renumber workgroups so each XCD runs whole heads (see wg_unit); set per launch
 };
 
 // dK/dV kernel over n_items key-block items x key/value heads (each sums its group of query heads).

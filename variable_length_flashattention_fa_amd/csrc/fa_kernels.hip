@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ d
         const float sm = ssum[s];
         const int64_t o = static_cast<int64_t>(n) * tq + t;
         rowstat[o] = -part;
-        rowstat[static_cast<int64_t>(heads) * tq + o] = mx * kLog2e + __builtin_amdgcn_logf(sm);
+        rowstat[static_cast<int64_t>(heads) * tq + o] = -(mx * kLog2e + __builtin_amdgcn_logf(sm));
     }
 }
 
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const DevArgs p) {
                 const int qi = q0 + tid;
                 const int64_t o = static_cast<int64_t>(n) * p.tq + it.q_start + qi;
                 const int64_t plane = static_cast<int64_t>(p.heads) * p.tq;
-                sStat[tid] = qi < L ? make_float2(-p.rowstat[o], p.rowstat[plane + o]) : make_float2(0.f, 0.f);
+                sStat[tid] = qi < L ? make_float2(-p.rowstat[o], -p.rowstat[plane + o]) : make_float2(0.f, 0.f);
             }
             __syncthreads();
 
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(2 * FA32_FWD_BLOCK) void bwd_dq32_kernel(const DevA
 #pragma unroll
     for (int d = 0; d < HV; ++d) dyr[d] = dy[d];
     const int64_t so = static_cast<int64_t>(n) * p.tq + row;
-    const float2 st = make_float2(-p.rowstat[so], p.rowstat[static_cast<int64_t>(p.heads) * p.tq + so]);  // {D_i, beta_i}
+    const float2 st = make_float2(-p.rowstat[so], -p.rowstat[static_cast<int64_t>(p.heads) * p.tq + so]);  // {D_i, beta_i}
     const int64_t bit0 = it.drop_base + (static_cast<int64_t>(n) * L + qi) * K;
     // this query's row of the explicit mask, if any (both lanes of the query skip the same keys)
     const uint8_t* mrow = p.mask.amask == nullptr
