@@ -40,8 +40,9 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     __shared__ __attribute__((aligned(16))) T sK[2][BK * DK];
     __shared__ __attribute__((aligned(16))) T sV[2][BK * DV];
 
-    const fa_work_item_t it = p.items[blockIdx.x];
-    const int n = blockIdx.y;
+    const Unit unit = wg_unit(p.xcd_group != 0);
+    const fa_work_item_t it = p.items[unit.item];
+    const int n = unit.head;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int col = lane & 31;
@@ -370,8 +371,10 @@ __global__ __launch_bounds__(FA32_FWD_BLOCK) void fwd32_kernel(const FwdArgs p) 
 
 template <typename T, int DK, int DV, bool DROP, bool XM>
 static hipError_t launch_fwd16_t(const FwdArgs& a, int64_t n, hipStream_t stream) {
+    FwdArgs g = a;
+    g.xcd_group = a.heads % 8 == 0;  // whole heads per XCD (wg_unit)
     fwd16_kernel<T, DK, DV, DROP, XM>
-        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(a);
+        <<<dim3(static_cast<unsigned>(n), static_cast<unsigned>(a.heads)), dim3(512), 0, stream>>>(g);
     return hipGetLastError();
 }
 

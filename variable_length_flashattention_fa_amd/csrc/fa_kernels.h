@@ -139,6 +139,7 @@ struct FwdArgs {
     MaskArg mask;
     int32_t tq, heads, group, mode, pre, nxt;  // heads: query heads; group: query heads per key/value head
     float scale, exp_scale, inv_keep;
+    int32_t xcd_group;  // renumber workgroups so each XCD runs whole heads (see wg_unit); set per launch
 };
 
 // bf16 / fp16 forward over n_items query-block items (FA16_DQ_BLOCK queries, FA16_DQ_TILE_K tiles).
