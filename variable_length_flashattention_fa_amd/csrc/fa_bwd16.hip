@@ -23,9 +23,10 @@
 // so that each query row's dQ has a single owner: no cross-workgroup reduction.
 //
 // Tiles move HBM -> LDS with buffer loads that write LDS directly (16 bytes per
-// lane, lane l at byte 16*l of a 1 KiB run).  Rows are unpadded; the 16-byte
-// chunks of a row are XOR-swizzled so that the row reads (one row per lane) and
-// the transposing reads (four rows per 16 lanes) hit distinct banks.
+// lane, lane l at byte 16*l of a 1 KiB run).  The runs are laid out (Tile) so that
+// the row reads (one row per lane) and the transposing reads (four rows per 16
+// lanes) hit distinct banks, and so that each lane reads a whole tile from one
+// address register plus instruction offsets.
 #include "fa_device.h"
 
 namespace fa {
@@ -135,13 +136,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     static_assert(BQ == 64 && BKV == 32 * NW && (TILED / 8 / 64) % NW == 0 && NOPS >= 16 && LA % 2 == 0 &&
                   LA < NOPS && DV <= DK && KD >= LA, "tile shape");
 
-    // buffer b: Q tile at sBuf[b], dY tile at sBuf[b] + TILEQ (one array, so that the reads of
+    // buffer b: Q tile at sBuf[b], dY tile at sBuf[b] + TEQ (one array, so that the reads of
     // both tiles share one base address and differ by an immediate offset)
-    __shared__ __attribute__((aligned(16))) T sBuf[NB][TILEQ + TILED];
+    constexpr int TEQ = Tile<DK>::kElems;  // LDS values a Q tile spans (see Tile)
+    constexpr int TED = Tile<DV>::kElems;
+    __shared__ __attribute__((aligned(16))) T sBuf[NB][TEQ + TED];
     // row statistics of buffer b: sSt[b][0] = -D, sSt[b][1] = -beta of the tile's rows
     __shared__ __attribute__((aligned(16))) float sSt[NB][2][BQ];
     auto qtile = [&](int b) -> T* { return sBuf[b]; };
-    auto dtile = [&](int b) -> T* { return sBuf[b] + TILEQ; };
+    auto dtile = [&](int b) -> T* { return sBuf[b] + TEQ; };
 
     const Unit unit = wg_unit(p.xcd_group != 0);
     const fa_work_item_t it = p.items_kv[unit.item];
@@ -166,11 +169,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     for (int i = 0; i < NTV; ++i) accV[i] = zero16();
 
     if (tb < te) {
-        LdsOffsets<DK> loQ;
+        Tile<DK> loQ;
         loQ.init(lane);
-        LdsOffsets<DV> loD_;
+        Tile<DV> loD_;
         if constexpr (DK != DV) loD_.init(lane);
-        const LdsOffsets<DV>& loD = offsets_for(loQ, loD_);
+        const Tile<DV>& loD = tile_for(loQ, loD_);
 
         // the query head being walked (set per head below), its tensors and (XM) its block of the
         // explicit mask
@@ -182,12 +185,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         __amdgpu_buffer_rsrc_t mrs;
         int qoff[TWQ];
         int dyoff[TWD];
-        // wave w copies 1 KiB chunks w*TWQ .. w*TWQ + TWQ - 1 of each Q tile (one run), and
-        // likewise TWD chunks of each dY tile
+        // wave w copies runs w*TWQ .. w*TWQ + TWQ - 1 of each Q tile, and likewise TWD runs of
+        // each dY tile
 #pragma unroll
-        for (int u = 0; u < TWQ; ++u) qoff[u] = dma_offset<DK>(w * TWQ + u, lane, p.q_st) - 1024 * u;
+        for (int u = 0; u < TWQ; ++u)
+            qoff[u] = Tile<DK>::dma_offset(w * TWQ + u, lane, p.q_st) - Tile<DK>::kRunBytes * u;
 #pragma unroll
-        for (int u = 0; u < TWD; ++u) dyoff[u] = dma_offset<DV>(w * TWD + u, lane, p.dy_st) - 1024 * u;
+        for (int u = 0; u < TWD; ++u)
+            dyoff[u] = Tile<DV>::dma_offset(w * TWD + u, lane, p.dy_st) - Tile<DV>::kRunBytes * u;
 
         // this lane's K and V rows: B operands of S = Q K^T and dP = dY V^T
         vec kreg[SK];
@@ -242,8 +247,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             const int q0 = t * BQ;
             const i32x4 rq = buffer_desc(gq + static_cast<int64_t>(q0) * p.q_st, tile_bytes(L - q0, BQ, p.q_st));
             const i32x4 rd = buffer_desc(gdy + static_cast<int64_t>(q0) * p.dy_st, tile_bytes(L - q0, BQ, p.dy_st));
-            const uint32_t mq = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(qtile(b) + w * TWQ * 512)));
-            const uint32_t md = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(dtile(b) + w * TWD * 512)));
+            const uint32_t mq = static_cast<uint32_t>(
+                reinterpret_cast<uintptr_t>((lds_void*)(qtile(b) + w * TWQ * Tile<DK>::kRunBytes / 2)));
+            const uint32_t md = static_cast<uint32_t>(
+                reinterpret_cast<uintptr_t>((lds_void*)(dtile(b) + w * TWD * Tile<DV>::kRunBytes / 2)));
             // statistics first: the last TWQ + TWD loads a wave issues for a tile are its Q / dY copies
             if (w == NW - 1 && lane < BQ / 4) {
                 // rows past the sequence read as zero
@@ -251,8 +258,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 dma16_async(sSt[b][0], buffer_desc(gstat + q0, nbytes), lane * 16);
                 dma16_async(sSt[b][1], buffer_desc(gstat + plane + q0, nbytes), lane * 16);
             }
-            dma_pair<TWQ, TWD>(__builtin_amdgcn_readfirstlane(mq), rq, qoff, __builtin_amdgcn_readfirstlane(md), rd,
-                               dyoff);
+            dma_pair<TWQ, Tile<DK>::kRunBytes, TWD, Tile<DV>::kRunBytes>(__builtin_amdgcn_readfirstlane(mq), rq, qoff,
+                                                                         __builtin_amdgcn_readfirstlane(md), rd, dyoff);
         };
 
         // where a step reads: X rows 32*xm.. of buffer xb, softmax statistics of rows 32*sm..
@@ -276,20 +283,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             if constexpr (k % 2 == 0) {
                 constexpr int s = XS::index(j);
                 if constexpr (XS::is_a(j)) {
-                    return lds_row<vec>(qtile(wh.xb) + 32 * wh.xm * DK, loQ.row[s]);
+                    return tile_row<vec>(qtile(wh.xb), loQ, 32 * wh.xm, s);
                 } else {
-                    return lds_row<vec>(dtile(wh.xb) + 32 * wh.xm * DV, loD.row[s]);
+                    return tile_row<vec>(dtile(wh.xb), loD, 32 * wh.xm, s);
                 }
             } else {
                 constexpr int i = YS::index(j);
                 if constexpr (YS::is_a(j)) {
                     constexpr int kk = i / NTV;
                     constexpr int nt = i % NTV;
-                    return lds_tr<vec>(dtile(wh.yb) + (32 * wh.ym + 16 * kk) * DV, loD.tr[nt][0], loD.tr[nt][1]);
+                    return tile_tr<vec>(dtile(wh.yb), loD, 32 * wh.ym + 16 * kk, nt);
                 } else {
                     constexpr int kk = i / NTK;
                     constexpr int nt = i % NTK;
-                    return lds_tr<vec>(qtile(wh.yb) + (32 * wh.ym + 16 * kk) * DK, loQ.tr[nt][0], loQ.tr[nt][1]);
+                    return tile_tr<vec>(qtile(wh.yb), loQ, 32 * wh.ym + 16 * kk, nt);
                 }
             }
         };
@@ -593,7 +600,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 #pragma unroll
             for (int i = 0; i < NB - 1; ++i)
                 if (tb + i < te) issue(tb + i, i);
-            for (int i = threadIdx.x; i < (TILEQ + TILED) / 8; i += 64 * NW)
+            for (int i = threadIdx.x; i < (TEQ + TED) / 8; i += 64 * NW)
                 reinterpret_cast<vec*>(sBuf[NB - 1])[i] = vec{};
             wait_dma();
             __syncthreads();
@@ -674,8 +681,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     constexpr int TWV = BK * DV / 8 / 64 / NW;  // ... and value tile
     static_assert(BQ == 32 * NW && BK == 64 && (BK * DV / 8 / 64) % NW == 0 && DV <= DK, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) T sK[2][BK * DK];
-    __shared__ __attribute__((aligned(16))) T sV[2][BK * DV];
+    __shared__ __attribute__((aligned(16))) T sK[2][Tile<DK>::kElems];
+    __shared__ __attribute__((aligned(16))) T sV[2][Tile<DV>::kElems];
 
     const Unit unit = wg_unit(p.xcd_group != 0);
     const fa_work_item_t it = p.items_q[unit.item];
@@ -690,30 +697,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     const int i0 = it.block * BQ + 32 * w;  // first query of this wave
     const int qi = i0 + col;                // this lane's query
 
-    LdsOffsets<DK> loK;
+    Tile<DK> loK;
     loK.init(lane);
-    LdsOffsets<DV> loV_;
+    Tile<DV> loV_;
     if constexpr (DK != DV) loV_.init(lane);
-    const LdsOffsets<DV>& loV = offsets_for(loK, loV_);
+    const Tile<DV>& loV = tile_for(loK, loV_);
 
     const int hk = n / p.group;  // the key/value head this query head reads
     const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh;
     const T* gv = static_cast<const T*>(p.v) + static_cast<int64_t>(it.kv_start) * p.v_st + hk * p.v_sh;
-    // wave w copies 1 KiB chunks w*TWK .. w*TWK + TWK - 1 of each key tile (one run), and
-    // likewise TWV chunks of each value tile
+    // wave w copies runs w*TWK .. w*TWK + TWK - 1 of each key tile, and likewise TWV runs of
+    // each value tile
     int koff[TWK];
     int voff[TWV];
 #pragma unroll
-    for (int u = 0; u < TWK; ++u) koff[u] = dma_offset<DK>(w * TWK + u, lane, p.k_st) - 1024 * u;
+    for (int u = 0; u < TWK; ++u) koff[u] = Tile<DK>::dma_offset(w * TWK + u, lane, p.k_st) - Tile<DK>::kRunBytes * u;
 #pragma unroll
-    for (int u = 0; u < TWV; ++u) voff[u] = dma_offset<DV>(w * TWV + u, lane, p.v_st) - 1024 * u;
+    for (int u = 0; u < TWV; ++u) voff[u] = Tile<DV>::dma_offset(w * TWV + u, lane, p.v_st) - Tile<DV>::kRunBytes * u;
     auto issue = [&](int kt, int b) __attribute__((always_inline)) {
         const int k0 = kt * BK;
         const i32x4 rk = buffer_desc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st));
         const i32x4 rv = buffer_desc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st));
-        const uint32_t mk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * 512)));
-        const uint32_t mv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * 512)));
-        dma_pair<TWK, TWV>(__builtin_amdgcn_readfirstlane(mk), rk, koff, __builtin_amdgcn_readfirstlane(mv), rv, voff);
+        const uint32_t mk = static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * Tile<DK>::kRunBytes / 2)));
+        const uint32_t mv = static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * Tile<DV>::kRunBytes / 2)));
+        dma_pair<TWK, Tile<DK>::kRunBytes, TWV, Tile<DV>::kRunBytes>(__builtin_amdgcn_readfirstlane(mk), rk, koff,
+                                                                     __builtin_amdgcn_readfirstlane(mv), rv, voff);
     };
 
     // this lane's Q and dY rows (B operands of S^T = K Q^T and dP^T = V dY^T) and statistics
@@ -823,8 +833,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         mrs = raw_rsrc(mb, static_cast<uint32_t>((L - 1) * p.mask.am_sq + K));
     }
 
-    // one 32-key step (keys k0s .. k0s + 31, rows 32 kh of the tile in cK / cV)
-    auto kstep = [&](const T* cK, const T* cV, int k0s) __attribute__((always_inline)) {
+    // one 32-key step (keys k0s .. k0s + 31, rows R .. R + 31 of the tiles cK / cV)
+    auto kstep = [&](const T* cK, const T* cV, auto rc, int k0s) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;
         // explicit mask bytes of keys k0s + 4h + cc(a), issued before the products that hide them
         // (with dropout as well: after them, like the dropout window, to stay within the registers)
         uint32_t mk[16];
@@ -863,13 +874,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         f32x16 accP = pinit;
 #pragma unroll
         for (int s = 0; s < SV; ++s) {
-            const vec ak = lds_row<vec>(cK, loK.row[s]);
-            const vec av = lds_row<vec>(cV, loV.row[s]);
+            const vec ak = tile_row<vec>(cK, loK, R, s);
+            const vec av = tile_row<vec>(cV, loV, R, s);
             accS = Op16<T>::mfma(ak, qreg[s], accS);
             accP = Op16<T>::mfma(av, dyreg[s], accP);
         }
 #pragma unroll
-        for (int s = SV; s < SK; ++s) accS = Op16<T>::mfma(lds_row<vec>(cK, loK.row[s]), qreg[s], accS);
+        for (int s = SV; s < SK; ++s) accS = Op16<T>::mfma(tile_row<vec>(cK, loK, R, s), qreg[s], accS);
         if constexpr (DROP && XM) {
             load_mask_bytes();
             load_window();
@@ -913,7 +924,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             const vec bs = __builtin_bit_cast(vec, make_uint4(dsw[kk][0], dsw[kk][1], dsw[kk][2], dsw[kk][3]));
 #pragma unroll
             for (int nd = 0; nd < ND; ++nd) {
-                const vec ak = lds_tr<vec>(cK + 16 * kk * DK, loK.tr[nd][0], loK.tr[nd][1]);
+                const vec ak = tile_tr<vec>(cK, loK, R + 16 * kk, nd);
                 accQ[nd] = Op16<T>::mfma(ak, bs, accQ[nd]);
             }
         }
@@ -926,8 +937,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         wait_dma();
         __syncthreads();  // tile kt is in buffer B; every wave is done with buffer B ^ 1
         if (kt + 1 < it.tile_end) issue(kt + 1, B ^ 1);
-        kstep(sK[B], sV[B], kt * BK);
-        kstep(sK[B] + 32 * DK, sV[B] + 32 * DV, kt * BK + 32);
+        kstep(sK[B], sV[B], IC<0>{}, kt * BK);
+        kstep(sK[B], sV[B], IC<32>{}, kt * BK + 32);
     };
     if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
     int kt = it.tile_begin;

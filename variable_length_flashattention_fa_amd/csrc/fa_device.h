@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 attention kernels (backward and forward): MFMA
-// wrappers, the swizzled LDS tile layout, transposing LDS reads and the LDS DMA copies.
+// wrappers, the LDS tile layouts, transposing LDS reads and the LDS DMA copies.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,37 +49,9 @@ __device__ __forceinline__ f32x16 zero16() {
 // Row (within a 32-row tile) of accumulator slot a for lane half h: 8*(a/4) + 4*h + a%4.
 __device__ __forceinline__ int acc_row(int a, int h) { return 8 * (a >> 2) + 4 * h + (a & 3); }
 
-// ---- swizzled [rows][D] tiles -----------------------------------------------------------------
-// Chunk c (16 bytes) of row r is stored at chunk c ^ swz(r).  For D = 128 a row fills all 64
-// banks; for D = 64 two rows share them.  The swizzle is a bijection on the chunk positions of
-// 16 consecutive rows (so 16 lanes reading one logical chunk of 16 rows hit 16 distinct bank
-// groups), and gives the four rows r0 .. r0+3 (r0 a multiple of 4) that a transposing read
-// touches chunk blocks that do not overlap for logical chunks 0..3 (32 lanes, 16 distinct
-// bank groups).
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 128) {
-        return ((row & 3) << 2) | ((row >> 2) & 3);
-    } else {
-        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ int swz_off(int row, int col) {
-    return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
-}
-
 // Raw buffer resource over `bytes` bytes at base: 32-bit data format, no swizzle.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-// 32 float2 row statistics {delta, beta} of a tile -> LDS (one 4-byte lane each).
-__device__ __forceinline__ void dma_stats32(float2* dst, const float2* g, int valid, int lane) {
-    const uint32_t bytes = valid > 0 ? static_cast<uint32_t>(min(valid, 32) * 8) : 0u;
-    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(g, bytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, lane * 4, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
@@ -120,33 +92,36 @@ __device__ __forceinline__ void dma16_async(T* lds, const i32x4& desc, int voff)
         : "memory");
 }
 
-// One 16-byte-per-lane run of TW KiB: LDS destination m0 + 1 KiB * u + 16 * lane for
-// instruction u, global source desc + v[u] + 1 KiB * u.  M0 is restored afterwards.
-template <int TW>
+// TW DMA instructions of 16 bytes per lane: instruction u writes LDS at m0 + RS * u + 16 * lane
+// from global desc + v[u] + RS * u (the instruction offset moves both addresses; v[u] makes up
+// for it on the global side).  M0 is restored afterwards; the DMA needs one wait state after M0
+// is written.
+template <int TW, int RS>
 __device__ __forceinline__ void dma_run(uint32_t m0, const i32x4& d, const int* v) {
+    static_assert(RS * (TW - 1) < 4096, "instruction offset field");
     uint32_t saved;
     if constexpr (TW == 4) {
         asm volatile(
             "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
             "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
-            "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
-            "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
-            "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
+            "buffer_load_dwordx4 %3, %6, 0 offen offset:%7 lds\n\t"
+            "buffer_load_dwordx4 %4, %6, 0 offen offset:%8 lds\n\t"
+            "buffer_load_dwordx4 %5, %6, 0 offen offset:%9 lds\n\t"
             "s_mov_b32 m0, %0"
             : "=&s"(saved)
-            : "s"(m0), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "s"(d)
+            : "s"(m0), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "s"(d), "n"(RS), "n"(2 * RS), "n"(3 * RS)
             : "memory");
     } else if constexpr (TW == 2) {
         asm volatile(
             "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
             "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
-            "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
+            "buffer_load_dwordx4 %3, %4, 0 offen offset:%5 lds\n\t"
             "s_mov_b32 m0, %0"
             : "=&s"(saved)
-            : "s"(m0), "v"(v[0]), "v"(v[1]), "s"(d)
+            : "s"(m0), "v"(v[0]), "v"(v[1]), "s"(d), "n"(RS)
             : "memory");
     } else {
-        static_assert(TW == 1, "runs of 1, 2 or 4 KiB");
+        static_assert(TW == 1, "1, 2 or 4 instructions");
         asm volatile(
             "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
             "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
@@ -157,57 +132,120 @@ __device__ __forceinline__ void dma_run(uint32_t m0, const i32x4& d, const int* 
     }
 }
 
-// Copy of two 16-byte-per-lane runs, TW KiB of tensor a (e.g. Q of a tile) and TB KiB of tensor
-// b (dY): LDS destination m0x + 1 KiB * u + 16 * lane for instruction u, global source
-// desc + voff[u] + 1 KiB * u (the instruction offset moves both addresses).  With equal runs one
-// M0 save / restore covers both.
-template <int TW, int TB = TW>
+// The copies of two tiles (e.g. Q and dY of one query tile): dma_run<TA, RA> of tensor a, then
+// dma_run<TB, RB> of tensor b.
+template <int TA, int RA, int TB, int RB>
 __device__ __forceinline__ void dma_pair(uint32_t m0a, const i32x4& da, const int* va, uint32_t m0b,
                                          const i32x4& db, const int* vb) {
-    uint32_t saved;
-    if constexpr (TW != TB) {
-        dma_run<TW>(m0a, da, va);
-        dma_run<TB>(m0b, db, vb);
-    } else if constexpr (TW == 4) {
-        asm volatile(
-            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
-            "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
-            "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
-            "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
-            "s_mov_b32 m0, %7\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %8, %12, 0 offen lds\n\t"
-            "buffer_load_dwordx4 %9, %12, 0 offen offset:1024 lds\n\t"
-            "buffer_load_dwordx4 %10, %12, 0 offen offset:2048 lds\n\t"
-            "buffer_load_dwordx4 %11, %12, 0 offen offset:3072 lds\n\t"
-            "s_mov_b32 m0, %0"
-            : "=&s"(saved)
-            : "s"(m0a), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "s"(da), "s"(m0b), "v"(vb[0]), "v"(vb[1]),
-              "v"(vb[2]), "v"(vb[3]), "s"(db)
-            : "memory");
-    } else if constexpr (TW == 1) {
-        asm volatile(
-            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-            "s_mov_b32 m0, %4\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %5, %6, 0 offen lds\n\t"
-            "s_mov_b32 m0, %0"
-            : "=&s"(saved)
-            : "s"(m0a), "v"(va[0]), "s"(da), "s"(m0b), "v"(vb[0]), "s"(db)
-            : "memory");
+    dma_run<TA, RA>(m0a, da, va);
+    dma_run<TB, RB>(m0b, db, vb);
+}
+
+// ---- [64][D] tiles of 16-bit values in LDS -----------------------------------------------------
+// Every tile is copied in by DMA instructions that each fill one run: 1 KiB of contiguous LDS,
+// 16 bytes per lane.  The kernels read a tile in two ways:
+//   row read:  lane (col = lane % 32, h = lane / 32) reads values 16 s + 8 h .. + 7 of row R + col
+//              (ds_read_b128; R a multiple of 16);
+//   transposing read (ds_read_b64_tr_b16, see below): lane reads 4 values at row
+//              R + 4 h + (lane % 16) / 4 + 8 x, columns 32 t + 16 ((lane / 16) % 2) + 4 (lane % 4)
+//              (R a multiple of 16, x = 0 or 1).
+// Tile<D> gives the layout, the DMA source offsets and each lane's read offsets (in values), so
+// that a read is lds_row / lds_tr at tile + imm(...) with the lane's offset.
+//
+// D = 128 (rows of 256 bytes): run c (c = 0..15) starts at byte 1040 c -- 16 bytes of gap after
+// each -- and holds rows j, j + 16, j + 32, j + 48 of j = jrow(c) = 8 (c % 2) + 4 ((c / 2) % 2)
+// + c / 4, each row's 16-byte chunks in order.  Row r starts at byte 1040 cls(r % 16) + 256 (r / 16)
+// with cls the inverse of jrow, so a row starts at bank group cls(r % 16) (1040 = 16 mod 256):
+// - a row read's 16 lanes of one 256-byte transfer cover rows R .. R + 15, whose cls are all
+//   distinct: 16 distinct bank groups;
+// - a transposing read's 32 lanes of one transfer cover rows r0 .. r0 + 3 (r0 = 4 h + 8 x + R)
+//   over 64 bytes each; their cls are 4 apart, so the four 64-byte pieces do not share a bank;
+// - and every offset that varies between the reads of a lane is a constant: one lane offset per
+//   read kind serves the whole tile (and any tile at a fixed distance from it), the rest goes
+//   into the instruction's offset field.
+// D = 64 (rows of 128 bytes): rows are contiguous and chunk c of row r sits at c ^ swz(r), with
+// swz(r) = 4 ((r / 2) % 2) + (r / 4) % 4: 16 lanes reading one logical chunk of rows R .. R + 15
+// hit 16 distinct bank groups, and the four rows of a transposing read occupy disjoint 64-byte
+// pieces; the per-lane offsets then differ per chunk (one register per s and per (t, x)).
+template <int D>
+struct Tile;
+
+template <>
+struct Tile<128> {
+    static constexpr int kRunBytes = 1040;
+    static constexpr int kElems = 16 * kRunBytes / 2;  // values of LDS one tile spans
+    static __host__ __device__ __forceinline__ int cls(int j) { return 4 * (j & 3) + 2 * ((j >> 2) & 1) + ((j >> 3) & 1); }
+    static __host__ __device__ __forceinline__ int jrow(int c) { return 8 * (c & 1) + 4 * ((c >> 1) & 1) + (c >> 2); }
+
+    int rowb;  // lane offset of the row reads
+    int trb;   // ... and of the transposing reads
+    __host__ __device__ __forceinline__ void init(int lane) {
+        const int col = lane & 31;
+        const int h = lane >> 5;
+        const int gi = lane & 15;
+        rowb = (kRunBytes * cls(col & 15) + 256 * (col >> 4)) / 2 + 8 * h;
+        trb = kRunBytes * cls(4 * h + (gi >> 2)) / 2 + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+    }
+    __host__ __device__ __forceinline__ int row_off(int) const { return rowb; }
+    static constexpr int row_imm(int R, int s) { return 8 * R + 16 * s; }
+    __host__ __device__ __forceinline__ int tr_off(int, int) const { return trb; }
+    static constexpr int tr_imm(int R, int t, int x) { return 8 * R + 32 * t + x * kRunBytes / 2; }
+
+    // Byte offset, from the tile's row 0 in global memory (row stride st values), of the 16 bytes
+    // lane `lane` copies in DMA instruction i (= run i).
+    static __host__ __device__ __forceinline__ int dma_offset(int i, int lane, int64_t st) {
+        const int row = jrow(i) + 16 * (lane >> 4);
+        return static_cast<int>(row * st * 2) + 16 * (lane & 15);
+    }
+};
+
+template <>
+struct Tile<64> {
+    static constexpr int kRunBytes = 1024;
+    static constexpr int kElems = 64 * 64;
+    static __host__ __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+    int row[4];
+    int tr[2][2];
+    __host__ __device__ __forceinline__ void init(int lane) {
+        const int col = lane & 31;
+        const int h = lane >> 5;
+        const int gi = lane & 15;
+        const int gc = 16 * ((lane >> 4) & 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) row[s] = col * 64 + (((2 * s + h) ^ swz(col)) << 3);
+        const int rr = 4 * h + (gi >> 2);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int r = rr + 8 * x;
+                const int c = 32 * t + gc + 4 * (gi & 3);
+                tr[t][x] = r * 64 + (((c >> 3) ^ swz(r)) << 3) + (c & 7);
+            }
+        }
+    }
+    __host__ __device__ __forceinline__ int row_off(int s) const { return row[s]; }
+    static constexpr int row_imm(int R, int) { return 64 * R; }
+    __host__ __device__ __forceinline__ int tr_off(int t, int x) const { return tr[t][x]; }
+    static constexpr int tr_imm(int R, int, int) { return 64 * R; }
+
+    static __host__ __device__ __forceinline__ int dma_offset(int i, int lane, int64_t st) {
+        const int pc = i * 64 + lane;
+        const int row = pc >> 3;
+        const int lc = (pc & 7) ^ swz(row);
+        return static_cast<int>(row * st * 2) + lc * 16;
+    }
+};
+
+// The lane offsets of a tile of DB values per row: `a` itself when DA == DB (one register set),
+// else `b`, which the caller has initialised.
+template <int DA, int DB>
+__device__ __forceinline__ const Tile<DB>& tile_for(const Tile<DA>& a, const Tile<DB>& b) {
+    if constexpr (DA == DB) {
+        return a;
     } else {
-        static_assert(TW == 2, "runs of 1, 2 or 4 KiB");
-        asm volatile(
-            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
-            "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
-            "s_mov_b32 m0, %5\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %6, %8, 0 offen lds\n\t"
-            "buffer_load_dwordx4 %7, %8, 0 offen offset:1024 lds\n\t"
-            "s_mov_b32 m0, %0"
-            : "=&s"(saved)
-            : "s"(m0a), "v"(va[0]), "v"(va[1]), "s"(da), "s"(m0b), "v"(vb[0]), "v"(vb[1]), "s"(db)
-            : "memory");
+        return b;
     }
 }
 
@@ -220,24 +258,6 @@ __device__ __forceinline__ void dma_pair(uint32_t m0a, const i32x4& da, const in
 template <typename T>
 __device__ __forceinline__ s16x4 ds_read_tr(const T* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
-
-// 8-value operand X[r0 + e][c], X[r1 + e][c] (e = 0..3) of a swizzled tile, c = c0 + lane%16.
-template <typename vec, int D, typename T>
-__device__ __forceinline__ vec tr_operand(const T* tile, int r0, int r1, int c0, int i) {
-    const int ra = r0 + (i >> 2);
-    const int rb = r1 + (i >> 2);
-    const int c = c0 + 4 * (i & 3);
-    const s16x4 lo = ds_read_tr(tile + swz_off<D>(ra, c));
-    const s16x4 hi = ds_read_tr(tile + swz_off<D>(rb, c));
-    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(vec, v);
-}
-
-// Row operand: 8 consecutive columns c..c+7 (c a multiple of 8) of row r of a swizzled tile.
-template <typename vec, int D, typename T>
-__device__ __forceinline__ vec row_operand(const T* tile, int r, int c) {
-    return *reinterpret_cast<const vec*>(tile + swz_off<D>(r, c));
 }
 
 template <typename T>
@@ -260,75 +280,30 @@ struct TypeTag {
 
 
 
-// Per-lane LDS offsets (elements) of the swizzled reads.  Kernels whose two tile kinds have
-// the same row length share one set (see offsets_for).  Rows of the reads below are
-// R + lane%32 (row reads) or R + 4h + (lane%16)/4 (+8) (transposing reads) with R a
-// multiple of 16, so the swizzle term depends on the lane only and R*D can be added as a
-// compile-time constant.
-template <int D>
-struct LdsOffsets {
-    int row[D / 16];      // row read of columns 16s + 8h .. +7 in row lane%32
-    int tr[D / 32][2];    // transposing read, columns 32t + lane%32 of rows 4h + (lane%16)/4 + 8x
-
-    __device__ __forceinline__ void init(int lane) {
-        const int col = lane & 31;
-        const int h = lane >> 5;
-        const int gi = lane & 15;
-        const int gc = 16 * ((lane >> 4) & 1);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) row[s] = col * D + (((2 * s + h) ^ swz<D>(col)) << 3);
-        const int rr = 4 * h + (gi >> 2);
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int r = rr + 8 * x;
-                const int c = 32 * t + gc + 4 * (gi & 3);
-                tr[t][x] = r * D + (((c >> 3) ^ swz<D>(r)) << 3) + (c & 7);
-            }
-        }
-    }
-};
-
-// The offsets of tiles with rows of DB elements: `a` itself when DA == DB (one register set),
-// else `b`, which the caller has initialised.
-template <int DA, int DB>
-__device__ __forceinline__ const LdsOffsets<DB>& offsets_for(const LdsOffsets<DA>& a, const LdsOffsets<DB>& b) {
-    if constexpr (DA == DB) {
-        return a;
-    } else {
-        return b;
-    }
-}
-
 template <typename vec, typename T>
 __device__ __forceinline__ vec lds_row(const T* base, int off) {
     return *reinterpret_cast<const vec*>(base + off);
 }
 
+// Two transposing reads (rows r0 + e and r0 + 8 + e) forming one 8-value MFMA operand.
 template <typename vec, typename T>
-__device__ __forceinline__ vec lds_tr(const T* base, int off0, int off1) {
-    const s16x4 lo = ds_read_tr(base + off0);
-    const s16x4 hi = ds_read_tr(base + off1);
+__device__ __forceinline__ vec lds_tr(const T* base0, int off0, const T* base1, int off1) {
+    const s16x4 lo = ds_read_tr(base0 + off0);
+    const s16x4 hi = ds_read_tr(base1 + off1);
     const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(vec, v);
 }
 
-// Byte offset, within a tile whose row 0 is at the buffer base, of the 16-byte chunk that
-// lane `lane` copies in DMA instruction i of a swizzled [rows][D] tile (row stride st).
-template <int D>
-__device__ __forceinline__ int dma_offset(int i, int lane, int64_t st) {
-    constexpr int CPR = D / 8;
-    const int pc = i * 64 + lane;
-    const int row = pc / CPR;
-    const int lc = (pc % CPR) ^ swz<D>(row);
-    return static_cast<int>(row * st * 2) + lc * 16;
+// Row read s of rows R .. of `tile` (see Tile).
+template <typename vec, int D, typename T>
+__device__ __forceinline__ vec tile_row(const T* tile, const Tile<D>& lo, int R, int s) {
+    return lds_row<vec>(tile + Tile<D>::row_imm(R, s), lo.row_off(s));
 }
 
-// One DMA instruction of a tile copy: 64 lanes x 16 bytes into LDS at dst + 1 KiB * i.
-template <typename T>
-__device__ __forceinline__ void dma_issue(T* dst, int i, __amdgpu_buffer_rsrc_t rs, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 512), 16, voff, 0, 0, 0);
+// Transposing operand of columns 32 t .. of rows R .. R + 15 of `tile` (see Tile).
+template <typename vec, int D, typename T>
+__device__ __forceinline__ vec tile_tr(const T* tile, const Tile<D>& lo, int R, int t) {
+    return lds_tr<vec>(tile + Tile<D>::tr_imm(R, t, 0), lo.tr_off(t, 0), tile + Tile<D>::tr_imm(R, t, 1), lo.tr_off(t, 1));
 }
 
 __device__ __forceinline__ uint32_t tile_bytes(int valid, int rows, int64_t st) {
@@ -367,12 +342,19 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// Empty instruction that claims to read and write x.  Volatile asm statements and LDS accesses
-// keep their program order through instruction selection, so fencing the inputs and outputs
-// of a piece of arithmetic pins it between its neighbours in the slot schedule below.
+// Empty instruction that reads x.  Volatile asm statements and LDS accesses keep their program
+// order through instruction selection, so fencing the inputs and results of a piece of
+// arithmetic pins it between its neighbours in the slot schedule below.  It only reads: the
+// compiler puts a wait state between an asm statement that writes a register and the next
+// instruction that reads it, which a fence that also claimed to write x would add at every use.
+// (Device pass only: the host pass, which also instantiates the kernels, has no such registers.)
 template <typename X>
-__device__ __forceinline__ void pin(X& x) {
-    asm volatile("" : "+v"(x));
+__device__ __forceinline__ void pin(const X& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" ::"v"(x));
+#else
+    (void)x;
+#endif
 }
 
 // acc += A B with acc in accumulation registers (volatile: keeps its slot).

@@ -37,8 +37,8 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     constexpr int TWV = BK * DV / 8 / 64 / NW;  // ... and value tile
     static_assert(BQ == 32 * NW && BK == 64 && (BK * DV / 8 / 64) % NW == 0 && DV <= DK, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) T sK[2][BK * DK];
-    __shared__ __attribute__((aligned(16))) T sV[2][BK * DV];
+    __shared__ __attribute__((aligned(16))) T sK[2][Tile<DK>::kElems];
+    __shared__ __attribute__((aligned(16))) T sV[2][Tile<DV>::kElems];
 
     const Unit unit = wg_unit(p.xcd_group != 0);
     const fa_work_item_t it = p.items[unit.item];
@@ -53,11 +53,11 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     const int i0 = it.block * BQ + 32 * w;
     const int qi = i0 + col;
 
-    LdsOffsets<DK> loK;
+    Tile<DK> loK;
     loK.init(lane);
-    LdsOffsets<DV> loV_;
+    Tile<DV> loV_;
     if constexpr (DK != DV) loV_.init(lane);
-    const LdsOffsets<DV>& loV = offsets_for(loK, loV_);
+    const Tile<DV>& loV = tile_for(loK, loV_);
 
     const int hk = n / p.group;  // the key/value head this query head reads
     const T* gk = static_cast<const T*>(p.k) + static_cast<int64_t>(it.kv_start) * p.k_st + hk * p.k_sh;
@@ -65,16 +65,19 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     int koff[TWK];
     int voff[TWV];
 #pragma unroll
-    for (int u = 0; u < TWK; ++u) koff[u] = dma_offset<DK>(w * TWK + u, lane, p.k_st) - 1024 * u;
+    for (int u = 0; u < TWK; ++u) koff[u] = Tile<DK>::dma_offset(w * TWK + u, lane, p.k_st) - Tile<DK>::kRunBytes * u;
 #pragma unroll
-    for (int u = 0; u < TWV; ++u) voff[u] = dma_offset<DV>(w * TWV + u, lane, p.v_st) - 1024 * u;
+    for (int u = 0; u < TWV; ++u) voff[u] = Tile<DV>::dma_offset(w * TWV + u, lane, p.v_st) - Tile<DV>::kRunBytes * u;
     auto issue = [&](int kt, int b) __attribute__((always_inline)) {
         const int k0 = kt * BK;
         const i32x4 rk = buffer_desc(gk + static_cast<int64_t>(k0) * p.k_st, tile_bytes(K - k0, BK, p.k_st));
         const i32x4 rv = buffer_desc(gv + static_cast<int64_t>(k0) * p.v_st, tile_bytes(K - k0, BK, p.v_st));
-        const uint32_t mk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * 512)));
-        const uint32_t mv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * 512)));
-        dma_pair<TWK, TWV>(__builtin_amdgcn_readfirstlane(mk), rk, koff, __builtin_amdgcn_readfirstlane(mv), rv, voff);
+        const uint32_t mk = static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * Tile<DK>::kRunBytes / 2)));
+        const uint32_t mv = static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * Tile<DV>::kRunBytes / 2)));
+        dma_pair<TWK, Tile<DK>::kRunBytes, TWV, Tile<DV>::kRunBytes>(__builtin_amdgcn_readfirstlane(mk), rk, koff,
+                                                                     __builtin_amdgcn_readfirstlane(mv), rv, voff);
     };
 
     // this lane's Q row
@@ -147,7 +150,9 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     float mref = -INFINITY;   // the max the P values and O^T are relative to
     float lsum = 0.f;         // sum of P over this lane's keys (relative to mref)
 
-    auto kstep = [&](const T* cK, const T* cV, int k0s) __attribute__((always_inline)) {
+    // one 32-key step (keys k0s .. k0s + 31, rows R .. R + 31 of the tiles cK / cV)
+    auto kstep = [&](const T* cK, const T* cV, auto rc, int k0s) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;
         // explicit mask bytes of keys k0s + 4h + cc(a), issued before the product that hides them
         uint32_t mk[16];
         if constexpr (XM) {
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         f32x16 accS = zero16();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const vec ak = lds_row<vec>(cK, loK.row[s]);
+            const vec ak = tile_row<vec>(cK, loK, R, s);
             accS = Op16<T>::mfma(ak, qreg[s], accS);
         }
         const bool full = !XM && wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
             const vec bp = __builtin_bit_cast(vec, make_uint4(pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]));
 #pragma unroll
             for (int nd = 0; nd < ND; ++nd) {
-                const vec av = lds_tr<vec>(cV + 16 * kk * DV, loV.tr[nd][0], loV.tr[nd][1]);
+                const vec av = tile_tr<vec>(cV, loV, R + 16 * kk, nd);
                 accO[nd] = Op16<T>::mfma(av, bp, accO[nd]);
             }
         }
@@ -254,8 +259,8 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         wait_dma();
         __syncthreads();  // tile kt is in buffer B; every wave is done with buffer B ^ 1
         if (kt + 1 < it.tile_end) issue(kt + 1, B ^ 1);
-        kstep(sK[B], sV[B], kt * BK);
-        kstep(sK[B] + 32 * DK, sV[B] + 32 * DV, kt * BK + 32);
+        kstep(sK[B], sV[B], IC<0>{}, kt * BK);
+        kstep(sK[B], sV[B], IC<32>{}, kt * BK + 32);
     };
     if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
     int kt = it.tile_begin;
