@@ -870,6 +870,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             win = __builtin_amdgcn_alignbit(hi, lo, lb & 7);
         };
         if constexpr (DROP && !XM) load_window();
+        // The two waves of a SIMD run the same sequence and meet at every tile barrier, so they
+        // tend to reach their products and their softmax gradients together, when the matrix
+        // pipe idles.  A wave issuing its S / dP products takes issue priority over one in any
+        // other phase, which pulls the two apart.
+        __builtin_amdgcn_s_setprio(1);
         f32x16 accS = sinit;
         f32x16 accP = pinit;
 #pragma unroll
@@ -881,6 +886,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         }
 #pragma unroll
         for (int s = SV; s < SK; ++s) accS = Op16<T>::mfma(tile_row<vec>(cK, loK, R, s), qreg[s], accS);
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (DROP && XM) {
             load_mask_bytes();
             load_window();
