@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     const int off = K - L;
     const int j0 = it.block * BKV;
     const int jw = j0 + 32 * w + col;  // this lane's key
+    const uint32_t inv_keep_bits = __builtin_bit_cast(uint32_t, p.inv_keep);
     const int tb = it.tile_begin;
     const int te = it.tile_end;
 
@@ -452,11 +453,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                         float y = pC[a];
                         pin(y);
                         if constexpr (DROP) {
+                            // z = Z / keepProb of the element; dS = P (dP z - D), Pd = P z
                             const float ndl = stC[a / 4][0][a % 4];
                             const int u = dcC + cc * K;
-                            const bool keep = __builtin_amdgcn_ubfe(dbC[a], u & 7, 1) != 0;
-                            pdv[a] = keep ? pv[a] * p.inv_keep : 0.f;
-                            dsv[a] = pv[a] * ((keep ? y * p.inv_keep : 0.f) + ndl);
+                            const float z = keep_scale(dbC[a], u & 7, inv_keep_bits);
+                            pdv[a] = pv[a] * z;
+                            dsv[a] = pv[a] * fmaf(y, z, ndl);
                         } else {
                             pdv[a] = pv[a];
                             dsv[a] = pv[a] * y;  // y = dP - D
@@ -696,6 +698,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     const int off = K - L;
     const int i0 = it.block * BQ + 32 * w;  // first query of this wave
     const int qi = i0 + col;                // this lane's query
+    const uint32_t inv_keep_bits = __builtin_bit_cast(uint32_t, p.inv_keep);
 
     Tile<DK> loK;
     loK.init(lane);
@@ -807,11 +810,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     f32x16 pinit;
 #pragma unroll
     for (int i = 0; i < 16; ++i) pinit[i] = FOLD_D ? ndelta : 0.f;
-    // Without dropout the S^T chain, too, does the softmax's affine step: the lane's Q row is
-    // scaled by scale * log2(e) (once, before rounding to the operand type) and the chain starts
-    // from -beta, so it ends with S * scale * log2(e) - beta and P = exp2(acc) needs no multiply.
-    // (With dropout or an explicit mask the registers are not there; the plain form stays.)
-    constexpr bool FOLD_B = !DROP && !XM;
+    // The S^T chain, too, does the softmax's affine step: the lane's Q row is scaled by
+    // scale * log2(e) (once, before rounding to the operand type) and the chain starts from
+    // -beta, so it ends with S * scale * log2(e) - beta and P = exp2(acc) needs no multiply.
+    // (With an explicit mask the registers are not there; the plain form stays.)
+    constexpr bool FOLD_B = !XM;
     f32x16 sinit;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sinit[i] = FOLD_B ? -beta : 0.f;
@@ -911,7 +914,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
                         pv = adm ? pv : 0.f;
                     }
                     if constexpr (DROP) {
-                        const float zk = __builtin_amdgcn_ubfe(win, cc + 4 * h, 1) != 0 ? p.inv_keep : 0.f;
+                        const float zk = keep_scale(win, cc + 4 * h, inv_keep_bits);
                         ds[e] = pv * fmaf(accP[a + e], zk, ndelta);
                     } else {
                         ds[e] = pv * accP[a + e];  // accP already holds dP - D

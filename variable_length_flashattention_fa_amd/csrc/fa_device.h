@@ -268,6 +268,13 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, t2));  // one packed conversion
 }
 
+// 1 / keep_prob where bit `pos` (taken modulo 32) of `bits` is set, else 0: the sign-extended bit
+// masks the bit pattern of 1 / keep_prob (`inv_keep_bits`), two instructions and no compare.
+__device__ __forceinline__ float keep_scale(uint32_t bits, int pos, uint32_t inv_keep_bits) {
+    const int bit = __builtin_amdgcn_sbfe(static_cast<int>(bits), static_cast<unsigned>(pos), 1u);
+    return __builtin_bit_cast(float, static_cast<uint32_t>(bit) & inv_keep_bits);
+}
+
 template <bool V>
 struct Tag {
     static constexpr bool value = V;

@@ -232,8 +232,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
                 lsum += pv;
                 if constexpr (DROP) {
                     const int cc = 8 * ((a + e) >> 2) + ((a + e) & 3);
-                    const bool keep = __builtin_amdgcn_ubfe(win, cc + 4 * h, 1) != 0;
-                    pd[e] = keep ? pv * p.inv_keep : 0.f;
+                    pd[e] = pv * keep_scale(win, cc + 4 * h, __builtin_bit_cast(uint32_t, p.inv_keep));
                 } else {
                     pd[e] = pv;
                 }
