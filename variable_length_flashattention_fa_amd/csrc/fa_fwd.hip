@@ -122,6 +122,17 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         wlo = max(wlo, i0 + 31 + off - p.pre);
         whi = min(whi, i0 + off + p.nxt);
     }
+    // keys admitted by some query of the wave (uniform): a step outside them contributes nothing
+    // to the wave's rows, and the wave skips its work (it still copies its part of each tile and
+    // meets every barrier)
+    int alo = 0;
+    int ahi = i0 < L ? K - 1 : -1;
+    if (p.mode == FA_MASK_CAUSAL) {
+        ahi = min(ahi, i0 + 31 + off);
+    } else if (p.mode == FA_MASK_BAND) {
+        alo = max(alo, i0 + off - p.pre);
+        ahi = min(ahi, i0 + 31 + off + p.nxt);
+    }
 
     // dropout: the (sequence, head) region of the bit stream starts at bit rb; the bits of this
     // lane's query row start rbit bits past the region's first byte
@@ -153,6 +164,7 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     // one 32-key step (keys k0s .. k0s + 31, rows R .. R + 31 of the tiles cK / cV)
     auto kstep = [&](const T* cK, const T* cV, auto rc, int k0s) __attribute__((always_inline)) {
         constexpr int R = decltype(rc)::value;
+        if (k0s > ahi || k0s + 31 < alo) return;
         // explicit mask bytes of keys k0s + 4h + cc(a), issued before the product that hides them
         uint32_t mk[16];
         if constexpr (XM) {
