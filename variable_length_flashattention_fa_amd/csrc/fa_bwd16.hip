@@ -218,6 +218,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                         kreg[s][e] = static_cast<T>(static_cast<float>(kreg[s][e]) * p.exp_scale);
                 }
             }
+            // wait for these rows here, before the tile copies are issued: a wait at their first use
+            // would also wait for every copy issued before it (loads complete in issue order)
+#pragma unroll
+            for (int s = 0; s < SK; ++s) pin(kreg[s]);
+#pragma unroll
+            for (int s = 0; s < SV; ++s) pin(vreg[s]);
         }
 
         // Query rows this lane's key admits, [lo_row, hi_row]; the element of step rows q0s..
@@ -604,7 +610,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 if (tb + i < te) issue(tb + i, i);
             for (int i = threadIdx.x; i < (TEQ + TED) / 8; i += 64 * NW)
                 reinterpret_cast<vec*>(sBuf[NB - 1])[i] = vec{};
-            wait_dma();
+            // the first step needs tile tb only: the copies of the tiles after it may still be in
+            // flight (a wave's copies complete in issue order; wave NW - 1 also copies each
+            // tile's statistics, two more loads per tile)
+            {
+                const int after = min(NB - 2, te - tb - 1);
+                if (w == NW - 1) {
+                    wait_dma_but_tiles<TWQ + TWD + 2, NB - 2>(after);
+                } else {
+                    wait_dma_but_tiles<TWQ + TWD, NB - 2>(after);
+                }
+            }
             __syncthreads();
             {
                 const Where w0 = where(kStepFirst, 0);

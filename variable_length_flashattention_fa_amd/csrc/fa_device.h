@@ -59,8 +59,21 @@ __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70);
 // complete in issue order for this count)
 template <int N>
 __device__ __forceinline__ void wait_dma_but() {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    // vmcnt is six bits: the low four at [3:0], the high two at [15:14]
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// vmcnt(PER * tiles) for a wave that issued PER loads per tile, tiles in [T, MAXT] (uniform)
+template <int PER, int MAXT, int T = 0>
+__device__ __forceinline__ void wait_dma_but_tiles(int tiles) {
+    if constexpr (T <= MAXT) {
+        if (tiles == T) {
+            wait_dma_but<PER * T>();
+        } else {
+            wait_dma_but_tiles<PER, MAXT, T + 1>(tiles);
+        }
+    }
 }
 
 // The same 16-byte-per-lane HBM -> LDS copy issued from inline assembly: the compiler then
