@@ -35,6 +35,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+# input preparation shared with the tests (torch fp32 forward for Y and the statistics, pair counts)
+TESTS = os.path.join(ROOT, "tests")
+if TESTS not in sys.path:
+    sys.path.append(TESTS)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -134,7 +138,7 @@ def cpu_baseline(inp, y_host, smax_h, ssum_h, wl, units_wanted: int):
 
     from oracle import fa_oracle as O
     from variable_length_flashattention_fa_amd import synth
-    from variable_length_flashattention_fa_amd.inputs_forward import pair_count
+    from inputs_forward import pair_count
 
     try:
         cores = len(os.sched_getaffinity(0))
@@ -219,7 +223,7 @@ def other_workload(number: int, steps: int, warmup: int) -> dict:
 
     from variable_length_flashattention_fa_amd import binding as B
     from variable_length_flashattention_fa_amd import synth
-    from variable_length_flashattention_fa_amd.inputs_forward import forward_stats, pair_count
+    from inputs_forward import forward_stats, pair_count
 
     wl = synth.workload(number)
     t0 = time.time()
@@ -302,7 +306,7 @@ def main(argv=None):
 
     from variable_length_flashattention_fa_amd import binding as B
     from variable_length_flashattention_fa_amd import synth
-    from variable_length_flashattention_fa_amd.inputs_forward import forward_stats, pair_count
+    from inputs_forward import forward_stats, pair_count
 
     B.load()  # fail loudly before any work if the library is missing
     wl = synth.workload(args.workload)

@@ -3,8 +3,8 @@
 The backward consumes the forward's output Y and its row max / row sum.  For
 workloads where the fp64 CPU forward would take too long, this module produces
 them on the GPU with plain torch fp32 matmuls, one sequence and a chunk of
-query rows at a time.  It is input preparation for benchmarks and full-size
-checks, outside any timed region; the backward never calls it.
+query rows at a time.  It is input preparation for the tests' full-size checks and
+for bench.py, outside any timed region; the library never calls it.
 
 Definitions (formulas section of the "FlashAttention梯度V2" page):
 S = scale * Q K^T restricted to admitted keys, m = row max, l = sum exp(S - m),

@@ -9,7 +9,7 @@ import torch
 from gpu_common import DEV, log, make
 from oracle import fa_oracle as O
 from variable_length_flashattention_fa_amd import binding as B
-from variable_length_flashattention_fa_amd.inputs_forward import forward_stats
+from inputs_forward import forward_stats
 
 pytestmark = pytest.mark.gpu
 

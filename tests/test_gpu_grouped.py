@@ -95,7 +95,7 @@ def test_grouped_narrow_v_full_size_sampled():
     from gpu_common import DEV, assert_close, log
     from variable_length_flashattention_fa_amd import binding as B
     from variable_length_flashattention_fa_amd import synth
-    from variable_length_flashattention_fa_amd.inputs_forward import forward_stats
+    from inputs_forward import forward_stats
 
     t0 = time.time()
     base = synth.workload(2)

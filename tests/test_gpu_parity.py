@@ -21,7 +21,7 @@ from gpu_common import assert_close, gpu_backward, log, make, oracle_backward, r
 from oracle import fa_oracle as O
 from variable_length_flashattention_fa_amd import binding as B
 from variable_length_flashattention_fa_amd import synth
-from variable_length_flashattention_fa_amd.inputs_forward import forward_stats
+from inputs_forward import forward_stats
 
 pytestmark = pytest.mark.gpu
 

@@ -8,7 +8,7 @@ import pytest
 
 from oracle import fa_oracle as O
 from variable_length_flashattention_fa_amd import binding as B
-from variable_length_flashattention_fa_amd.inputs_forward import pair_count
+from inputs_forward import pair_count
 
 def _check(lq, lkv, mode, pre, nxt, heads, block_rows, tile_rows, kind):
     cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
