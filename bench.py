@@ -44,7 +44,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "variable_length_flashattention_fa_amd", "csrc", f)
-                  for f in ("fa_kernels.hip", "fa_bwd16.hip", "fa_fwd.hip", "fa_device.h", "fa_kernels.h", "build.py")]
+                  for f in ("fa_kernels.hip", "fa_bwd16.hip", "fa_fwd.hip", "fa_device.h", "fa_kernels.h", "build.py",
+                            "fa_worklist.cpp")]  # the work-list order decides which tiles share an L2
 # kernel name fragment in a counter trace -> the name bench reports it under
 PMC_KERNELS = {"bwd_dkdv16_kernel": "bwd_dkdv16_kernel", "bwd_dq16_kernel": "bwd_dq16_kernel",
                "preprocess_kernel": "preprocess", "bwd_main_kernel": "bwd_main_kernel", "fwd16_kernel": "fwd16_kernel"}

@@ -254,7 +254,9 @@ enum {
  * every sequence with Lq_b > 0; its range covers exactly the key tiles of
  * tile_rows rows that hold a key admitted by some query of the block.
  * Blocks with an empty range are kept so their outputs are written as zeros.
- * Items are ordered longest range first.
+ * Items are ordered sequence by sequence (sequences whose longest range is
+ * longest first, ties by sequence index), and longest range first within a
+ * sequence.
  *
  * items: HOST array of capacity entries, may be NULL to only count.
  * Returns the number of items (>= 0), or -FA_ERR_* on invalid input.

@@ -214,7 +214,7 @@ def test_full_size_complete_units_and_every_head(number):
     device).  Compared with the oracle: two complete (sequence, head) units, every row of dQ and
     every key of dK / dV; and, for every head, sampled rows and keys, including the shortest items
     of both work lists (the first query blocks and the last key blocks of each sequence, which the
-    longest-first order runs last) and the tile and block edges."""
+    work-list order runs last within each sequence) and the tile and block edges."""
     t0 = time.time()
     wl = synth.workload(number)
     log(f"full-size workload {number} ({wl.name}): generating inputs")

@@ -21,9 +21,16 @@ def _check(lq, lkv, mode, pre, nxt, heads, block_rows, tile_rows, kind):
     got_blocks = [(it["seq"], it["block"]) for it in items]
     assert len(got_blocks) == len(set(got_blocks))
     assert set(got_blocks) == expect_blocks
-    # longest first
+    # sequence by sequence (longest item first, ties by index), longest first within a sequence
     spans = [it["tile_end"] - it["tile_begin"] for it in items]
-    assert spans == sorted(spans, reverse=True)
+    seqs = [it["seq"] for it in items]
+    order = [b for i, b in enumerate(seqs) if i == 0 or seqs[i - 1] != b]
+    assert len(order) == len(set(order)), "a sequence's items are not contiguous"
+    longest = {b: max(s for s, bb in zip(spans, seqs) if bb == b) for b in order}
+    assert order == sorted(order, key=lambda b: (-longest[b], b))
+    for b in order:
+        own = [s for s, bb in zip(spans, seqs) if bb == b]
+        assert own == sorted(own, reverse=True)
     bases = O.dropout_bit_bases(cu_q, cu_k, heads)
     index = {(it["seq"], it["block"]): it for it in items}
     for b in range(len(lq)):

@@ -118,8 +118,19 @@ int64_t build_worklist(const int64_t* cu_q, const int64_t* cu_kv, int64_t batch,
         }
         drop_base += heads * lq * lkv;
     }
-    // longest first, so the long causal blocks do not trail at the end of the grid
-    std::stable_sort(out.begin(), out.end(), [](const fa_work_item_t& a, const fa_work_item_t& b) {
+    // Sequence by sequence, sequences with the longest item first, and within a sequence longest
+    // item first: the long blocks do not trail at the end of the grid, and the workgroups that run
+    // together (consecutive items of one head) belong to one sequence, so they walk the same tiles
+    // and share an L2.  (A plain longest-first order mixes the sequences' blocks: on 4 x 16384
+    // causal the dK/dV kernel then reads 5.2 GB past the L2 per launch instead of 1.8 GB.)
+    std::vector<int64_t> longest(static_cast<size_t>(batch), 0);
+    for (const fa_work_item_t& it : out)
+        longest[it.seq] = std::max<int64_t>(longest[it.seq], it.tile_end - it.tile_begin);
+    std::stable_sort(out.begin(), out.end(), [&](const fa_work_item_t& a, const fa_work_item_t& b) {
+        if (a.seq != b.seq) {
+            if (longest[a.seq] != longest[b.seq]) return longest[a.seq] > longest[b.seq];
+            return a.seq < b.seq;
+        }
         return (a.tile_end - a.tile_begin) > (b.tile_end - b.tile_begin);
     });
     return static_cast<int64_t>(out.size());
