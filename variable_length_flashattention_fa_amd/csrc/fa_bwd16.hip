@@ -110,9 +110,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     constexpr int NOPS = 2 * NX;          // slots per step: X and Y MFMAs alternate
     constexpr int LA = 4;                 // LDS reads run LA slots ahead of their MFMA
     // Query tile buffers.  With four, the copy of a tile has two tile periods to land before the
-    // barrier that waits for it.  With dropout or an explicit mask, byte loads interleave with the
-    // tile copies in the load counter, so those kernels keep three buffers and wait for all loads.
-    constexpr int NB = DROP || XM ? 3 : 4;
+    // barrier that waits for it.  With an explicit mask, byte loads interleave with the tile copies
+    // in the load counter, so that kernel keeps three buffers and waits for all loads.  (Dropout
+    // keep bits come with the tile copies: see sKeep.)
+    constexpr int NB = XM ? 3 : 4;
     constexpr int TILEQ = BQ * DK;
     constexpr int TILED = BQ * DV;
     constexpr int TWQ = TILEQ / 8 / 64 / NW;  // DMA instructions per wave and Q tile
@@ -143,6 +144,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     __shared__ __attribute__((aligned(16))) T sBuf[NB][TEQ + TED];
     // row statistics of buffer b: sSt[b][0] = -D, sSt[b][1] = -beta of the tile's rows
     __shared__ __attribute__((aligned(16))) float sSt[NB][2][BQ];
+    // dropout keep bits of buffer b: row r of the tile at sKeep[b][8r .. 8r + 7], the 8 words of the
+    // mask that start with the word holding the bit of (row r, the block's first key)
+    __shared__ __attribute__((aligned(16))) uint32_t sKeep[NB][DROP ? BQ * 8 : 1];
     auto qtile = [&](int b) -> T* { return sBuf[b]; };
     auto dtile = [&](int b) -> T* { return sBuf[b] + TEQ; };
 
@@ -158,6 +162,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     const int off = K - L;
     const int j0 = it.block * BKV;
     const int jw = j0 + 32 * w + col;  // this lane's key
+    // the bit of (query row q of this sequence and head n, key j0) in the dropout mask
+    auto keep_bit0 = [&](int nq, int q) -> int64_t {
+        return it.drop_base + (static_cast<int64_t>(nq) * L + q) * K + j0;
+    };
     const uint32_t inv_keep_bits = __builtin_bit_cast(uint32_t, p.inv_keep);
     const int tb = it.tile_begin;
     const int te = it.tile_end;
@@ -258,12 +266,55 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 reinterpret_cast<uintptr_t>((lds_void*)(qtile(b) + w * TWQ * Tile<DK>::kRunBytes / 2)));
             const uint32_t md = static_cast<uint32_t>(
                 reinterpret_cast<uintptr_t>((lds_void*)(dtile(b) + w * TWD * Tile<DV>::kRunBytes / 2)));
-            // statistics first: the last TWQ + TWD loads a wave issues for a tile are its Q / dY copies
+            // statistics and keep bits first: the last TWQ + TWD loads a wave issues for a tile are
+            // its Q / dY copies
             if (w == NW - 1 && lane < BQ / 4) {
                 // rows past the sequence read as zero
                 const uint32_t nbytes = q0 < L ? static_cast<uint32_t>(min(L - q0, BQ) * 4) : 0u;
                 dma16_async(sSt[b][0], buffer_desc(gstat + q0, nbytes), lane * 16);
                 dma16_async(sSt[b][1], buffer_desc(gstat + plane + q0, nbytes), lane * 16);
+            }
+            if constexpr (DROP) {
+                if (w == NW - 2) {
+                    // 32 rows per copy, 16 bytes per lane: row r's 32 bytes start at the word holding
+                    // bit B_r = B_0 + r K (its first key's bit)
+                    const int64_t b0 = keep_bit0(n, q0);
+                    const int64_t byte0 = (b0 >> 5) << 2;
+                    const int64_t left = p.drop_bytes - byte0;
+                    const uint32_t nrec =
+                        left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left));
+                    const int s0 = static_cast<int>(b0 & 31);
+                    // A 16-byte copy that runs past the end of the mask may read as zero as a whole,
+                    // its bytes inside the mask included.  Records ending inside the mask (all but
+                    // those of the mask's last rows) are copied; otherwise every byte is loaded on
+                    // its own (bytes past the mask read as zero) and stored by the lane.  The byte
+                    // loads are waited for here, and with them every earlier copy of this wave.
+                    if (4 * static_cast<int64_t>((s0 + (BQ - 1) * K) >> 5) + 32 <= left) {
+                        const i32x4 rk = buffer_desc(p.drop_mask + byte0, nrec);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const int r = 32 * i + (lane >> 1);
+                            dma16_async(sKeep[b] + 256 * i, rk, 4 * ((s0 + r * K) >> 5) + 16 * (lane & 1));
+                        }
+                    } else {
+                        const __amdgpu_buffer_rsrc_t rk = raw_rsrc(p.drop_mask + byte0, nrec);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const int r = 32 * i + (lane >> 1);
+                            const int o = 4 * ((s0 + r * K) >> 5) + 16 * (lane & 1);
+                            uint32_t wv[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                wv[j] = 0;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    wv[j] |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rk, o + 4 * j + e, 0, 0))
+                                             << (8 * e);
+                            }
+                            *reinterpret_cast<uint4*>(&sKeep[b][256 * i + 4 * lane]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                        }
+                    }
+                }
             }
             dma_pair<TWQ, Tile<DK>::kRunBytes, TWD, Tile<DV>::kRunBytes>(__builtin_amdgcn_readfirstlane(mq), rq, qoff,
                                                                          __builtin_amdgcn_readfirstlane(md), rd, dyoff);
@@ -345,8 +396,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
         f32x16 pC = zero16();
         vec pkY[2];            // packed P and dS consumed by this step's Y (two 16-row halves)
         vec dsY[2];
-        uint32_t dbC[16];      // dropout mask bytes and bit base of the softmax rows
-        int dcC = 0;
+        uint32_t dwC = 0;      // keep bits of this lane's key for the softmax rows (bit = row in step)
         uint32_t mkC[16];      // explicit mask bytes of the softmax rows (XM)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -354,10 +404,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             dsY[i] = vec{};
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            dbC[i] = 0;
-            mkC[i] = 0;
-        }
+        for (int i = 0; i < 16; ++i) mkC[i] = 0;
 
         // One step (see the kinds above) of the tile in buffer b, tile index t; nkind / nb:
         // the step that follows (its first operands and statistics are read at the end).
@@ -382,8 +429,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             float pv[16];
             float pdv[16];
             float dsv[16];
-            uint32_t dbN[16];
-            int dcN = 0;
+            uint32_t dwN = 0;  // keep bits of the X rows, transposed to this lane's key
+            uint32_t kw[2];    // the words of this lane's row (row lane % 32 of the X rows) ...
+            int ks = 0;        // ... and the bit offset of the wave's first key in them
             uint32_t mkN[16];
             // explicit mask bytes of the X rows: element a sits at mbN + cc(a) * am_sq of the block
             uint32_t mbN = 0;
@@ -392,18 +440,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                 mbN = static_cast<uint32_t>(xt * BQ + 32 * wh.xm + 4 * h) * static_cast<uint32_t>(p.mask.am_sq) +
                       static_cast<uint32_t>(jw);
             }
-            // dropout bits of the X rows: the bit of (row 4h + cc(a), key jw) sits at bit
-            // dcN + cc(a) * K of the buffer that starts at the step's first mask byte
-            __amdgpu_buffer_rsrc_t drs;
+            // dropout keep bits of the X rows: lane l takes the 32 bits of row l % 32 for the wave's
+            // keys from its record (bit B_r + 32 w on, B_r the row's first key's bit), and a 32 x 32
+            // bit transpose across each half wave leaves in lane (col, h) the bits of key j0 + 32 w +
+            // col for rows 0..31 of the step: bit 4h + cc(a) is element a's
+            int xrow = 0;
             if constexpr (DROP && HX) {
                 const int xt = t + (KIND == kStepB ? 1 : 0);
-                const int64_t bits =
-                    it.drop_base + (static_cast<int64_t>(n) * L + xt * BQ + 32 * wh.xm) * K;
-                const int64_t byte0 = bits >> 3;
-                const int64_t left = p.drop_bytes - byte0;
-                drs = raw_rsrc(p.drop_mask + byte0,
-                               left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left)));
-                dcN = static_cast<int>(bits & 7) + 4 * h * K + jw;
+                xrow = 32 * wh.xm + col;
+                // low five bits only: 32-bit arithmetic suffices
+                ks = static_cast<int>((static_cast<uint32_t>(keep_bit0(n, xt * BQ)) +
+                                       static_cast<uint32_t>(xrow * K)) & 31u);
             }
             static_for<0, NOPS>([&](auto slot) {
                 constexpr int k = decltype(slot)::value;
@@ -461,8 +508,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                         if constexpr (DROP) {
                             // z = Z / keepProb of the element; dS = P (dP z - D), Pd = P z
                             const float ndl = stC[a / 4][0][a % 4];
-                            const int u = dcC + cc * K;
-                            const float z = keep_scale(dbC[a], u & 7, inv_keep_bits);
+                            const float z = keep_scale(dwC, 4 * h + cc, inv_keep_bits);
                             pdv[a] = pv[a] * z;
                             dsv[a] = pv[a] * fmaf(y, z, ndl);
                         } else {
@@ -509,11 +555,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                     if constexpr (kr == NOPS && (NKIND == kStepA || NKIND == kStepB)) read_stats(nw, 0, stN);
                     if constexpr (kr == NOPS && NKIND != kStepLast) read_binit(nw, bN);
                 }
-                // ---- dropout mask byte of X element k
-                if constexpr (DROP && HX && k < 16) {
-                    constexpr int cc = 8 * (k / 4) + (k % 4);
-                    const int u = dcN + cc * K;
-                    dbN[k] = __builtin_amdgcn_raw_buffer_load_b8(drs, u >> 3, 0, 0);
+                // ---- dropout keep bits of the X rows: record words at slot 0, the window and the five
+                // transpose stages (swap the off-diagonal j-blocks with lane ^ j) every two slots
+                if constexpr (DROP && HX) {
+                    if constexpr (k == 0) {
+                        const uint32_t* rec = &sKeep[wh.xb][8 * xrow + w];
+                        kw[0] = rec[0];
+                        kw[1] = rec[1];
+                    }
+                    if constexpr (k == 2) dwN = __builtin_amdgcn_alignbit(kw[1], kw[0], static_cast<uint32_t>(ks));
+                    if constexpr (k >= 2 && k <= 10 && k % 2 == 0) {
+                        constexpr int st = k / 2 - 1;  // stage of slots 2, 4, .., 10: j = 16, 8, .., 1
+                        constexpr int jj = 16 >> st;
+                        constexpr uint32_t msk = jj == 16 ? 0x0000FFFFu
+                                                          : jj == 8 ? 0x00FF00FFu
+                                                                    : jj == 4 ? 0x0F0F0F0Fu : jj == 2 ? 0x33333333u : 0x55555555u;
+                        // the partner lane's word (lane ^ j within each 32 lanes: ds_swizzle, xor mode)
+                        const uint32_t y = static_cast<uint32_t>(
+                            __builtin_amdgcn_ds_swizzle(static_cast<int>(dwN), 0x1F | (jj << 10)));
+                        // lanes with bit j clear keep their msk bits and take the partner's shifted up;
+                        // the others keep their ~msk bits and take the partner's shifted down
+                        const uint32_t up = (dwN & msk) | ((y << jj) & ~msk);
+                        const uint32_t dn = ((y >> jj) & msk) | (dwN & ~msk);
+                        const uint32_t sel = static_cast<uint32_t>(__builtin_amdgcn_sbfe(col, 4 - st, 1));
+                        dwN = (dn & sel) | (up & ~sel);
+                    }
                 }
                 // ---- explicit mask byte of X element k (rows past the sequence read zero or are
                 // excluded by the row range anyway)
@@ -528,11 +594,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             if constexpr (HX) {
                 sC = sN;
                 pC = pN;
-                if constexpr (DROP) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) dbC[i] = dbN[i];
-                    dcC = dcN;
-                }
+                if constexpr (DROP) dwC = dwN;
                 if constexpr (XM) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) mkC[i] = mkN[i];
@@ -615,7 +677,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
             // tile's statistics, two more loads per tile)
             {
                 const int after = min(NB - 2, te - tb - 1);
-                if (w == NW - 1) {
+                if (w == NW - 1 || (DROP && w == NW - 2)) {
                     wait_dma_but_tiles<TWQ + TWD + 2, NB - 2>(after);
                 } else {
                     wait_dma_but_tiles<TWQ + TWD, NB - 2>(after);
