@@ -79,6 +79,15 @@ def test_dropout_band_unaligned_bits():
     run_small(inp, O.MASK_BAND, 40, 9, kp=0.7)
 
 
+@pytest.mark.parametrize("dtype,dim", [("bf16", 128), ("fp16", 64)])
+def test_dropout_mask_ends_inside_tile_records(dtype, dim):
+    # The last sequence has 70 queries and 5 keys, so its rows sit 5 bits apart at the very end of the
+    # mask: the keep-bit records of both of its query tiles reach past the mask's last byte (the
+    # kernel then loads them byte by byte), one tile right after the other.
+    inp = make((100, 70), 2, dim, dtype, mode=O.MASK_NONE, kp=0.7, seed=14, kv_lens=(90, 5))
+    run_small(inp, O.MASK_NONE, kp=0.7)
+
+
 def test_dropout_bits_at_masked_positions_are_ignored():
     lens = (150, 70)
     kp = 0.75
