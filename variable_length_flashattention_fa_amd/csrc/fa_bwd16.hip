@@ -763,6 +763,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 
     __shared__ __attribute__((aligned(16))) T sK[2][Tile<DK>::kElems];
     __shared__ __attribute__((aligned(16))) T sV[2][Tile<DV>::kElems];
+    // dropout keep bits of buffer b: query row r of the workgroup (r = 0 .. BQ - 1) at
+    // sKeep[b][4r .. 4r + 3], the 4 words of the mask that start with the word holding the bit of
+    // (row r, the tile's first key)
+    __shared__ __attribute__((aligned(16))) uint32_t sKeep[2][DROP ? BQ * 4 : 1];
 
     const Unit unit = wg_unit(p.xcd_group != 0);
     const fa_work_item_t it = p.items_q[unit.item];
@@ -803,6 +807,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * Tile<DK>::kRunBytes / 2)));
         const uint32_t mv = static_cast<uint32_t>(
             reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * Tile<DV>::kRunBytes / 2)));
+        if constexpr (DROP) {
+            if (w < BQ / 64) {
+                // rows 64w .. 64w + 63 of the workgroup, one row per lane: row r's 16 bytes start at
+                // the word holding bit B_r = B_0 + r K (its bit of key k0)
+                const int64_t b0 = it.drop_base + (static_cast<int64_t>(n) * L + it.block * BQ + 64 * w) * K + k0;
+                const int64_t byte0 = (b0 >> 5) << 2;
+                const int64_t left = p.drop_bytes - byte0;
+                const uint32_t nrec =
+                    left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left));
+                const int s0 = static_cast<int>(b0 & 31);
+                const int o = 4 * ((s0 + lane * K) >> 5);
+                uint32_t* dst = sKeep[b] + 256 * w;
+                // A 16-byte copy that runs past the end of the mask may read as zero as a whole, its
+                // bytes inside the mask included.  Records ending inside the mask are copied;
+                // otherwise (the mask's last rows) every byte is loaded on its own (bytes past the
+                // mask read as zero) and stored by the lane.
+                if (4 * static_cast<int64_t>((s0 + 63 * K) >> 5) + 16 <= left) {
+                    dma16_async(dst, buffer_desc(p.drop_mask + byte0, nrec), o);
+                } else {
+                    // (a word at a time, in a loop kept rolled: few registers are free here)
+                    const __amdgpu_buffer_rsrc_t rb = raw_rsrc(p.drop_mask + byte0, nrec);
+#pragma unroll 1
+                    for (int j = 0; j < 4; ++j) {
+                        uint32_t wv = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            wv |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rb, o + 4 * j + e, 0, 0)) << (8 * e);
+                        dst[4 * lane + j] = wv;
+                    }
+                }
+            }
+        }
         dma_pair<TWK, Tile<DK>::kRunBytes, TWV, Tile<DV>::kRunBytes>(__builtin_amdgcn_readfirstlane(mk), rk, koff,
                                                                      __builtin_amdgcn_readfirstlane(mv), rv, voff);
     };
@@ -915,9 +951,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         }
     }
 
-    // bit offset of this lane's query row from the wave's first row in the dropout stream
-    const uint32_t drow = static_cast<uint32_t>(col) * static_cast<uint32_t>(K);
-
     // explicit mask block of this (sequence, head); this lane reads row qi
     __amdgpu_buffer_rsrc_t mrs;
     if constexpr (XM) {
@@ -925,12 +958,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         mrs = raw_rsrc(mb, static_cast<uint32_t>((L - 1) * p.mask.am_sq + K));
     }
 
-    // one 32-key step (keys k0s .. k0s + 31, rows R .. R + 31 of the tiles cK / cV)
-    auto kstep = [&](const T* cK, const T* cV, auto rc, int k0s) __attribute__((always_inline)) {
+    // one 32-key step (keys k0s .. k0s + 31, rows R .. R + 31 of the tiles cK / cV); win: the
+    // dropout keep bits of this lane's query for those keys (bit t = key k0s + t)
+    auto kstep = [&](const T* cK, const T* cV, auto rc, int k0s, uint32_t win) __attribute__((always_inline)) {
         constexpr int R = decltype(rc)::value;
         if (k0s > ahi || k0s + 31 < alo) return;
         // explicit mask bytes of keys k0s + 4h + cc(a), issued before the products that hide them
-        // (with dropout as well: after them, like the dropout window, to stay within the registers)
+        // (with dropout as well: after them, to stay within the registers)
         uint32_t mk[16];
         auto load_mask_bytes = [&]() __attribute__((always_inline)) {
             const uint32_t mrow = static_cast<uint32_t>(qi) * static_cast<uint32_t>(p.mask.am_sq) +
@@ -940,29 +974,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
                 mk[a] = __builtin_amdgcn_raw_buffer_load_b8(mrs, mrow + 8 * (a >> 2) + (a & 3), 0, 0);
         };
         if constexpr (XM && !DROP) load_mask_bytes();
-        // dropout bits of keys k0s .. k0s + 31 of this lane's query: contiguous in the bit stream, so
-        // five byte loads and one funnel shift give them as a 32-bit window (bit t = key k0s + t).
-        // The buffer starts at the byte that holds the bit of (wave's first query, key k0s), so
-        // lane offsets stay small; bytes past the end of the mask read as zero.  Issued before the
-        // products that hide their latency -- except with an explicit mask as well, whose 16 byte
-        // registers are live there too: then after them, which keeps the kernel within its registers.
-        uint32_t win = 0;
-        auto load_window = [&]() __attribute__((always_inline)) {
-            const int64_t b0 = it.drop_base + (static_cast<int64_t>(n) * L + i0) * K + k0s;
-            const int64_t byte0 = b0 >> 3;
-            const int64_t left = p.drop_bytes - byte0;
-            const __amdgpu_buffer_rsrc_t drs = raw_rsrc(
-                p.drop_mask + byte0, left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left)));
-            const uint32_t lb = static_cast<uint32_t>(b0 & 7) + drow;
-            const uint32_t byte = lb >> 3;
-            uint32_t lo = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                lo |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(drs, byte + i, 0, 0)) << (8 * i);
-            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b8(drs, byte + 4, 0, 0);
-            win = __builtin_amdgcn_alignbit(hi, lo, lb & 7);
-        };
-        if constexpr (DROP && !XM) load_window();
         // The two waves of a SIMD run the same sequence and meet at every tile barrier, so they
         // tend to reach their products and their softmax gradients together, when the matrix
         // pipe idles.  A wave issuing its S / dP products takes issue priority over one in any
@@ -980,10 +991,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
 #pragma unroll
         for (int s = SV; s < SK; ++s) accS = Op16<T>::mfma(tile_row<vec>(cK, loK, R, s), qreg[s], accS);
         __builtin_amdgcn_s_setprio(0);
-        if constexpr (DROP && XM) {
-            load_mask_bytes();
-            load_window();
-        }
+        if constexpr (DROP && XM) load_mask_bytes();
         // dS^T = Ps (dP Z/kp - D); element (key k0s + 4h + cc(a), query qi)
         const bool full = !XM && wave_rows_full && (k0s >= wlo) && (k0s + 31 <= whi);
         uint32_t dsw[2][4];
@@ -1036,8 +1044,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         wait_dma();
         __syncthreads();  // tile kt is in buffer B; every wave is done with buffer B ^ 1
         if (kt + 1 < it.tile_end) issue(kt + 1, B ^ 1);
-        kstep(sK[B], sV[B], IC<0>{}, kt * BK);
-        kstep(sK[B], sV[B], IC<32>{}, kt * BK + 32);
+        // dropout keep bits of this lane's query for the tile's 64 keys, from its record
+        uint32_t win0 = 0;
+        uint32_t win1 = 0;
+        if constexpr (DROP) {
+            const uint4 rec = *reinterpret_cast<const uint4*>(&sKeep[B][4 * (32 * w + col)]);
+            // low five bits only: 32-bit arithmetic suffices
+            const uint32_t sh = (static_cast<uint32_t>(it.drop_base) +
+                                 (static_cast<uint32_t>(n) * static_cast<uint32_t>(L) + static_cast<uint32_t>(qi)) *
+                                     static_cast<uint32_t>(K) +
+                                 static_cast<uint32_t>(kt * BK)) & 31u;
+            win0 = __builtin_amdgcn_alignbit(rec.y, rec.x, sh);
+            win1 = __builtin_amdgcn_alignbit(rec.z, rec.y, sh);
+        }
+        kstep(sK[B], sV[B], IC<0>{}, kt * BK, win0);
+        kstep(sK[B], sV[B], IC<32>{}, kt * BK + 32, win1);
     };
     if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
     int kt = it.tile_begin;
