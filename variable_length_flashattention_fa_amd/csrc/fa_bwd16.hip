@@ -807,37 +807,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
             reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * Tile<DK>::kRunBytes / 2)));
         const uint32_t mv = static_cast<uint32_t>(
             reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * Tile<DV>::kRunBytes / 2)));
+        // keep-bit records of rows 64w .. 64w + 63 of the workgroup (waves 0 .. 3)
         if constexpr (DROP) {
-            if (w < BQ / 64) {
-                // rows 64w .. 64w + 63 of the workgroup, one row per lane: row r's 16 bytes start at
-                // the word holding bit B_r = B_0 + r K (its bit of key k0)
-                const int64_t b0 = it.drop_base + (static_cast<int64_t>(n) * L + it.block * BQ + 64 * w) * K + k0;
-                const int64_t byte0 = (b0 >> 5) << 2;
-                const int64_t left = p.drop_bytes - byte0;
-                const uint32_t nrec =
-                    left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left));
-                const int s0 = static_cast<int>(b0 & 31);
-                const int o = 4 * ((s0 + lane * K) >> 5);
-                uint32_t* dst = sKeep[b] + 256 * w;
-                // A 16-byte copy that runs past the end of the mask may read as zero as a whole, its
-                // bytes inside the mask included.  Records ending inside the mask are copied;
-                // otherwise (the mask's last rows) every byte is loaded on its own (bytes past the
-                // mask read as zero) and stored by the lane.
-                if (4 * static_cast<int64_t>((s0 + 63 * K) >> 5) + 16 <= left) {
-                    dma16_async(dst, buffer_desc(p.drop_mask + byte0, nrec), o);
-                } else {
-                    // (a word at a time, in a loop kept rolled: few registers are free here)
-                    const __amdgpu_buffer_rsrc_t rb = raw_rsrc(p.drop_mask + byte0, nrec);
-#pragma unroll 1
-                    for (int j = 0; j < 4; ++j) {
-                        uint32_t wv = 0;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            wv |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rb, o + 4 * j + e, 0, 0)) << (8 * e);
-                        dst[4 * lane + j] = wv;
-                    }
-                }
-            }
+            if (w < BQ / 64)
+                copy_keep_records(sKeep[b] + 256 * w, p.drop_mask, p.drop_bytes,
+                                  it.drop_base + (static_cast<int64_t>(n) * L + it.block * BQ + 64 * w) * K + k0, K, lane);
         }
         dma_pair<TWK, Tile<DK>::kRunBytes, TWV, Tile<DV>::kRunBytes>(__builtin_amdgcn_readfirstlane(mk), rk, koff,
                                                                      __builtin_amdgcn_readfirstlane(mv), rv, voff);
@@ -1045,20 +1019,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
         __syncthreads();  // tile kt is in buffer B; every wave is done with buffer B ^ 1
         if (kt + 1 < it.tile_end) issue(kt + 1, B ^ 1);
         // dropout keep bits of this lane's query for the tile's 64 keys, from its record
-        uint32_t win0 = 0;
-        uint32_t win1 = 0;
+        uint32_t win[2] = {0u, 0u};
         if constexpr (DROP) {
-            const uint4 rec = *reinterpret_cast<const uint4*>(&sKeep[B][4 * (32 * w + col)]);
-            // low five bits only: 32-bit arithmetic suffices
-            const uint32_t sh = (static_cast<uint32_t>(it.drop_base) +
-                                 (static_cast<uint32_t>(n) * static_cast<uint32_t>(L) + static_cast<uint32_t>(qi)) *
-                                     static_cast<uint32_t>(K) +
-                                 static_cast<uint32_t>(kt * BK)) & 31u;
-            win0 = __builtin_amdgcn_alignbit(rec.y, rec.x, sh);
-            win1 = __builtin_amdgcn_alignbit(rec.z, rec.y, sh);
+            // (low five bits only: 32-bit arithmetic suffices)
+            keep_windows(&sKeep[B][4 * (32 * w + col)],
+                         static_cast<uint32_t>(it.drop_base) +
+                             (static_cast<uint32_t>(n) * static_cast<uint32_t>(L) + static_cast<uint32_t>(qi)) *
+                                 static_cast<uint32_t>(K) +
+                             static_cast<uint32_t>(kt * BK),
+                         win);
         }
-        kstep(sK[B], sV[B], IC<0>{}, kt * BK, win0);
-        kstep(sK[B], sV[B], IC<32>{}, kt * BK + 32, win1);
+        kstep(sK[B], sV[B], IC<0>{}, kt * BK, win[0]);
+        kstep(sK[B], sV[B], IC<32>{}, kt * BK + 32, win[1]);
     };
     if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
     int kt = it.tile_begin;

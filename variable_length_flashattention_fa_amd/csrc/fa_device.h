@@ -281,6 +281,45 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, t2));  // one packed conversion
 }
 
+// Keep-bit records of 64 query rows for one 64-key tile, one row per lane: row `lane`'s record is
+// the 16 bytes of the dropout mask that start at the word holding bit b0 + lane * K (the row's bit
+// of the tile's first key), stored at dst + 4 * lane.  Its bits s .. s + 63, s = that bit mod 32,
+// are the row's bits of the tile's keys (keep_windows).  A 16-byte copy that runs past the end of
+// the mask may read as zero as a whole, its bytes inside the mask included, so records ending inside
+// the mask are copied by LDS DMA (complete at the next wait for all loads); otherwise (the mask's
+// last rows) every byte is loaded on its own, bytes past the mask reading as zero, and the lane
+// stores the words itself, a word at a time in a loop kept rolled (few registers are free at the
+// callers).  Uniform arguments except lane.
+__device__ __forceinline__ void copy_keep_records(uint32_t* dst, const uint8_t* mask, int64_t mask_bytes,
+                                                  int64_t b0, int K, int lane) {
+    const int64_t byte0 = (b0 >> 5) << 2;
+    const int64_t left = mask_bytes - byte0;
+    const uint32_t nrec = left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left));
+    const int s0 = static_cast<int>(b0 & 31);
+    const int o = 4 * ((s0 + lane * K) >> 5);
+    if (4 * static_cast<int64_t>((s0 + 63 * K) >> 5) + 16 <= left) {
+        dma16_async(dst, buffer_desc(mask + byte0, nrec), o);
+    } else {
+        const __amdgpu_buffer_rsrc_t rb = raw_rsrc(mask + byte0, nrec);
+#pragma unroll 1
+        for (int j = 0; j < 4; ++j) {
+            uint32_t wv = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wv |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rb, o + 4 * j + e, 0, 0)) << (8 * e);
+            dst[4 * lane + j] = wv;
+        }
+    }
+}
+
+// The two 32-bit keep windows of a record (see copy_keep_records): bit t of win[i] is the bit of key
+// 32 i + t of the tile; `bit` is the row's bit of the tile's first key (only its low 5 bits count).
+__device__ __forceinline__ void keep_windows(const uint32_t* rec, uint32_t bit, uint32_t* win) {
+    const uint4 r = *reinterpret_cast<const uint4*>(rec);
+    win[0] = __builtin_amdgcn_alignbit(r.y, r.x, bit & 31u);
+    win[1] = __builtin_amdgcn_alignbit(r.z, r.y, bit & 31u);
+}
+
 // 1 / keep_prob where bit `pos` (taken modulo 32) of `bits` is set, else 0: the sign-extended bit
 // masks the bit pattern of 1 / keep_prob (`inv_keep_bits`), two instructions and no compare.
 __device__ __forceinline__ float keep_scale(uint32_t bits, int pos, uint32_t inv_keep_bits) {

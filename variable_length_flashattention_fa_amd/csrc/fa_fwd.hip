@@ -39,6 +39,9 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
 
     __shared__ __attribute__((aligned(16))) T sK[2][Tile<DK>::kElems];
     __shared__ __attribute__((aligned(16))) T sV[2][Tile<DV>::kElems];
+    // dropout keep bits of buffer b: the record of query row r of the workgroup (r = 0 .. BQ - 1) at
+    // sKeep[b][4r .. 4r + 3] (copy_keep_records)
+    __shared__ __attribute__((aligned(16))) uint32_t sKeep[2][DROP ? BQ * 4 : 1];
 
     const Unit unit = wg_unit(p.xcd_group != 0);
     const fa_work_item_t it = p.items[unit.item];
@@ -76,6 +79,12 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
             reinterpret_cast<uintptr_t>((lds_void*)(sK[b] + w * TWK * Tile<DK>::kRunBytes / 2)));
         const uint32_t mv = static_cast<uint32_t>(
             reinterpret_cast<uintptr_t>((lds_void*)(sV[b] + w * TWV * Tile<DV>::kRunBytes / 2)));
+        // keep-bit records of rows 64w .. 64w + 63 of the workgroup (waves 0 .. 3)
+        if constexpr (DROP) {
+            if (w < BQ / 64)
+                copy_keep_records(sKeep[b] + 256 * w, p.drop_mask, p.drop_bytes,
+                                  it.drop_base + (static_cast<int64_t>(n) * L + it.block * BQ + 64 * w) * K + k0, K, lane);
+        }
         dma_pair<TWK, Tile<DK>::kRunBytes, TWV, Tile<DV>::kRunBytes>(__builtin_amdgcn_readfirstlane(mk), rk, koff,
                                                                      __builtin_amdgcn_readfirstlane(mv), rv, voff);
     };
@@ -134,19 +143,6 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         ahi = min(ahi, i0 + 31 + off + p.nxt);
     }
 
-    // dropout: the (sequence, head) region of the bit stream starts at bit rb; the bits of this
-    // lane's query row start rbit bits past the region's first byte
-    __amdgpu_buffer_rsrc_t drs;
-    int64_t rbit = 0;
-    if constexpr (DROP) {
-        const int64_t rb = it.drop_base + static_cast<int64_t>(n) * L * K;
-        const int64_t byte0 = rb >> 3;
-        const int64_t left = p.drop_bytes - byte0;
-        drs = raw_rsrc(p.drop_mask + byte0,
-                       left <= 0 ? 0u : (left >= 0xffffffffll ? 0xffffffffu : static_cast<uint32_t>(left)));
-        rbit = (rb & 7) + static_cast<int64_t>(qi < L ? qi : 0) * K;
-    }
-
     // explicit mask block of this (sequence, head); this lane reads row qi
     __amdgpu_buffer_rsrc_t mrs;
     if constexpr (XM) {
@@ -161,8 +157,9 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
     float mref = -INFINITY;   // the max the P values and O^T are relative to
     float lsum = 0.f;         // sum of P over this lane's keys (relative to mref)
 
-    // one 32-key step (keys k0s .. k0s + 31, rows R .. R + 31 of the tiles cK / cV)
-    auto kstep = [&](const T* cK, const T* cV, auto rc, int k0s) __attribute__((always_inline)) {
+    // one 32-key step (keys k0s .. k0s + 31, rows R .. R + 31 of the tiles cK / cV); win: the
+    // dropout keep bits of this lane's query for those keys (bit t = key k0s + t)
+    auto kstep = [&](const T* cK, const T* cV, auto rc, int k0s, uint32_t win) __attribute__((always_inline)) {
         constexpr int R = decltype(rc)::value;
         if (k0s > ahi || k0s + 31 < alo) return;
         // explicit mask bytes of keys k0s + 4h + cc(a), issued before the product that hides them
@@ -220,20 +217,6 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         }
         // mref is -inf only while every score so far was masked; those give P = 0
         const float mb = mref == -INFINITY ? 0.f : mref;
-        uint32_t win = 0;
-        if constexpr (DROP) {
-            // bits of keys k0s .. k0s + 31 of this query: the five bytes that hold them, read one
-            // by one (a read that straddles the end of the mask would return zeros for the whole
-            // word, while bytes past the end read as zero individually)
-            const int64_t b0 = rbit + k0s;
-            const uint32_t byte = static_cast<uint32_t>(b0 >> 3);
-            uint32_t lo = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                lo |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(drs, byte + i, 0, 0)) << (8 * i);
-            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b8(drs, byte + 4, 0, 0);
-            win = __builtin_amdgcn_alignbit(hi, lo, static_cast<uint32_t>(b0 & 7));
-        }
         uint32_t pw[2][4];
 #pragma unroll
         for (int a = 0; a < 16; a += 2) {
@@ -270,8 +253,18 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
         wait_dma();
         __syncthreads();  // tile kt is in buffer B; every wave is done with buffer B ^ 1
         if (kt + 1 < it.tile_end) issue(kt + 1, B ^ 1);
-        kstep(sK[B], sV[B], IC<0>{}, kt * BK);
-        kstep(sK[B], sV[B], IC<32>{}, kt * BK + 32);
+        uint32_t win[2] = {0u, 0u};
+        if constexpr (DROP) {
+            // this lane's keep bits for the tile's 64 keys (low five bits of the bit index only)
+            keep_windows(&sKeep[B][4 * (32 * w + col)],
+                         static_cast<uint32_t>(it.drop_base) +
+                             (static_cast<uint32_t>(n) * static_cast<uint32_t>(L) + static_cast<uint32_t>(qi)) *
+                                 static_cast<uint32_t>(K) +
+                             static_cast<uint32_t>(kt * BK),
+                         win);
+        }
+        kstep(sK[B], sV[B], IC<0>{}, kt * BK, win[0]);
+        kstep(sK[B], sV[B], IC<32>{}, kt * BK + 32, win[1]);
     };
     if (it.tile_begin < it.tile_end) issue(it.tile_begin, 0);
     int kt = it.tile_begin;
