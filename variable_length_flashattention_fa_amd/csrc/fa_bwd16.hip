@@ -125,8 +125,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
     // Likewise the S chain starts from -beta of its rows, with this lane's K row scaled by
     // scale * log2(e) (once, before rounding to the operand type), so that it ends with
     // S * scale * log2(e) - beta and P = exp2(acc).  Its start block is read at the end of the step
-    // before.  With dropout or an explicit mask those registers are taken: the plain form stays.
-    constexpr bool FOLD_B = !DROP && !XM;
+    // before.  With an explicit mask those registers are taken: the plain form stays.
+    constexpr bool FOLD_B = !XM;
     // X slots: S (chain A) and dP (chain B); S leads by LA / 2 so that the start of the dP chain
     // (-D of the step's rows) can be read from LDS LA slots ahead, within the step
     // (with dropout the chain starts at zero and the plain alternation is kept)
