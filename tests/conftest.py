@@ -9,5 +9,8 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    import progress
+
+    progress.set_config(config)
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workload checks (minutes)")

@@ -18,6 +18,7 @@ import pytest
 import torch
 
 from gpu_common import assert_close, gpu_backward, log, make, oracle_backward, run_small
+from progress import progress
 from oracle import fa_oracle as O
 from variable_length_flashattention_fa_amd import binding as B
 from variable_length_flashattention_fa_amd import synth
@@ -200,21 +201,37 @@ def test_full_size_whole_tensors(number):
     wl = synth.workload(number)
     inp = synth.make(wl)
     w = _workers()
-    log(f"full-size workload {number} ({wl.name}): T={inp.q.shape[0]} N={wl.heads}; oracle forward on {w} workers")
+    progress(f"full-size workload {number} ({wl.name}): T={inp.q.shape[0]} N={wl.heads}; oracle forward on {w} workers")
     q, k, v = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v))
     y, m, l = O.forward(q, k, v, inp.cu_q, inp.cu_kv, mode=wl.mode, pre=wl.pre, nxt=wl.nxt, keep_prob=wl.keep_prob,
                         drop_mask=inp.drop_mask, scale=wl.scale, head_num=wl.heads, workers=w)
     yt = torch.from_numpy(y).to(wl.torch_dtype)
     smax, ssum = O.stats_to_page_layout(m, l)
     del y, m, l
-    log(f"  forward done {time.time() - t0:.1f}s; GPU backward (outputs NaN-poisoned)")
+    progress(f"  forward done {time.time() - t0:.1f}s; GPU backward (outputs NaN-poisoned)")
     got = gpu_backward(inp, yt, smax, ssum, wl.mode, wl.pre, wl.nxt, wl.keep_prob, wl.scale)
-    log(f"  GPU done {time.time() - t0:.1f}s; oracle backward on {w} workers")
-    ref = oracle_backward(inp, yt, smax, ssum, wl.mode, wl.pre, wl.nxt, wl.keep_prob, wl.scale, workers=w)
-    log(f"  oracle done {time.time() - t0:.1f}s")
+    progress(f"  GPU done {time.time() - t0:.1f}s; oracle backward on {w} workers")
+    # The oracle runs in chunks of (sequence, head) units, longest first, so that a line appears
+    # every few tens of seconds.  Each call fills only its units (zeros elsewhere) and adds the
+    # grouped heads' dK / dV, so the chunks' results sum to the whole.
+    lens_q, lens_k = np.diff(inp.cu_q), np.diff(inp.cu_kv)
+    units = sorted(((b, n) for b in range(len(lens_q)) for n in range(wl.heads) if lens_q[b] > 0 and lens_k[b] > 0),
+                   key=lambda u: -int(lens_q[u[0]]) * int(lens_k[u[0]]))
+    cost = np.cumsum([int(lens_q[b]) * int(lens_k[b]) for b, _ in units])
+    chunks = np.searchsorted(cost, cost[-1] * np.arange(1, 8) / 8, side="left")
+    bounds = [0] + sorted(set(int(c) + 1 for c in chunks if c + 1 < len(units))) + [len(units)]
+    y64 = synth.as_float_array(yt)
+    q64, k64, v64, dy64 = (synth.as_float_array(x) for x in (inp.q, inp.k, inp.v, inp.dy))
+    ref = None
+    for c0, c1 in zip(bounds[:-1], bounds[1:]):
+        part = O.backward(q64, k64, v64, dy64, y64, smax, ssum, inp.cu_q, inp.cu_kv, mode=wl.mode, pre=wl.pre,
+                          nxt=wl.nxt, keep_prob=wl.keep_prob, drop_mask=inp.drop_mask, scale=wl.scale,
+                          head_num=wl.heads, workers=w, units=units[c0:c1])
+        ref = part if ref is None else tuple(r + s for r, s in zip(ref, part))
+        progress(f"  oracle units {c1} of {len(units)} done {time.time() - t0:.1f}s")
     for name, g, o in zip(("dq", "dk", "dv"), got, ref):
         assert_close(name, g.double().numpy(), o, wl.torch_dtype)
-    log(f"  workload {number} whole-tensor parity ok ({time.time() - t0:.1f}s)")
+    progress(f"  workload {number} whole-tensor parity ok ({time.time() - t0:.1f}s)")
 
 
 @pytest.mark.parametrize("number", [3, 4])
@@ -226,12 +243,12 @@ def test_full_size_complete_units_and_every_head(number):
     work-list order runs last within each sequence) and the tile and block edges."""
     t0 = time.time()
     wl = synth.workload(number)
-    log(f"full-size workload {number} ({wl.name}): generating inputs")
+    progress(f"full-size workload {number} ({wl.name}): generating inputs")
     inp = synth.make(wl)
     dev = torch.device(DEV)
     q, k, v, dy = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.dy))
     drop = torch.from_numpy(inp.drop_mask).to(dev) if inp.drop_mask is not None else None
-    log(f"  inputs ready {time.time() - t0:.1f}s; device forward for Y and statistics")
+    progress(f"  inputs ready {time.time() - t0:.1f}s; device forward for Y and statistics")
     y, smax, ssum = forward_stats(q, k, v, inp.cu_q, inp.cu_kv, mode=wl.mode, pre=wl.pre, nxt=wl.nxt,
                                   keep_prob=wl.keep_prob, drop_mask=drop, scale=wl.scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -240,7 +257,7 @@ def test_full_size_complete_units_and_every_head(number):
     B.fa_varlen_bwd(q, k, v, dy, y, smax, ssum, inp.cu_q, inp.cu_kv, wl.mode, wl.pre, wl.nxt, wl.keep_prob, drop,
                     wl.scale, wl.heads, dq, dk, dv)
     torch.cuda.synchronize()
-    log(f"  backward done {time.time() - t0:.1f}s; comparing with the oracle")
+    progress(f"  backward done {time.time() - t0:.1f}s; comparing with the oracle")
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.isfinite(t.float()).all(), f"{name}: unwritten or non-finite elements"
@@ -262,7 +279,7 @@ def test_full_size_complete_units_and_every_head(number):
         assert_close(f"dk[{b},{n}]", dk[sk, n].double().numpy(), ref[1][sk, n], wl.torch_dtype)
         assert_close(f"dv[{b},{n}]", dv[sk, n].double().numpy(), ref[2][sk, n], wl.torch_dtype)
     del ref
-    log(f"  complete units ok {time.time() - t0:.1f}s; sampled rows and keys of every head")
+    progress(f"  complete units ok {time.time() - t0:.1f}s; sampled rows and keys of every head")
     rng = np.random.default_rng(1000 + number)
     gq, oq, gk, ok_, gv, ov = [], [], [], [], [], []
     for n in range(wl.heads):
@@ -280,6 +297,8 @@ def test_full_size_complete_units_and_every_head(number):
         ov.append(c)
         gk.append(dk[inp.cu_kv[b] + idx, n].double().numpy())
         gv.append(dv[inp.cu_kv[b] + idx, n].double().numpy())
+        if n % 8 == 7:
+            progress(f"  sampled heads {n + 1} of {wl.heads} done {time.time() - t0:.1f}s")
     for name, g, o in (("dq", gq, oq), ("dk", gk, ok_), ("dv", gv, ov)):
         assert_close(f"{name} (every head, sampled)", np.concatenate(g), np.concatenate(o), wl.torch_dtype)
-    log(f"  workload {number} full-size parity ok ({time.time() - t0:.1f}s)")
+    progress(f"  workload {number} full-size parity ok ({time.time() - t0:.1f}s)")
