@@ -570,13 +570,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
                         constexpr uint32_t msk = jj == 16 ? 0x0000FFFFu
                                                           : jj == 8 ? 0x00FF00FFu
                                                                     : jj == 4 ? 0x0F0F0F0Fu : jj == 2 ? 0x33333333u : 0x55555555u;
-                        // the partner lane's word (lane ^ j within each 32 lanes: ds_swizzle, xor mode)
-                        const uint32_t y = static_cast<uint32_t>(
-                            __builtin_amdgcn_ds_swizzle(static_cast<int>(dwN), 0x1F | (jj << 10)));
+                        // the partner lane's word, lane ^ j: across the two 16-lane rows of each 32
+                        // lanes (j = 16) by ds_swizzle in xor mode; within a row by DPP, where a row
+                        // rotate by r gives lane i the word of lane i - r (mod 16): j = 8, rotate by 8;
+                        // j = 4, rotate by 12 (lane i + 4) for the lanes with bit 2 clear and by 4
+                        // (lane i - 4) for the others; j = 2, 1: quad permutations
+                        uint32_t yu;  // partner of the lanes with bit j clear
+                        uint32_t yd;  // ... with bit j set
+                        if constexpr (jj == 16) {
+                            yu = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(dwN), 0x1F | (16 << 10)));
+                            yd = yu;
+                        } else if constexpr (jj == 8) {
+                            yu = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(dwN), 0x128, 0xF, 0xF, false));
+                            yd = yu;
+                        } else if constexpr (jj == 4) {
+                            yu = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(dwN), 0x12C, 0xF, 0xF, false));
+                            yd = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(dwN), 0x124, 0xF, 0xF, false));
+                        } else {
+                            constexpr int qp = jj == 2 ? 0x4E : 0xB1;  // [2,3,0,1] / [1,0,3,2]
+                            yu = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(dwN), qp, 0xF, 0xF, false));
+                            yd = yu;
+                        }
                         // lanes with bit j clear keep their msk bits and take the partner's shifted up;
                         // the others keep their ~msk bits and take the partner's shifted down
-                        const uint32_t up = (dwN & msk) | ((y << jj) & ~msk);
-                        const uint32_t dn = ((y >> jj) & msk) | (dwN & ~msk);
+                        const uint32_t up = (dwN & msk) | ((yu << jj) & ~msk);
+                        const uint32_t dn = ((yd >> jj) & msk) | (dwN & ~msk);
                         const uint32_t sel = static_cast<uint32_t>(__builtin_amdgcn_sbfe(col, 4 - st, 1));
                         dwN = (dn & sel) | (up & ~sel);
                     }
