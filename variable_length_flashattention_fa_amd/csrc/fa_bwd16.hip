@@ -739,21 +739,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(const Bwd16Args p) {
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(accV[nt]));
 
-    // epilogue: dK = scale * sum dS^T Q, dV = sum Pd^T dY; the lane holds column nt*32 + col
-    // of key rows 8g + 4h + r
+    // epilogue: dK = scale * sum dS^T Q, dV = sum Pd^T dY.  The lane holds column nt*32 + col of
+    // key rows 8g + 4h + r (acc_row), one value per key row: written as they are, that is one
+    // 2-byte store per value.  Instead each wave stages its 32 key rows in LDS (the tile buffers,
+    // free once every wave has left the tile loop) and writes whole rows back, 16 bytes per lane.
     T* gdk = static_cast<T*>(p.dk) + static_cast<int64_t>(it.kv_start) * p.dk_st + hk * p.dk_sh;
     T* gdv = static_cast<T*>(p.dv) + static_cast<int64_t>(it.kv_start) * p.dv_st + hk * p.dv_sh;
+    constexpr int SROW = DK + 8;  // staged row (values), padded so that a row starts 4 banks on
+    static_assert(NW * 32 * SROW <= NB * (TEQ + TED), "staging area");
+    T* stage = reinterpret_cast<T*>(sBuf) + w * 32 * SROW;
+    auto write_rows = [&](const f32x16* acc, auto ntc, float mul, T* dst, int64_t st) __attribute__((always_inline)) {
+        constexpr int NT = decltype(ntc)::value;
+        constexpr int CH = NT * 32 / 8;  // 16-byte chunks per row
+        __syncthreads();  // every wave is done with the LDS it is about to overwrite
 #pragma unroll
-    for (int nt = 0; nt < NTK; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            const int j = j0 + 32 * w + acc_row(a, h);
-            if (j < K) {
-                gdk[static_cast<int64_t>(j) * p.dk_st + nt * 32 + col] = static_cast<T>(accK[nt][a] * p.scale);
-                if (nt < NTV) gdv[static_cast<int64_t>(j) * p.dv_st + nt * 32 + col] = static_cast<T>(accV[nt][a]);
-            }
+            for (int a = 0; a < 16; ++a) stage[acc_row(a, h) * SROW + nt * 32 + col] = static_cast<T>(acc[nt][a] * mul);
         }
-    }
+        __syncthreads();  // the rows are staged (lanes read what other lanes wrote)
+#pragma unroll
+        for (int i = 0; i < 32 * CH / 64; ++i) {
+            const int c = lane + 64 * i;
+            const int row = c / CH;
+            const int j = j0 + 32 * w + row;
+            if (j < K)
+                *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(j) * st + (c % CH) * 8) =
+                    *reinterpret_cast<const uint4*>(stage + row * SROW + (c % CH) * 8);
+        }
+    };
+    write_rows(accK, IC<NTK>{}, p.scale, gdk, p.dk_st);
+    write_rows(accV, IC<NTV>{}, 1.0f, gdv, p.dv_st);
 }
 
 // ------------------------------------------------------------------------------------------------
