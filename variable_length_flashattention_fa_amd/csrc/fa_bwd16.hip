@@ -1074,17 +1074,40 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16_kernel(const Bwd16Args p) {
     }
     if (kt < it.tile_end) tile(kt, IC<0>{});
 
-    // epilogue: dQ = scale * (dQ^T)^T; the lane holds query qi, head-dim rows
-    // nd*32 + 8g + 4h + 0..3 (four consecutive values)
-    if (qi < L) {
-        T* dst = static_cast<T*>(p.dq) + static_cast<int64_t>(it.q_start + qi) * p.dq_st + n * p.dq_sh;
+    // epilogue: dQ = scale * (dQ^T)^T; the lane holds query qi, head-dim values nd*32 + 8g + 4h
+    // + 0..3: 8 bytes of its row per store, each store touching 32 rows.  Instead each wave stages
+    // its 32 rows in the key-tile buffers (free after a barrier; waves 0..3, then waves 4..7, whose
+    // rows would not fit at once in every head-dim variant) and writes whole rows back, 16 bytes per
+    // lane.  Chunk c (8 values) of staged row r sits at chunk c ^ (r % CH): the rows are not padded,
+    // and without the swizzle every row of a write would start on the same bank.
+    constexpr int CH = DK / 8;
+    static_assert(4 * 32 * DK <= 2 * Tile<DK>::kElems, "staging area");
+    T* stage = reinterpret_cast<T*>(sK) + (w & 3) * 32 * DK;
+    for (int round = 0; round < 2; ++round) {
+        __syncthreads();  // every wave is done with the LDS about to be overwritten
+        if ((w >> 2) == round) {
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
+            for (int nd = 0; nd < ND; ++nd) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t w0 = pack2<T>(accQ[nd][4 * g] * p.scale, accQ[nd][4 * g + 1] * p.scale);
-                const uint32_t w1 = pack2<T>(accQ[nd][4 * g + 2] * p.scale, accQ[nd][4 * g + 3] * p.scale);
-                *reinterpret_cast<uint2*>(dst + nd * 32 + 8 * g + 4 * h) = make_uint2(w0, w1);
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t w0 = pack2<T>(accQ[nd][4 * g] * p.scale, accQ[nd][4 * g + 1] * p.scale);
+                    const uint32_t w1 = pack2<T>(accQ[nd][4 * g + 2] * p.scale, accQ[nd][4 * g + 3] * p.scale);
+                    *reinterpret_cast<uint2*>(stage + col * DK + (((4 * nd + g) ^ (col % CH)) * 8) + 4 * h) =
+                        make_uint2(w0, w1);
+                }
+            }
+        }
+        __syncthreads();  // the rows are staged (lanes read what other lanes wrote)
+        if ((w >> 2) == round) {
+#pragma unroll
+            for (int i = 0; i < 32 * CH / 64; ++i) {
+                const int c = lane + 64 * i;
+                const int row = c / CH;
+                const int q = i0 + row;
+                if (q < L)
+                    *reinterpret_cast<uint4*>(static_cast<T*>(p.dq) + static_cast<int64_t>(it.q_start + q) * p.dq_st +
+                                              n * p.dq_sh + (c % CH) * 8) =
+                        *reinterpret_cast<const uint4*>(stage + row * DK + (((c % CH) ^ (row % CH)) * 8));
             }
         }
     }
