@@ -276,18 +276,44 @@ __global__ __launch_bounds__(512, 1) void fwd16_kernel(const FwdArgs p) {
 
     // epilogue: the two lane halves' sums; Y = O / l; statistics in natural units
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (qi < L) {
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        T* dst = static_cast<T*>(p.y) + static_cast<int64_t>(it.q_start + qi) * p.y_st + n * p.y_sh;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    // Y rows: the lane holds head-dim values nd*32 + 8g + 4h + 0..3 of its query, 8 bytes of its
+    // row per store, each store touching 32 rows.  Instead each wave stages its 32 rows in the
+    // key-tile buffers (free after a barrier; waves 0..3, then waves 4..7) and writes whole rows
+    // back, 16 bytes per lane.  Chunk c (8 values) of staged row r sits at chunk c ^ (r % CH), so
+    // that the rows of a write do not all start on one bank.
+    constexpr int CH = DV / 8;
+    static_assert(4 * 32 * DV <= 2 * Tile<DK>::kElems, "staging area");
+    T* stage = reinterpret_cast<T*>(sK) + (w & 3) * 32 * DV;
+    for (int round = 0; round < 2; ++round) {
+        __syncthreads();  // every wave is done with the LDS about to be overwritten
+        if ((w >> 2) == round) {
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
+            for (int nd = 0; nd < ND; ++nd) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t w0 = pack2<T>(accO[nd][4 * g] * inv, accO[nd][4 * g + 1] * inv);
-                const uint32_t w1 = pack2<T>(accO[nd][4 * g + 2] * inv, accO[nd][4 * g + 3] * inv);
-                *reinterpret_cast<uint2*>(dst + nd * 32 + 8 * g + 4 * h) = make_uint2(w0, w1);
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t w0 = pack2<T>(accO[nd][4 * g] * inv, accO[nd][4 * g + 1] * inv);
+                    const uint32_t w1 = pack2<T>(accO[nd][4 * g + 2] * inv, accO[nd][4 * g + 3] * inv);
+                    *reinterpret_cast<uint2*>(stage + col * DV + (((4 * nd + g) ^ (col % CH)) * 8) + 4 * h) =
+                        make_uint2(w0, w1);
+                }
             }
         }
+        __syncthreads();  // the rows are staged (lanes read what other lanes wrote)
+        if ((w >> 2) == round) {
+#pragma unroll
+            for (int i = 0; i < 32 * CH / 64; ++i) {
+                const int c = lane + 64 * i;
+                const int row = c / CH;
+                const int q = i0 + row;
+                if (q < L)
+                    *reinterpret_cast<uint4*>(static_cast<T*>(p.y) + static_cast<int64_t>(it.q_start + q) * p.y_st +
+                                              n * p.y_sh + (c % CH) * 8) =
+                        *reinterpret_cast<const uint4*>(stage + row * DV + (((c % CH) ^ (row % CH)) * 8));
+            }
+        }
+    }
+    if (qi < L) {
         const bool empty = mtrue == -INFINITY;
         const float mnat = empty ? -INFINITY : mtrue * 0.69314718055994531f;
         const float lnat = empty ? 0.f : ltot * __builtin_amdgcn_exp2f(mref - mtrue);
