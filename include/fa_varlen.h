@@ -293,9 +293,8 @@ int fa_profile_read(double* ms, int64_t* launches, int capacity);
  * max of the admitted scaled scores and its sum of exp(S - max), repeated 8 times.  A row with
  * no admitted key gets max -inf, sum 0 and a zero Y row.  The statistics are those of the
  * softmax before dropout, which is what fa_varlen_bwd expects.
- * Returns the status codes of fa_varlen_bwd.  FA_ERR_UNSUPPORTED also when dropout is on and
- * a sequence has Lq * Lkv >= 2^34.  Asynchronous on stream; its work lists follow the rules of
- * fa_varlen_bwd (it has no row statistics).
+ * Returns the status codes of fa_varlen_bwd.  Asynchronous on stream; its work lists follow
+ * the rules of fa_varlen_bwd (it has no row statistics).
  */
 int fa_varlen_fwd(const fa_tensor_t* q, const fa_tensor_t* k, const fa_tensor_t* v,
                   const fa_seqlens_t* cu_seqlens_q, const fa_seqlens_t* cu_seqlens_kv,

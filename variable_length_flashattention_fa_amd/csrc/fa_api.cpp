@@ -662,12 +662,6 @@ extern "C" int fa_varlen_fwd_masked(const fa_tensor_t* q, const fa_tensor_t* k, 
     for (int64_t b = 0; b < batch; ++b) {
         const int64_t lq = cu_seqlens_q->cu[b + 1] - cu_seqlens_q->cu[b];
         const int64_t lk = cu_seqlens_kv->cu[b + 1] - cu_seqlens_kv->cu[b];
-        // the 16-bit kernel addresses one (sequence, head) region of the bit stream with 32-bit
-        // byte offsets
-        if (keep_prob < 1.0 && lq * lk >= (int64_t(1) << 34)) {
-            set_error("dropout: a sequence's Lq * Lkv must stay below 2^34");
-            return FA_ERR_UNSUPPORTED;
-        }
         drop_bits += q->heads * lq * lk;
     }
 
