@@ -102,6 +102,15 @@ def test_forward_dropout(dtype):
     run_fwd(inp, O.MASK_CAUSAL, kp=0.8)
 
 
+@pytest.mark.parametrize("dtype,dim", [("bf16", 128), ("fp16", 64)])
+def test_forward_dropout_mask_ends_inside_tile_records(dtype, dim):
+    # The last sequence has 70 queries and 5 keys, so its rows sit 5 bits apart at the very end of the
+    # mask: the keep-bit records of its rows reach past the mask's last byte (the kernel then loads
+    # them byte by byte), in several waves of the workgroup at once.
+    inp = make((100, 70), 2, dim, dtype, mode=O.MASK_NONE, kp=0.7, seed=15, kv_lens=(90, 5))
+    run_fwd(inp, O.MASK_NONE, kp=0.7)
+
+
 def test_forward_dropout_band_unaligned_bits():
     inp = make((93, 45, 257), 2, 64, "bf16", mode=O.MASK_BAND, pre=40, nxt=7, kp=0.7, seed=12,
                kv_lens=(101, 38, 255))
